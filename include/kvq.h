@@ -1,0 +1,203 @@
+/*
+ * kvq.h -- C ABI of the quantized KV-cache library for MI355X (gfx950).
+ *
+ * The library writes new K/V vectors into a quantized cache (quantize, then
+ * scatter to slots) and runs decode / chunked-prefill attention that
+ * dequantizes the cache on the fly.  Every entry point is asynchronous: it
+ * validates its arguments on the host, enqueues its kernels on the caller's
+ * HIP stream and returns.  Nothing is enqueued when an argument is rejected.
+ * The library never allocates, frees or synchronizes; every buffer is owned by
+ * the caller and lives in device memory unless a comment says otherwise.
+ * Scalars that change from step to step (start position, kv_len) are device
+ * int32 values read by the kernels, so a captured step replays correctly.
+ *
+ * Page references (titles and sections of the pages this follows):
+ *   [PR24473]  pytorch/executorch pull request 24473, Summary
+ *   [PR20351]  pytorch/executorch pull request 20351 (gemma4_31b on the CUDA
+ *              backend), commit notes on index_copy_, the per-tile causal
+ *              upper bound and the kv_len bound
+ *   [IQC]      IndexerQuantCache (ops-transformer): function description,
+ *              parameter table, constraints
+ *   [ABADDON]  abaddon 0.2.0-rc.1, src/attention_cache/mod.rs, trait KvCache
+ *
+ * Layouts (row-major, innermost last):
+ *   new K/V x        [B, H, T, D]   bf16 or fp32; D contiguous, other strides
+ *                                   given in elements     ([ABADDON] append)
+ *   cache codes      [B, H, S, row_bytes] uint8           ([PR20351] positions
+ *                                   on dim 2, nibble packing on the last dim)
+ *   cache scales     INT8_TH/UINT4_TH: float [B, H, S]
+ *                    FP8E4M3_B32:      float [B, H, S, D/32]
+ *                    MXFP4_B32:        uint8 E8M0 [B, H, S, D/32]
+ *   cache zps        INT8_TH/UINT4_TH: int8 [B, H, S]; NULL for block modes
+ *   q / out          [B, Hq, Lq, D] contiguous             ([ABADDON]
+ *                                   forward_attention)
+ *   row_bytes        D for INT8_TH and FP8E4M3_B32, D/2 for UINT4_TH and
+ *                    MXFP4_B32 (two codes per byte, element 2i in the low
+ *                    nibble).
+ *
+ * Device error flags: entry points that take `int32_t* err_flags` (device,
+ * nullable) OR these bits into it when the data (not the arguments) is out of
+ * range; the offending token is skipped or the bound clamped, never written
+ * out of bounds.  The caller clears the word and reads it when it wants to.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = 1,        /* a required pointer is NULL */
+    KVQ_ERR_SHAPE = 2,       /* a size or stride is out of the supported range */
+    KVQ_ERR_DTYPE = 3,       /* dtype / quantization mode not valid for the call */
+    KVQ_ERR_UNSUPPORTED = 4, /* valid request this build does not run (never degraded) */
+    KVQ_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+    KVQ_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+} kvq_status;
+
+typedef enum kvq_qmode {
+    KVQ_INT8_TH = 0,      /* per token-head affine int8, fp32 scale, int8 zp [PR24473] */
+    KVQ_UINT4_TH = 1,     /* per token-head affine 4-bit, two codes per byte [PR20351] */
+    KVQ_FP8E4M3_B32 = 2,  /* per-32 block FP8-E4M3FN + fp32 scale, amax/448 [IQC] */
+    KVQ_MXFP4_B32 = 3     /* per-32 block FP4-E2M1 + E8M0 scale [IQC] */
+} kvq_qmode;
+
+typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+#define KVQ_FLAG_SLOT_RANGE 1    /* a slot outside [-1, n_slots): token skipped */
+#define KVQ_FLAG_KVLEN 2         /* kv_len outside [Lq, n_slots]: clamped */
+#define KVQ_FLAG_POS_CAPACITY 4  /* full-context position >= capacity: not written */
+
+#define KVQ_NO_CAUSAL_SKIP 1u    /* prefill: scan all KV tiles below kv_len
+                                    (the per-tile causal bound switched off) */
+
+/* One quantized cache (K or V).  Caller-owned device planes, see layouts. */
+typedef struct kvq_cache {
+    int32_t qmode;      /* kvq_qmode */
+    int32_t batch;      /* B */
+    int32_t heads;      /* KV heads H */
+    int32_t n_slots;    /* S, slots per (b, h) */
+    int32_t head_dim;   /* D */
+    void* codes;
+    void* scales;
+    int8_t* zps;        /* NULL for the block modes */
+} kvq_cache;
+
+/* Human-readable name of a status code (static storage). */
+const char* kvq_status_string(kvq_status s);
+
+/* Bytes of each plane of a cache with these sizes ([ABADDON] memory_bytes).
+ * Any output pointer may be NULL.  KVQ_ERR_SHAPE for non-positive sizes, odd
+ * D in the 4-bit modes or D % 32 != 0 in the block modes. */
+kvq_status kvq_cache_bytes(int qmode, int B, int H, int n_slots, int D,
+                           size_t* codes_bytes, size_t* scales_bytes, size_t* zps_bytes);
+
+/* Quantize new vectors and scatter them into cache slots.
+ *   [PR24473] int8 per token and head, affine asymmetric, fp32 scale + int8
+ *   zero point, written through the slot indices;  [PR20351] static scatter
+ *   along the position dim, nibble-packed 4-bit codes;  [IQC] per-32 block
+ *   formula scale = max|x_g| / Q_MAX, q = round(x / scale), slot -1 skipped.
+ * x: [B, H, T, D] in x_dtype with element strides (stride_b, stride_h,
+ *   stride_t), D contiguous; B, H, D must equal the cache's.
+ * slot_mapping: int32, token (b, t) uses slot_mapping[b*slot_stride_b + t];
+ *   slot_stride_b = 0 shares one row of T slots across the batch.  -1 skips
+ *   the token; any other value outside [0, n_slots) skips it and sets
+ *   KVQ_FLAG_SLOT_RANGE.  Valid slots of one call must be distinct (a
+ *   repeated slot leaves either token's row, unspecified which).
+ * Every head of the token is written: codes, scale and (affine modes) zero
+ *   point of row (b, h, slot).  All other bytes of the cache are untouched.
+ * Rounding: round half to even, IEEE fp32 division, no contraction; codes,
+ *   scales and zero points are bit-exact with the documented formulas.
+ * Limits: T >= 0 (T == 0 enqueues nothing), D % 8 == 0 and D <= 8192
+ *   (affine modes), D % 32 == 0 and D <= 8192 (block modes). */
+kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, int D,
+                             int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                             const int32_t* slot_mapping, int64_t slot_stride_b,
+                             const kvq_cache* cache, int32_t* err_flags, void* stream);
+
+/* Write slots for positions p = *start_pos + t, t in [0, T), attention-sink
+ * layout ([PR24473]): n_slots = sink_size + window, slot = p for p < sink_size,
+ * else sink_size + (p - sink_size) mod window.  slot_mapping_out: int32 [T].
+ * cache_positions: int32 [sink_size + window], in/out, -1 = empty; receives
+ * cache_positions[slot] = p (the latest position wins when a chunk wraps).
+ * start_pos is a device int32 scalar; a negative value writes slot -1 for
+ * every token and sets KVQ_FLAG_SLOT_RANGE.  sink_size >= 0, window >= 1. */
+kvq_status kvq_positions_with_sink(const int32_t* start_pos, int T, int sink_size, int window,
+                                   int32_t* slot_mapping_out, int32_t* cache_positions,
+                                   int32_t* err_flags, void* stream);
+
+/* Ring / sliding-window layout ([PR24473]): the sink layout with sink_size 0,
+ * slot = p mod window. */
+kvq_status kvq_positions_ring(const int32_t* start_pos, int T, int window,
+                              int32_t* slot_mapping_out, int32_t* cache_positions,
+                              int32_t* err_flags, void* stream);
+
+/* Full-context layout ([PR24473]): slot = p; a position >= capacity is
+ * rejected (slot -1, KVQ_FLAG_POS_CAPACITY) instead of written.
+ * cache_positions may be NULL. */
+kvq_status kvq_positions_full(const int32_t* start_pos, int T, int capacity,
+                              int32_t* slot_mapping_out, int32_t* cache_positions,
+                              int32_t* err_flags, void* stream);
+
+/* Additive mask for a ring/sink cache ([PR24473]: those caches build an
+ * additive float mask): mask_out[r, s] (fp32 [Lq, n_slots]) is 0 when the
+ * slot's position cp = cache_positions[s] is visible to query position
+ * qp = *start_pos + r, i.e. cp >= 0, cp <= qp and (cp < sink_size or
+ * qp - cp < window), and -inf otherwise. */
+kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos,
+                          int Lq, int sink_size, int window, float* mask_out, void* stream);
+
+/* Workspace bytes kvq_sdpa_decode needs for these sizes (partial softmax
+ * states of the split-K pass).  0 on invalid sizes. */
+size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D);
+
+/* Decode attention (Lq = 1) over quantized K/V caches ([ABADDON]
+ * forward_attention; [PR20351] kv_len bound; [PR24473] additive mask for
+ * ring/sink caches):
+ *   out[b, h, 0, :] = softmax_j(sm_scale * q[b,h,0,:] . k_hat[b,g,j,:] + mask[b,j]) v_hat[b,g,j,:]
+ * over j in [0, kv_len), g = h / (Hq / Hkv), k_hat / v_hat dequantized on the
+ * fly ((code - zp) * scale).  A row with no visible key gives 0.
+ * q: [B, Hq, 1, D] (q_dtype); out: [B, Hq, 1, D] (out_dtype).
+ * k, v: INT8_TH or UINT4_TH caches with equal sizes; Hq % heads == 0.
+ * kv_len: device int32 scalar or NULL (= n_slots); a value outside
+ *   [1, n_slots] is clamped and sets KVQ_FLAG_KVLEN.
+ * mask: NULL or fp32 [B, n_slots] with batch stride mask_stride_b (0 shares
+ *   one row); values 0 or -inf.  mask_is_causal is accepted for symmetry with
+ *   prefill: at Lq = 1 the causal bound is kv_len itself.
+ * workspace: device buffer of kvq_sdpa_decode_workspace_bytes() bytes
+ *   (contents need no initialisation).
+ * Supported D: 64, 128, 256; Hq / heads in {1, 2, 4, 8}. */
+kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
+                           const kvq_cache* k, const kvq_cache* v,
+                           const int32_t* kv_len, const float* mask, int64_t mask_stride_b,
+                           int mask_is_causal, float sm_scale, void* out, int out_dtype,
+                           void* workspace, size_t workspace_bytes,
+                           int32_t* err_flags, void* stream);
+
+/* Chunked-prefill attention over quantized K/V caches ([PR20351]): the Lq
+ * query rows sit at positions [kv_len - Lq, kv_len); row r attends keys
+ * j < kv_len, and when mask_is_causal only j <= kv_len - Lq + r.  The KV loop
+ * of a tile of rows stops at the per-tile causal bound
+ *   loop_end = min(kv_len, kv_len - Lq + max_row + 1)
+ * (flag KVQ_NO_CAUSAL_SKIP scans all tiles below kv_len instead; the result
+ * is bit-identical).  mask: NULL or fp32 [Lq, n_slots] shared over the batch
+ * (0 / -inf).  q: [B, Hq, Lq, D] (q_dtype); out: [B, Hq, Lq, D] (out_dtype).
+ * kv_len: device int32 scalar or NULL (= n_slots), clamped to [Lq, n_slots]
+ * with KVQ_FLAG_KVLEN.  Supported: INT8_TH or UINT4_TH, D in {64, 128, 256},
+ * Hq / heads in {1, 2, 4, 8}, Lq >= 1. */
+kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq,
+                            const kvq_cache* k, const kvq_cache* v,
+                            const int32_t* kv_len, const float* mask, int mask_is_causal,
+                            unsigned flags, float sm_scale, void* out, int out_dtype,
+                            int32_t* err_flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,240 @@
+// kvq_api.hip -- the C ABI of libkvq: argument validation, sizes, launches.
+//
+// Every entry point validates on the host and returns a kvq_status without
+// enqueuing anything when an argument is rejected; otherwise it enqueues on
+// the caller's stream and returns without synchronizing.  The library never
+// allocates device memory.  Unsupported-but-valid requests are rejected with
+// KVQ_ERR_UNSUPPORTED rather than run in a degraded form (pytorch/executorch
+// PR 24473, Summary: caches that cannot be run are rejected, never flattened).
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+#define KVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int row_bytes(int qmode, int D) { return (qmode == KVQ_UINT4_TH || qmode == KVQ_MXFP4_B32) ? D / 2 : D; }
+int scales_per_row(int qmode, int D) { return (qmode == KVQ_FP8E4M3_B32 || qmode == KVQ_MXFP4_B32) ? D / 32 : 1; }
+bool is_affine(int qmode) { return qmode == KVQ_INT8_TH || qmode == KVQ_UINT4_TH; }
+
+kvq_status check_dims(int qmode, int D) {
+    if (qmode < KVQ_INT8_TH || qmode > KVQ_MXFP4_B32) return KVQ_ERR_DTYPE;
+    if (D <= 0 || D > 8192) return KVQ_ERR_SHAPE;
+    if (is_affine(qmode) ? (D % 8 != 0) : (D % 32 != 0)) return KVQ_ERR_SHAPE;
+    return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache* c) {
+    if (!c) return KVQ_ERR_NULL;
+    kvq_status st = check_dims(c->qmode, c->head_dim);
+    if (st != KVQ_OK) return st;
+    if (c->batch <= 0 || c->heads <= 0 || c->n_slots <= 0) return KVQ_ERR_SHAPE;
+    if (!c->codes || !c->scales) return KVQ_ERR_NULL;
+    if (is_affine(c->qmode) && !c->zps) return KVQ_ERR_NULL;
+    // code rows are written and read 4..16 bytes at a time
+    if (!aligned(c->codes, 16) || !aligned(c->scales, 4)) return KVQ_ERR_SHAPE;
+    return KVQ_OK;
+}
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
+
+}  // namespace
+
+KVQ_API const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer argument";
+    case KVQ_ERR_SHAPE: return "size, stride or alignment out of the supported range";
+    case KVQ_ERR_DTYPE: return "dtype or quantization mode not valid for this call";
+    case KVQ_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+KVQ_API kvq_status kvq_cache_bytes(int qmode, int B, int H, int n_slots, int D, size_t* codes_bytes,
+                                   size_t* scales_bytes, size_t* zps_bytes) {
+    kvq_status st = check_dims(qmode, D);
+    if (st != KVQ_OK) return st;
+    if (B <= 0 || H <= 0 || n_slots <= 0) return KVQ_ERR_SHAPE;
+    const size_t rows = (size_t)B * H * n_slots;
+    if (codes_bytes) *codes_bytes = rows * row_bytes(qmode, D);
+    if (scales_bytes) *scales_bytes = rows * scales_per_row(qmode, D) * (qmode == KVQ_MXFP4_B32 ? 1 : 4);
+    if (zps_bytes) *zps_bytes = is_affine(qmode) ? rows : 0;
+    return KVQ_OK;
+}
+
+KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, int D, int64_t stride_b,
+                                     int64_t stride_h, int64_t stride_t, const int32_t* slot_mapping,
+                                     int64_t slot_stride_b, const kvq_cache* cache, int32_t* err_flags,
+                                     void* stream) {
+    kvq_status st = check_cache(cache);
+    if (st != KVQ_OK) return st;
+    if (x_dtype != KVQ_F32 && x_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (T < 0 || B != cache->batch || H != cache->heads || D != cache->head_dim) return KVQ_ERR_SHAPE;
+    if (T == 0) return KVQ_OK;
+    if (!x || !slot_mapping) return KVQ_ERR_NULL;
+    if (stride_b < 0 || stride_h < 0 || stride_t < 0 || slot_stride_b < 0) return KVQ_ERR_SHAPE;
+    // 8 elements per lane are loaded with 16-byte loads
+    const int64_t vec = x_dtype == KVQ_BF16 ? 8 : 4;
+    if (!aligned(x, 16) || stride_b % vec || stride_h % vec || stride_t % vec) return KVQ_ERR_SHAPE;
+    return from_hip(kvq::launch_quant_scatter(cache->qmode, x_dtype == KVQ_BF16, x, B, H, T, D, stride_b, stride_h,
+                                              stride_t, slot_mapping, slot_stride_b, cache->n_slots,
+                                              reinterpret_cast<uint8_t*>(cache->codes), cache->scales, cache->zps,
+                                              err_flags, reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_positions_with_sink(const int32_t* start_pos, int T, int sink_size, int window,
+                                           int32_t* slot_mapping_out, int32_t* cache_positions,
+                                           int32_t* err_flags, void* stream) {
+    if (T < 0 || sink_size < 0 || window < 1 || (int64_t)sink_size + window > INT32_MAX) return KVQ_ERR_SHAPE;
+    if (T == 0) return KVQ_OK;
+    if (!start_pos || !slot_mapping_out) return KVQ_ERR_NULL;
+    return from_hip(kvq::launch_positions_sink(start_pos, T, sink_size, window, slot_mapping_out, cache_positions,
+                                               err_flags, reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_positions_ring(const int32_t* start_pos, int T, int window, int32_t* slot_mapping_out,
+                                      int32_t* cache_positions, int32_t* err_flags, void* stream) {
+    return kvq_positions_with_sink(start_pos, T, 0, window, slot_mapping_out, cache_positions, err_flags, stream);
+}
+
+KVQ_API kvq_status kvq_positions_full(const int32_t* start_pos, int T, int capacity, int32_t* slot_mapping_out,
+                                      int32_t* cache_positions, int32_t* err_flags, void* stream) {
+    if (T < 0 || capacity < 1) return KVQ_ERR_SHAPE;
+    if (T == 0) return KVQ_OK;
+    if (!start_pos || !slot_mapping_out) return KVQ_ERR_NULL;
+    return from_hip(kvq::launch_positions_full(start_pos, T, capacity, slot_mapping_out, cache_positions, err_flags,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos, int Lq,
+                                  int sink_size, int window, float* mask_out, void* stream) {
+    if (n_slots < 1 || Lq < 0 || sink_size < 0 || window < 1) return KVQ_ERR_SHAPE;
+    if (Lq == 0) return KVQ_OK;
+    if (!cache_positions || !start_pos || !mask_out) return KVQ_ERR_NULL;
+    return from_hip(kvq::launch_build_mask(cache_positions, n_slots, start_pos, Lq, sink_size, window, mask_out,
+                                           reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v,
+                           void* out, int out_dtype) {
+    kvq_status st = check_cache(k);
+    if (st != KVQ_OK) return st;
+    st = check_cache(v);
+    if (st != KVQ_OK) return st;
+    if (!q || !out) return KVQ_ERR_NULL;
+    if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
+        return KVQ_ERR_DTYPE;
+    if (k->qmode != v->qmode) return KVQ_ERR_DTYPE;
+    if (!is_affine(k->qmode)) return KVQ_ERR_UNSUPPORTED;   // block-mode attention is not built
+    if (k->batch != v->batch || k->heads != v->heads || k->n_slots != v->n_slots || k->head_dim != v->head_dim)
+        return KVQ_ERR_SHAPE;
+    if (B != k->batch || Hq <= 0 || Hq % k->heads != 0) return KVQ_ERR_SHAPE;
+    const int G = Hq / k->heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return KVQ_ERR_UNSUPPORTED;
+    const int D = k->head_dim;
+    if (D != 64 && D != 128 && D != 256) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(out, 4)) return KVQ_ERR_SHAPE;
+    return KVQ_OK;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int splits, int D) {
+    return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
+}
+
+int decode_splits_any(int B, int Hkv, int S, int D) {
+    const int a = kvq::decode_splits(B, Hkv, S, D, KVQ_INT8_TH);
+    const int b = kvq::decode_splits(B, Hkv, S, D, KVQ_UINT4_TH);
+    return a > b ? a : b;
+}
+
+}  // namespace
+
+KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16) return 0;
+    return decode_ws_bytes(B, Hq, decode_splits_any(B, Hkv, n_slots, D), D);
+}
+
+KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
+                                   const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                   int64_t mask_stride_b, int mask_is_causal, float sm_scale, void* out,
+                                   int out_dtype, void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                   void* stream) {
+    (void)mask_is_causal;   // at Lq = 1 the causal bound equals kv_len
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
+    if (st != KVQ_OK) return st;
+    if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
+    const int D = k->head_dim;
+    const int nsplit = kvq::decode_splits(B, k->heads, k->n_slots, D, k->qmode);
+    const size_t need = decode_ws_bytes(B, Hq, nsplit, D);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
+    kvq::DecodeLaunch L;
+    L.q = q;
+    L.q_bf16 = q_dtype == KVQ_BF16;
+    L.B = B;
+    L.Hq = Hq;
+    L.Hkv = k->heads;
+    L.S = k->n_slots;
+    L.D = D;
+    L.qmode = k->qmode;
+    L.kc = reinterpret_cast<const uint8_t*>(k->codes);
+    L.ks = reinterpret_cast<const float*>(k->scales);
+    L.kz = k->zps;
+    L.vc = reinterpret_cast<const uint8_t*>(v->codes);
+    L.vs = reinterpret_cast<const float*>(v->scales);
+    L.vz = v->zps;
+    L.kv_len = kv_len;
+    L.mask = mask;
+    L.mask_sb = mask_stride_b;
+    L.sm_scale = sm_scale;
+    L.out = out;
+    L.out_bf16 = out_dtype == KVQ_BF16;
+    L.nsplit = nsplit;
+    L.part_o = reinterpret_cast<float*>(workspace);
+    L.part_ml = L.part_o + (size_t)B * Hq * nsplit * D;
+    L.err = err_flags;
+    return from_hip(kvq::launch_sdpa_decode(L, reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
+                                    const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                    int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
+                                    int32_t* err_flags, void* stream) {
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
+    if (st != KVQ_OK) return st;
+    if (Lq < 1 || Lq > k->n_slots) return KVQ_ERR_SHAPE;
+    if (flags & ~KVQ_NO_CAUSAL_SKIP) return KVQ_ERR_UNSUPPORTED;
+    kvq::PrefillLaunch L;
+    L.q = q;
+    L.q_bf16 = q_dtype == KVQ_BF16;
+    L.B = B;
+    L.Hq = Hq;
+    L.Hkv = k->heads;
+    L.S = k->n_slots;
+    L.D = k->head_dim;
+    L.Lq = Lq;
+    L.qmode = k->qmode;
+    L.kc = reinterpret_cast<const uint8_t*>(k->codes);
+    L.ks = reinterpret_cast<const float*>(k->scales);
+    L.kz = k->zps;
+    L.vc = reinterpret_cast<const uint8_t*>(v->codes);
+    L.vs = reinterpret_cast<const float*>(v->scales);
+    L.vz = v->zps;
+    L.kv_len = kv_len;
+    L.mask = mask;
+    L.causal = mask_is_causal != 0;
+    L.no_skip = (flags & KVQ_NO_CAUSAL_SKIP) != 0;
+    L.sm_scale = sm_scale;
+    L.out = out;
+    L.out_bf16 = out_dtype == KVQ_BF16;
+    L.err = err_flags;
+    hipError_t e = kvq::launch_sdpa_prefill(L, reinterpret_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported) return KVQ_ERR_UNSUPPORTED;
+    return from_hip(e);
+}

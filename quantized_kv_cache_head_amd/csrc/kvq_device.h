@@ -1,0 +1,118 @@
+// kvq_device.h -- device helpers shared by the gfx950 kernels of libkvq.
+// (Product code: nothing here is shared with the CPU oracle.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bit level; bf16 -> fp32 is exact)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 with round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Load 8 consecutive input elements as fp32 (16-byte aligned for bf16,
+// 32-byte span for fp32).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t elem_off, float v[8]) {
+    if constexpr (BF16) {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem_off);
+        v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+        v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+        v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+        v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + elem_off);
+        const float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Element encoders (integer rounding on the fp32 bit pattern)
+// ---------------------------------------------------------------------------
+
+// FP8 E4M3FN, round to nearest even, |y| >= 448 saturates to 0x7E, sign kept.
+__device__ __forceinline__ uint32_t enc_e4m3fn(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a >= 0x43E00000u) {                 // >= 448
+        mag = 0x7Eu;
+    } else if (a < 0x3C800000u) {           // < 2^-6: multiples of 2^-9
+        mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+    } else {                                // keep 3 mantissa bits, RNE
+        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+        mag = (r >> 20) - (120u << 3);      // rebias exponent 127 -> 7
+    }
+    return sign | mag;
+}
+
+// FP4 E2M1 (magnitudes 0,.5,1,1.5,2,3,4,6), RNE, |y| >= 6 saturates, sign bit 3.
+__device__ __forceinline__ uint32_t enc_e2m1(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a >= 0x40C00000u) {                 // >= 6
+        mag = 7u;
+    } else if (a < 0x3F800000u) {           // < 1: multiples of 0.5
+        mag = (uint32_t)rintf(__uint_as_float(a) * 2.0f);
+    } else {                                // keep 1 mantissa bit, RNE
+        const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
+        mag = (r >> 22) - (126u << 1);      // rebias exponent 127 -> 1
+    }
+    return sign | mag;
+}
+
+// Biased E8M0 exponent of the smallest power of two >= s (s >= 0), clamped
+// to [0, 254].
+__device__ __forceinline__ uint32_t e8m0_ceil(float s) {
+    if (!(s > 0.0f)) return 0u;
+    const uint32_t u = __float_as_uint(s);
+    const int ef = (int)(u >> 23);
+    const uint32_t mant = u & 0x7FFFFFu;
+    int e;
+    if (ef == 0) e = (32 - (int)__clz(mant - 1u)) - 149;   // ceil(log2(mant * 2^-149))
+    else e = ef - 127 + (mant != 0u ? 1 : 0);
+    int b = e + 127;
+    b = b < 0 ? 0 : (b > 254 ? 254 : b);
+    return (uint32_t)b;
+}
+
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+    return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (wave64)
+// ---------------------------------------------------------------------------
+template <int WIDTH>
+__device__ __forceinline__ float wave_max_sub(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float wave_min_sub(float v) {
+#pragma unroll
+    for (int o = WIDTH / 2; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+}  // namespace kvq

@@ -1,0 +1,75 @@
+// kvq_internal.h -- host-side launchers behind the C ABI of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define KVQ_DEV_FLAG_SLOT_RANGE 1
+#define KVQ_DEV_FLAG_KVLEN 2
+#define KVQ_DEV_FLAG_POS_CAPACITY 4
+
+namespace kvq {
+
+enum { QM_INT8_TH = 0, QM_UINT4_TH = 1, QM_FP8E4M3_B32 = 2, QM_MXFP4_B32 = 3 };
+
+hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,
+                                int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
+                                int64_t ssb, int n_slots, uint8_t* codes, void* scales,
+                                int8_t* zps, int32_t* err, hipStream_t s);
+
+hipError_t launch_positions_sink(const int32_t* start_pos, int T, int sink, int window, int32_t* slot_out,
+                                 int32_t* cache_positions, int32_t* err, hipStream_t s);
+hipError_t launch_positions_full(const int32_t* start_pos, int T, int capacity, int32_t* slot_out,
+                                 int32_t* cache_positions, int32_t* err, hipStream_t s);
+hipError_t launch_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos, int Lq,
+                             int sink, int window, float* mask, hipStream_t s);
+
+struct DecodeLaunch {
+    const void* q;
+    bool q_bf16;
+    int B, Hq, Hkv, S, D, qmode;
+    const uint8_t* kc;
+    const float* ks;
+    const int8_t* kz;
+    const uint8_t* vc;
+    const float* vs;
+    const int8_t* vz;
+    const int32_t* kv_len;
+    const float* mask;
+    int64_t mask_sb;
+    float sm_scale;
+    void* out;
+    bool out_bf16;
+    int nsplit;
+    float* part_o;
+    float* part_ml;
+    int32_t* err;
+};
+
+int decode_splits(int B, int Hkv, int S, int D, int qmode);
+hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s);
+
+struct PrefillLaunch {
+    const void* q;
+    bool q_bf16;
+    int B, Hq, Hkv, S, D, Lq, qmode;
+    const uint8_t* kc;
+    const float* ks;
+    const int8_t* kz;
+    const uint8_t* vc;
+    const float* vs;
+    const int8_t* vz;
+    const int32_t* kv_len;
+    const float* mask;
+    bool causal;
+    bool no_skip;
+    float sm_scale;
+    void* out;
+    bool out_bf16;
+    int32_t* err;
+};
+
+hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s);
+
+}  // namespace kvq

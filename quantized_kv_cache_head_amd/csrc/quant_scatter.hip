@@ -1,0 +1,232 @@
+// quant_scatter.hip -- quantize new K/V vectors and scatter them to cache slots.
+//
+// Affine per token-head modes (int8 and 4-bit): pytorch/executorch PR 24473
+// (Summary: int8 entries per token and head, affine asymmetric, float32 scale,
+// int8 zero point, written through slot indices) and PR 20351 (4-bit codes
+// packed two per byte along head_dim; static scatter along the position dim).
+// Block modes (FP8-E4M3 + fp32 scale, MX-FP4 + E8M0 scale, 32 elements per
+// block): IndexerQuantCache page, function description (scale = max|x_g| /
+// Q_MAX, q = round(x / scale)), parameter table and constraints (slot -1
+// skipped, valid slots in [0, num_slots)).
+//
+// Affine rule (the pages name the scheme without a formula; this is the
+// reading the library implements): lo = min(0, min x), hi = max(0, max x),
+// scale = max((hi - lo) / (qmax - qmin), 2^-23), zp = clamp(qmin -
+// rne(lo / scale)), code = clamp(rne(x / scale) + zp).  MX-FP4 scale: the
+// smallest power of two >= amax / 6.
+//
+// Work mapping: a row (one token of one head) is split over L lanes of a
+// wavefront, 8 elements per lane (one 16-byte bf16 load), so a wave covers
+// 64/L rows and the min/max reduction stays inside the row's lanes.  Each lane
+// writes its 8 codes (8 or 4 bytes) in one store; the L lanes of a row write
+// the contiguous code row.  Block modes: 4 lanes per 32-element block.
+// All arithmetic is single IEEE fp32 operations (file built with
+// -ffp-contract=off; division is correctly rounded; rintf is RNE), so codes,
+// scales and zero points are bit-exact with the documented formulas.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+struct ScatterArgs {
+    const void* x;
+    int B, H, T, D;
+    int64_t sb, sh, st;
+    const int32_t* slots;
+    int64_t ssb;
+    int n_slots;
+    uint8_t* codes;
+    void* scales;
+    int8_t* zps;
+    int32_t* err;
+};
+
+// Decode row index -> (b, h, t) and look up its slot.
+__device__ __forceinline__ void row_coords(const ScatterArgs& a, int64_t row, int& b, int& h, int& t) {
+    t = (int)(row % a.T);
+    const int64_t bh = row / a.T;
+    h = (int)(bh % a.H);
+    b = (int)(bh / a.H);
+}
+
+template <int L, int NP, bool BF16, bool U4>
+__global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a) {
+    constexpr int QMIN = U4 ? 0 : -128;
+    constexpr int QMAX = U4 ? 15 : 127;
+    const int lane = threadIdx.x & 63;
+    const int li = lane % L;
+    const int64_t rows = (int64_t)a.B * a.H * a.T;
+    const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * (64 / L) + lane / L;
+
+    int b = 0, h = 0, t = 0, slot = -1;
+    if (row < rows) {
+        row_coords(a, row, b, h, t);
+        slot = a.slots[(int64_t)b * a.ssb + t];
+        if (slot < -1 || slot >= a.n_slots) {
+            if (h == 0 && li == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
+            slot = -1;
+        }
+    }
+    const bool valid = slot >= 0;
+
+    // Load (zeros where the row is skipped or past D; zeros never change the
+    // range, which always contains 0).
+    float v[NP][8];
+    float lo = 0.0f, hi = 0.0f;
+    const int64_t xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int d0 = (p * L + li) * 8;
+        if (valid && d0 < a.D) {
+            load8<BF16>(a.x, xoff + d0, v[p]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { lo = fminf(lo, v[p][i]); hi = fmaxf(hi, v[p][i]); }
+    }
+    lo = wave_min_sub<L>(lo);
+    hi = wave_max_sub<L>(hi);
+    if (!valid) return;
+
+    const float range = hi - lo;
+    float scale = range / (float)(QMAX - QMIN);
+    scale = fmaxf(scale, 0x1p-23f);
+    int zp = QMIN - (int)rintf(lo / scale);
+    zp = min(max(zp, QMIN), QMAX);
+
+    const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int d0 = (p * L + li) * 8;
+        if (d0 >= a.D) break;
+        int c[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int q = (int)rintf(v[p][i] / scale) + zp;
+            c[i] = min(max(q, QMIN), QMAX);
+        }
+        if constexpr (U4) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= (uint32_t)c[i] << (4 * i);
+            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+        } else {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w0 |= ((uint32_t)c[i] & 0xFFu) << (8 * i);
+                w1 |= ((uint32_t)c[4 + i] & 0xFFu) << (8 * i);
+            }
+            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+        }
+    }
+    if (li == 0) {
+        reinterpret_cast<float*>(a.scales)[crow] = scale;
+        a.zps[crow] = (int8_t)zp;
+    }
+}
+
+template <bool BF16, bool MX>
+__global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a) {
+    const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int qi = (int)(gl & 3);                  // lane within the 32-block
+    const int64_t blk = gl >> 2;
+    const int gpr = a.D / 32;                      // blocks per row
+    const int64_t rows = (int64_t)a.B * a.H * a.T;
+    const int64_t row = blk / gpr;
+    const int g = (int)(blk % gpr);
+
+    int b = 0, h = 0, t = 0, slot = -1;
+    if (row < rows) {
+        row_coords(a, row, b, h, t);
+        slot = a.slots[(int64_t)b * a.ssb + t];
+        if (slot < -1 || slot >= a.n_slots) {
+            if (h == 0 && g == 0 && qi == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
+            slot = -1;
+        }
+    }
+    const bool valid = slot >= 0;
+    float v[8];
+    const int d0 = g * 32 + qi * 8;
+    if (valid) {
+        load8<BF16>(a.x, (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st + d0, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = wave_max_sub<4>(amax);
+    if (!valid) return;
+
+    const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+    if constexpr (!MX) {
+        const float scale = amax / 448.0f;
+        uint32_t w0 = 0, w1 = 0;
+        if (scale != 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w0 |= enc_e4m3fn(v[i] / scale) << (8 * i);
+                w1 |= enc_e4m3fn(v[4 + i] / scale) << (8 * i);
+            }
+        }
+        *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+        if (qi == 0) reinterpret_cast<float*>(a.scales)[crow * gpr + g] = scale;
+    } else {
+        const float s = amax / 6.0f;
+        const uint32_t e8 = e8m0_ceil(s);
+        const float X = e8m0_value(e8);
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] / X) << (4 * i);
+        *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+        if (qi == 0) reinterpret_cast<uint8_t*>(a.scales)[crow * gpr + g] = (uint8_t)e8;
+    }
+}
+
+template <int L, int NP, bool BF16, bool U4>
+static hipError_t launch_affine(const ScatterArgs& a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.B * a.H * a.T;
+    const int64_t rows_per_block = 4 * (64 / L);
+    const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((quant_scatter_affine<L, NP, BF16, U4>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool BF16, bool U4>
+static hipError_t dispatch_affine(const ScatterArgs& a, hipStream_t s) {
+    switch (a.D) {
+    case 64: return launch_affine<8, 1, BF16, U4>(a, s);
+    case 128: return launch_affine<16, 1, BF16, U4>(a, s);
+    case 256: return launch_affine<32, 1, BF16, U4>(a, s);
+    case 512: return launch_affine<64, 1, BF16, U4>(a, s);
+    default:
+        if (a.D <= 1024) return launch_affine<64, 2, BF16, U4>(a, s);
+        if (a.D <= 2048) return launch_affine<64, 4, BF16, U4>(a, s);
+        return launch_affine<64, 16, BF16, U4>(a, s);
+    }
+}
+
+hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,
+                                int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
+                                int64_t ssb, int n_slots, uint8_t* codes, void* scales,
+                                int8_t* zps, int32_t* err, hipStream_t s) {
+    ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err};
+    if (qmode == QM_INT8_TH) return bf16 ? dispatch_affine<true, false>(a, s) : dispatch_affine<false, false>(a, s);
+    if (qmode == QM_UINT4_TH) return bf16 ? dispatch_affine<true, true>(a, s) : dispatch_affine<false, true>(a, s);
+    const int64_t lanes = (int64_t)B * H * T * (D / 8);
+    const unsigned blocks = (unsigned)((lanes + 255) / 256);
+    if (qmode == QM_FP8E4M3_B32) {
+        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, false>), dim3(blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((quant_scatter_block<false, false>), dim3(blocks), dim3(256), 0, s, a);
+    } else {
+        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, true>), dim3(blocks), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((quant_scatter_block<false, true>), dim3(blocks), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

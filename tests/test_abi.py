@@ -1,0 +1,119 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/kvq.h declares, and rejects bad arguments on the host (no GPU work is
+started by any call here: each one fails validation before a launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import quantized_kv_cache_head_amd as kvq
+    if not os.path.exists(kvq.LIB_PATH):
+        from quantized_kv_cache_head_amd import build
+        build.build()
+    kvq.lib()
+    return kvq
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree(kvq):
+    assert _declared() == sorted(kvq.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(kvq):
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(kvq.lib(), name)
+    # nothing else leaks out of the library
+    assert exported == set(_declared())
+
+
+def test_status_strings(kvq):
+    for st in range(7):
+        assert kvq.status_string(st)
+    assert kvq.status_string(0) == "ok"
+
+
+def test_cache_bytes(kvq):
+    assert kvq.cache_bytes(kvq.INT8_TH, 8, 8, 8192, 128) == (8 * 8 * 8192 * 128, 8 * 8 * 8192 * 4, 8 * 8 * 8192)
+    assert kvq.cache_bytes(kvq.UINT4_TH, 1, 16, 131072, 256) == (16 * 131072 * 128, 16 * 131072 * 4, 16 * 131072)
+    assert kvq.cache_bytes(kvq.FP8E4M3_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
+    assert kvq.cache_bytes(kvq.MXFP4_B32, 1, 1, 65536, 128) == (65536 * 64, 65536 * 4, 0)
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_bytes(kvq.FP8E4M3_B32, 1, 1, 16, 48)        # D % 32 != 0
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_bytes(kvq.UINT4_TH, 1, 1, 16, 60)           # D % 8 != 0
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_bytes(7, 1, 1, 16, 64)
+
+
+def _fake_cache(kvq, qmode=0, B=1, H=2, S=64, D=64, zps=True):
+    # host addresses are never dereferenced: every call below fails validation
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    c = kvq.kvq_cache(qmode, B, H, S, D, base, base, base if zps else 0)
+    return c, buf
+
+
+def test_host_validation_errors(kvq):
+    L = kvq.lib()
+    c, keep = _fake_cache(kvq)
+    s = None
+    # NULL cache / NULL x
+    assert L.kvq_quant_scatter(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, None, None, s) == 1
+    assert L.kvq_quant_scatter(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c), None, s) == 1
+    # shape mismatch with the cache
+    assert L.kvq_quant_scatter(None, 1, 1, 3, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c), None, s) == 2
+    # bad dtype
+    assert L.kvq_quant_scatter(None, 5, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c), None, s) == 3
+    # T == 0 is a no-op
+    assert L.kvq_quant_scatter(None, 1, 1, 2, 0, 64, 0, 0, 64, None, 0, ctypes.byref(c), None, s) == 0
+    # affine cache without zero points
+    cz, keep2 = _fake_cache(kvq, zps=False)
+    assert L.kvq_quant_scatter(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(cz), None, s) == 1
+    # positions: window must be >= 1, T >= 0
+    assert L.kvq_positions_with_sink(None, 4, 4, 0, None, None, None, s) == 2
+    assert L.kvq_positions_ring(None, -1, 8, None, None, None, s) == 2
+    assert L.kvq_positions_full(None, 4, 0, None, None, None, s) == 2
+    assert L.kvq_positions_full(None, 4, 16, None, None, None, s) == 1
+    assert L.kvq_build_mask(None, 0, None, 1, 0, 4, None, s) == 2
+    # attention: block-mode caches are rejected as unsupported, never degraded
+    cb, keep3 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
+    q = ctypes.c_void_p(c.codes)
+    assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(cb), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
+                             None, 0, None, s) == 4
+    # Hq not a multiple of the KV heads
+    assert L.kvq_sdpa_decode(q, 1, 1, 3, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
+                             None, 0, None, s) == 2
+    # missing workspace
+    assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
+                             None, 0, None, s) == 5
+    # unsupported head_dim for attention
+    c96, keep4 = _fake_cache(kvq, D=96)
+    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 8, ctypes.byref(c96), ctypes.byref(c96), None, None, 1, 0, 0.1, q, 1,
+                              None, s) == 4
+    # unknown prefill flag
+    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 2, 0.1, q, 1,
+                              None, s) == 4
+    # Lq beyond the cache
+    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 65, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
+                              None, s) == 2
+
+
+def test_workspace_size(kvq):
+    n = kvq.sdpa_decode_workspace_bytes(8, 32, 8, 8192, 128)
+    assert n > 0 and n % (8 * 32 * 130 * 4) == 0
+    assert kvq.sdpa_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0

@@ -1,0 +1,142 @@
+"""GPU parity of kvq_sdpa_decode (split-K + combine) against the oracle's fp64
+attention on the same quantized cache, plus the bit-identities the pages fix:
+data past kv_len cannot matter, an all-zero mask equals no mask, the causal
+flag is a no-op at Lq = 1, and reruns are deterministic."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_kv_cache_head_amd as kvq
+import quantized_kv_cache_head_amd.workloads as wl
+from _gpu import DEV, assert_cache_equal, check_attention, dev_input, new_pair, say
+
+pytestmark = pytest.mark.gpu
+
+
+def fill_caches(qmode, B, Hkv, S, D, n_fill, seed, bf16=True, outliers=True):
+    """K and V caches with slots [0, n_fill) written by the GPU kernel and by the
+    oracle from the same inputs (checked bit-exact), the rest sentinel."""
+    rng = np.random.default_rng(seed)
+    pairs = []
+    for which in range(2):
+        x = rng.standard_normal((B, Hkv, n_fill, D)).astype(np.float32)
+        if outliers:
+            x[..., rng.choice(D, 4, replace=False)] *= 10
+        if bf16:
+            x = wl.to_bf16_values(x)
+        dc, hc = new_pair(qmode, B, Hkv, S, D)
+        slots = np.broadcast_to(np.arange(n_fill, dtype=np.int32), (B, n_fill)).copy()
+        kvq.quant_scatter(dev_input(x, bf16), torch.from_numpy(slots).to(DEV), dc)
+        oracle.quant_scatter(hc, x, slots, parallel=True)
+        pairs.append((dc, hc))
+    torch.cuda.synchronize()
+    for dc, hc in pairs:
+        assert_cache_equal(dc, hc, "history")
+    return pairs[0], pairs[1]
+
+
+def run_decode(q_np, K, V, kv_len, q_bf16=True, out_dtype=None, mask=None, sm=None):
+    q = dev_input(q_np, q_bf16)
+    kl = torch.tensor([kv_len], dtype=torch.int32, device=DEV)
+    m = None if mask is None else torch.from_numpy(mask).to(DEV)
+    out = kvq.sdpa_decode(q, K[0], V[0], kv_len=kl, mask=m, sm_scale=sm, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_decode_parity_shapes(qmode, D, G):
+    B, Hkv, S = 2, 2, 700
+    Hq = Hkv * G
+    kv_len = 611                                  # several splits, ragged last step
+    say(f"decode qmode={qmode} D={D} G={G}")
+    K, V = fill_caches(qmode, B, Hkv, S, D, 650, seed=D * 10 + G)
+    q = wl.to_bf16_values(np.random.default_rng(G).standard_normal((B, Hq, 1, D)).astype(np.float32))
+    ref = oracle.sdpa(q, K[1], V[1], kv_len)
+    for od in (torch.bfloat16, torch.float32):
+        out = run_decode(q, K, V, kv_len, out_dtype=od)
+        check_attention(out, ref, f"qmode {qmode} D {D} G {G} out {od}")
+
+
+@pytest.mark.parametrize("kv_len", [1, 2, 31, 32, 33, 127, 128, 129, 1000, 4096])
+def test_decode_kv_len_edges(kv_len):
+    B, Hkv, G, S, D = 1, 2, 4, 4096, 128
+    say(f"decode kv_len={kv_len}")
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, kv_len, seed=kv_len)
+    q = wl.to_bf16_values(np.random.default_rng(kv_len).standard_normal((B, Hkv * G, 1, D)).astype(np.float32))
+    ref = oracle.sdpa(q, K[1], V[1], kv_len)
+    check_attention(run_decode(q, K, V, kv_len, out_dtype=torch.float32), ref, f"kv_len {kv_len}")
+
+
+def test_decode_fp32_query_and_scale():
+    B, Hkv, G, S, D = 1, 2, 2, 256, 64
+    say("decode fp32 q")
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, 96, seed=3, bf16=False)
+    q = np.random.default_rng(5).standard_normal((B, Hkv * G, 1, D)).astype(np.float32)
+    ref = oracle.sdpa(q, K[1], V[1], 96, sm_scale=0.3)
+    out = run_decode(q, K, V, 96, q_bf16=False, out_dtype=torch.float32, sm=0.3)
+    check_attention(out, ref, "fp32 q")
+
+
+def test_decode_query_magnitudes():
+    """Queries far from unit scale (the fp16 prescale must cover them)."""
+    B, Hkv, G, S, D = 1, 1, 4, 300, 128
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, 300, seed=8)
+    for mag in (1e-30, 1e-6, 1e4, 1e30):
+        say(f"decode |q| ~ {mag}")
+        q = wl.to_bf16_values((np.random.default_rng(9).standard_normal((B, Hkv * G, 1, D)) * mag).astype(np.float32))
+        sm = 1.0 / (mag * np.sqrt(D))
+        ref = oracle.sdpa(q, K[1], V[1], 300, sm_scale=sm)
+        check_attention(run_decode(q, K, V, 300, out_dtype=torch.float32, sm=sm), ref, f"|q| {mag}")
+
+
+def test_decode_mask_and_identities():
+    B, Hkv, G, S, D = 2, 2, 4, 1024, 128
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, 1024, seed=11)
+    q = wl.to_bf16_values(np.random.default_rng(12).standard_normal((B, Hkv * G, 1, D)).astype(np.float32))
+    kv_len = 900
+    say("decode identities")
+    base = run_decode(q, K, V, kv_len)
+    # all-zero mask == no mask, bit for bit
+    zero = np.zeros((1, S), np.float32)
+    assert torch.equal(base, run_decode(q, K, V, kv_len, mask=zero))
+    # causal flag is a no-op at Lq = 1
+    qd = dev_input(q, True)
+    kl = torch.tensor([kv_len], dtype=torch.int32, device=DEV)
+    c1 = kvq.sdpa_decode(qd, K[0], V[0], kv_len=kl, mask_is_causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(base, c1)
+    # deterministic
+    assert torch.equal(base, run_decode(q, K, V, kv_len))
+    # garbage past kv_len (codes, NaN scales, zero points) cannot change anything
+    for dc, _ in (K, V):
+        dc.codes[:, :, kv_len:] = torch.randint(0, 256, dc.codes[:, :, kv_len:].shape, dtype=torch.uint8, device=DEV)
+        dc.scales[:, :, kv_len:] = float("nan")
+        dc.zps[:, :, kv_len:] = 77
+    assert torch.equal(base, run_decode(q, K, V, kv_len))
+    # a real mask, per batch row, vs the oracle
+    rng = np.random.default_rng(13)
+    mask = np.where(rng.random((B, S)) < 0.3, -np.inf, 0.0).astype(np.float32)
+    mask[:, 0] = 0.0
+    ref = oracle.sdpa(q, K[1], V[1], kv_len, mask=mask[:, None, :])
+    check_attention(run_decode(q, K, V, kv_len, mask=mask, out_dtype=torch.float32), ref, "mask")
+    # a fully masked row outputs 0
+    full = np.full((1, S), -np.inf, np.float32)
+    out = run_decode(q, K, V, kv_len, mask=full, out_dtype=torch.float32)
+    assert torch.count_nonzero(out) == 0
+
+
+def test_decode_kv_len_out_of_range_is_clamped_and_flagged():
+    B, Hkv, G, S, D = 1, 1, 2, 128, 64
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, 128, seed=21)
+    q = wl.to_bf16_values(np.random.default_rng(22).standard_normal((B, Hkv * G, 1, D)).astype(np.float32))
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say("decode kv_len out of range")
+    out = kvq.sdpa_decode(dev_input(q, True), K[0], V[0], kv_len=torch.tensor([S + 50], dtype=torch.int32, device=DEV),
+                          err_flags=err, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert int(err.item()) == kvq.FLAG_KVLEN
+    check_attention(out, oracle.sdpa(q, K[1], V[1], S), "clamped")

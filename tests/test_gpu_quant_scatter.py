@@ -1,0 +1,109 @@
+"""GPU parity of kvq_quant_scatter against the oracle: every byte of the cache
+(codes, scales, zero points, untouched rows) must be bit-identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_kv_cache_head_amd as kvq
+import quantized_kv_cache_head_amd.workloads as wl
+from _gpu import DEV, assert_cache_equal, dev_input, new_pair, say
+
+pytestmark = pytest.mark.gpu
+
+MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32]
+
+
+def _inputs(rng, B, H, T, D, bf16):
+    x = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    x[..., ::7, :3] *= 30          # outlier channels
+    x[:, :, 1::11] = 0.0           # all-zero vectors
+    x[:, :, 2::13] = np.abs(x[:, :, 2::13])
+    x[:, :, 3::17] *= 1e-6         # tiny
+    x[:, :, 4::19] = -np.abs(x[:, :, 4::19])
+    return wl.to_bf16_values(x) if bf16 else x
+
+
+@pytest.mark.parametrize("qmode", MODES)
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("bf16", [True, False])
+def test_scatter_parity(qmode, D, bf16):
+    rng = np.random.default_rng(100 + qmode * 10 + D)
+    B, H, T, S = 3, 5, 37, 300                    # several blocks and a ragged tail
+    x = _inputs(rng, B, H, T, D, bf16)
+    slots = np.stack([rng.choice(S, T, replace=False) for _ in range(B)]).astype(np.int32)
+    slots[0, 3] = -1
+    slots[1, 5] = -1
+    slots[2, 7] = S + 4                            # out of range: skipped, flagged
+    slots[2, 8] = -7
+    say(f"scatter qmode={qmode} D={D} bf16={bf16}")
+    dc, hc = new_pair(qmode, B, H, S, D)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvq.quant_scatter(dev_input(x, bf16), torch.from_numpy(slots).to(DEV), dc, err_flags=err)
+    torch.cuda.synchronize()
+    flags = oracle.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, f"qmode {qmode} D {D}")
+    assert int(err.item()) == flags == kvq.FLAG_SLOT_RANGE
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH])
+@pytest.mark.parametrize("D", [96, 520, 1024, 8192])
+def test_scatter_other_head_dims(qmode, D):
+    rng = np.random.default_rng(D)
+    B, H, T, S = 1, 2, 5, 9
+    x = _inputs(rng, B, H, T, D, True)
+    slots = np.array([[8, 0, -1, 3, 4]], np.int32)
+    say(f"scatter qmode={qmode} D={D}")
+    dc, hc = new_pair(qmode, B, H, S, D)
+    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, f"D {D}")
+
+
+@pytest.mark.parametrize("qmode", [kvq.FP8E4M3_B32, kvq.MXFP4_B32])
+def test_scatter_block_mode_extremes(qmode):
+    """Blocks at the edges of the encoders: exact ties, saturation, subnormal
+    results, power-of-two amax, all-zero blocks, E8M0 clamp."""
+    g = oracle
+    vals = [0.0, -0.0, 448.0, -448.0, 1.0, 0.5, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 6.0, 5.0, 0.25, 0.75]
+    rows = []
+    for scale in (1.0, 2.0 ** -20, 2.0 ** 20, 1.5, 3e-38, 1e30):
+        r = np.zeros(128, np.float32)
+        r[:len(vals)] = np.array(vals, np.float32) * np.float32(scale)
+        rows.append(r)
+    rows.append(np.zeros(128, np.float32))
+    rows.append(np.full(128, 1e-40, np.float32))
+    x = wl.to_bf16_values(np.stack(rows)[None, None])
+    T = x.shape[2]
+    slots = np.arange(T, dtype=np.int32)[None]
+    say(f"scatter extremes qmode={qmode}")
+    dc, hc = new_pair(qmode, 1, 1, T, 128)
+    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    g.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, "extremes")
+
+
+def test_scatter_strided_input_and_shared_slots():
+    """x given as a strided view ([B, T, H, D] storage) and one slot row shared
+    over the batch."""
+    rng = np.random.default_rng(4)
+    B, H, T, D, S = 2, 4, 9, 128, 64
+    xs = wl.to_bf16_values(rng.standard_normal((B, T, H, D)).astype(np.float32))
+    xv = torch.from_numpy(xs).to(torch.bfloat16).to(DEV).permute(0, 2, 1, 3)      # [B, H, T, D] view
+    slots = np.array([5, 1, 60, -1, 7, 8, 9, 33, 2], np.int32)
+    say("scatter strided")
+    dc, hc = new_pair(kvq.INT8_TH, B, H, S, D)
+    kvq.quant_scatter(xv, torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, np.ascontiguousarray(xs.transpose(0, 2, 1, 3)), slots)
+    assert_cache_equal(dc, hc, "strided")
+
+
+def test_scatter_empty_call_is_noop():
+    dc, hc = new_pair(kvq.INT8_TH, 1, 2, 8, 64)
+    x = torch.zeros((1, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    kvq.quant_scatter(x, torch.zeros((1, 0), dtype=torch.int32, device=DEV), dc)
+    torch.cuda.synchronize()
+    assert_cache_equal(dc, hc, "empty")
