@@ -1,0 +1,432 @@
+"""Benchmark of the quantized KV-cache hot path on one MI355X.
+
+Headline workload (Llama-3-8B-shaped decode layer): B 8, 32 query / 8 KV
+heads, head_dim 128, 8192-slot int8 per-token-head cache filled to kv_len 4096,
+bf16 inputs with 4 of every 128 K/V channels scaled x10.  One step is the
+whole decode-side path: slot position of the new token (full-context layout),
+quantize + scatter of its K and V, and decode attention over the cache
+(split-K with the combine fused in).
+
+The value is decode-attention HBM throughput: the algorithmic bytes the
+attention must move (codes, scales and zero points of slots [0, kv_len) plus
+q and out) divided by the decode kernel's time, measured with HIP events on
+the launch stream.  The step rotates over cache replicas whose total size is
+far above the 256 MB Infinity Cache, so the bytes come from HBM.  The line
+also carries quant-scatter Mtokens/s, the roofline record of the decode
+kernel and the CPU oracle timed on the same step.  Secondary legs time the
+other workloads (sink/ring decode, 4-bit chunked prefill on MFMA, block
+scatter).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_kv_cache_head_amd as kvq  # noqa: E402
+import quantized_kv_cache_head_amd.workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0    # dense fp16 / bf16 MFMA
+DEV = "cuda"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def i32(v):
+    return torch.tensor([v], dtype=torch.int32, device=DEV)
+
+
+class EventTimer:
+    """Pairs of HIP events on the launch stream; mean milliseconds per pair."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+
+
+# --------------------------------------------------------------------------
+# Headline: Llama-3-8B-shaped decode step
+# --------------------------------------------------------------------------
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one decode-attention call: K and V codes, fp32
+    scales and int8 zero points of slots [0, kv_len), q and out (bf16)."""
+    rows = w.B * w.Hkv * w.kv_len
+    return 2 * rows * (w.D + 4 + 1) + 2 * w.B * w.Hq * w.D * 2
+
+
+def scatter_bytes(w) -> int:
+    """Algorithmic bytes of the quant-scatter of one new token (K and V):
+    bf16 inputs read, codes + scale + zero point written, the slot read."""
+    rows = w.B * w.Hkv
+    return 2 * rows * (w.D * 2 + w.D + 4 + 1) + 4
+
+
+class Llama8BStep:
+    def __init__(self, replicas: int):
+        w = self.w = wl.LLAMA8B
+        log(f"[bench] generating inputs B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} S={w.S} kv_len={w.kv_len}")
+        k_np, v_np = wl.llama8b_kv(w)
+        self.k_np, self.v_np = k_np, v_np
+        kb = torch.from_numpy(k_np).to(torch.bfloat16).to(DEV)
+        vb = torch.from_numpy(v_np).to(torch.bfloat16).to(DEV)
+        self.q_np = wl.llama8b_q(w)
+        self.q = torch.from_numpy(self.q_np).to(torch.bfloat16).to(DEV)
+        hist = w.kv_len - 1
+        self.k_new = kb[:, :, hist:hist + 1]
+        self.v_new = vb[:, :, hist:hist + 1]
+        slots = torch.arange(hist, dtype=torch.int32, device=DEV)
+        self.K, self.V = [], []
+        for r in range(replicas):
+            K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
+            V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
+            kvq.quant_scatter(kb[:, :, :hist], slots, K)
+            kvq.quant_scatter(vb[:, :, :hist], slots, V)
+            self.K.append(K)
+            self.V.append(V)
+        del kb, vb
+        self.start_pos = i32(hist)
+        self.kv_len = i32(w.kv_len)
+        self.slot = torch.empty(1, dtype=torch.int32, device=DEV)
+        self.out = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.bfloat16, device=DEV)
+        self.ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
+        self.replica_bytes = self.K[0].nbytes() + self.V[0].nbytes()
+        torch.cuda.synchronize()
+
+    def step(self, r, t_scatter=None, t_decode=None):
+        K, V = self.K[r], self.V[r]
+        s = t_scatter.start() if t_scatter else None
+        kvq.positions_full(self.start_pos, 1, self.w.S, self.slot)
+        kvq.quant_scatter(self.k_new, self.slot, K)
+        kvq.quant_scatter(self.v_new, self.slot, V)
+        if t_scatter:
+            t_scatter.stop(s)
+        d = t_decode.start() if t_decode else None
+        kvq.sdpa_decode(self.q, K, V, kv_len=self.kv_len, out=self.out, workspace=self.ws)
+        if t_decode:
+            t_decode.stop(d)
+
+
+def oracle_step(st: Llama8BStep, hk, hv, parity_out=None):
+    """The oracle on one step: quant-scatter of the new token into its
+    (pre-filled) caches and attention over all B x Hq rows."""
+    import oracle
+    w = st.w
+    hist = w.kv_len - 1
+    slot = np.array([hist], np.int32)
+    t0 = time.perf_counter()
+    oracle.quant_scatter(hk, st.k_np[:, :, hist:hist + 1], slot)
+    oracle.quant_scatter(hv, st.v_np[:, :, hist:hist + 1], slot)
+    out = oracle.sdpa(st.q_np, hk, hv, w.kv_len)
+    return time.perf_counter() - t0, out
+
+
+def cpu_baseline(st: Llama8BStep, gpu_out, budget_s=10.0):
+    import oracle
+    w = st.w
+    hist = w.kv_len - 1
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    log(f"[bench] oracle: quantizing the history on {cores} host threads")
+    hk = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    hv = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    slots = np.arange(hist, dtype=np.int32)
+    oracle.quant_scatter(hk, st.k_np[:, :, :hist], slots, parallel=True)
+    oracle.quant_scatter(hv, st.v_np[:, :, :hist], slots, parallel=True)
+    times = []
+    out = None
+    while sum(times) < budget_s and len(times) < 50:
+        dt, out = oracle_step(st, hk, hv)
+        times.append(dt)
+        log(f"[bench] oracle step {len(times)}: {dt:.2f} s")
+    t = float(np.mean(times))
+    ref = out
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    err = float(np.abs(g - ref).max())
+    return {
+        "value": round(decode_bytes(w) / t / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{len(times)} full decode steps of the headline workload (quant-scatter of the new "
+                   f"K/V token + fp64 attention over all {w.B}x{w.Hq} query rows, kv_len {w.kv_len}); "
+                   f"{t:.3f} s per step"),
+    }, err, ref
+
+
+# --------------------------------------------------------------------------
+# Roofline traffic from committed PMC summaries
+# --------------------------------------------------------------------------
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("sdpa_decode.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "quantized_kv_cache_head_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from profiles/decode_llama8b_traffic.json
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a copy-kernel calibration);
+    None when missing or taken on another version of the kernel source."""
+    p = os.path.join(ROOT, "profiles", "decode_llama8b_traffic.json")
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+# Secondary legs
+# --------------------------------------------------------------------------
+
+def time_ms(fn, iters=20, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def leg_block_scatter():
+    w = wl.BLOCKSCATTER
+    x_np, slots_np = wl.blockscatter_inputs(w)
+    x = torch.from_numpy(x_np).to(torch.bfloat16).to(DEV)[None, None]
+    slots = torch.from_numpy(slots_np).to(DEV)
+    res = {}
+    valid = int((slots_np >= 0).sum())
+    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
+        caches = [kvq.Cache.empty(mode, 1, 1, w.n_slots, w.d).sentinel_fill() for _ in range(8)]
+        it = iter(range(10 ** 9))
+        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8]), iters=40)
+        rb = w.d if mode == kvq.FP8E4M3_B32 else w.d // 2
+        sb = (w.d // 32) * (4 if mode == kvq.FP8E4M3_B32 else 1)
+        nbytes = w.bs * 4 + valid * (w.d * 2 + rb + sb)
+        res[name] = {"us": round(ms * 1e3, 3), "mtok_s": round(w.bs / ms / 1e3, 1),
+                     "gbs": round(nbytes / ms / 1e6, 1)}
+    return res
+
+
+def leg_sink_ring():
+    w = wl.SINKRING
+    res = {}
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1003)
+    p = w.last_pos
+    for name, sink, window in (("sink", w.sink, w.window), ("ring", 0, w.ring_window)):
+        S = sink + window
+        K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+        V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+        cp = torch.full((S,), -1, dtype=torch.int32, device=DEV)
+        # steady state at position p: the cache holds positions p-S+1 .. p-1
+        hist = torch.randn((w.B, w.Hkv, S, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        sm = torch.empty(S, dtype=torch.int32, device=DEV)
+        if sink:
+            kvq.positions_with_sink(i32(0), sink, sink, window, sm[:sink], cp)
+            kvq.positions_with_sink(i32(p - window + 1), window, sink, window, sm[sink:], cp)
+        else:
+            kvq.positions_ring(i32(p - window + 1), window, window, sm, cp)
+        kvq.quant_scatter(hist, sm, K)
+        kvq.quant_scatter(hist, sm, V)
+        q = torch.randn((w.B, w.Hq, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        knew = torch.randn((w.B, w.Hkv, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        start, kvl = i32(p), i32(min(p + 1, S))
+        slot = torch.empty(1, dtype=torch.int32, device=DEV)
+        mask = torch.empty((1, S), dtype=torch.float32, device=DEV)
+        out = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.bfloat16, device=DEV)
+        ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, S, w.D)
+
+        def step():
+            if sink:
+                kvq.positions_with_sink(start, 1, sink, window, slot, cp)
+            else:
+                kvq.positions_ring(start, 1, window, slot, cp)
+            kvq.quant_scatter(knew, slot, K)
+            kvq.quant_scatter(knew, slot, V)
+            kvq.build_mask(cp, start, 1, sink, window, mask)
+            kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+
+        def dec():
+            kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+
+        step_ms = time_ms(step, iters=50)
+        dec_ms = time_ms(dec, iters=50)
+        nbytes = 2 * w.B * w.Hkv * S * (w.D + 5) + 2 * w.B * w.Hq * w.D * 2 + S * 4
+        res[name] = {"step_us": round(step_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
+                     "decode_gbs": round(nbytes / dec_ms / 1e6, 1), "note": "cache planes L2/MALL-warm"}
+    return res
+
+
+def leg_long_prefill():
+    w = wl.LONGPREFILL
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1004)
+    K = kvq.Cache.empty(kvq.UINT4_TH, w.B, w.Hkv, w.S, w.D)
+    V = kvq.Cache.empty(kvq.UINT4_TH, w.B, w.Hkv, w.S, w.D)
+    blk = 8192
+    for j0 in range(0, w.S, blk):
+        x = torch.randn((w.B, w.Hkv, blk, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        sl = torch.arange(j0, j0 + blk, dtype=torch.int32, device=DEV)
+        kvq.quant_scatter(x, sl, K)
+        kvq.quant_scatter(x, sl, V)
+    xc = torch.randn((w.B, w.Hkv, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+    res = {}
+    for end in w.chunk_ends:
+        q = torch.randn((w.B, w.Hq, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        kvl = i32(end)
+        out = torch.empty_like(q)
+        sl = torch.arange(end - w.Lq, end, dtype=torch.int32, device=DEV)
+        sc_ms = time_ms(lambda: kvq.quant_scatter(xc, sl, K), iters=20)
+        ms = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=5, warmup=1)
+        Lq = w.Lq
+        pairs = Lq * (end - Lq) + Lq * (Lq + 1) // 2
+        flops = 4.0 * w.D * w.Hq * pairs
+        tfs = flops / ms / 1e9
+        sc_bytes = w.Hkv * w.Lq * (w.D * 2 + w.D // 2 + 5) + w.Lq * 4
+        res[f"kv_len_{end}"] = {"prefill_ms": round(ms, 3), "tflops": round(tfs, 1),
+                                "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4),
+                                "chunk_scatter_us": round(sc_ms * 1e3, 2),
+                                "chunk_scatter_gbs": round(sc_bytes / sc_ms / 1e6, 1)}
+    return res
+
+
+# --------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (PMC calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part "
+                                   "of this build (see the sharding notes in the design document)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    kvq.lib()
+    torch.cuda.set_device(0)
+
+    st = Llama8BStep(args.replicas)
+    w = st.w
+    R = args.replicas
+    log(f"[bench] {R} replicas x {st.replica_bytes / 2**20:.0f} MiB of cache planes")
+    for i in range(args.warmup):
+        st.step(i % R)
+    torch.cuda.synchronize()
+
+    t_sc, t_dec = EventTimer(), EventTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.step(i % R, t_sc, t_dec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    dec_ms = t_dec.mean_ms()
+    sc_ms = t_sc.mean_ms()
+    gbs = decode_bytes(w) / dec_ms / 1e6
+    tokens = w.B
+    log(f"[bench] decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), scatter+positions {sc_ms * 1e3:.2f} us, "
+        f"step {ms_per_step * 1e3:.2f} us")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=DEV)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    traffic = measured_traffic()
+    result = {
+        "metric": "quantized-KV decode attention HBM GB/s (% of peak); quant-scatter Mtokens/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 cache codes, bf16 q/out, fp32 accumulation",
+        "data": "synthetic (seeded N(0,1), 4 of every 128 K/V channels x10)",
+        "config": {"workload": "llama3-8b-shaped decode layer", "batch": w.B, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "n_slots": w.S, "kv_len": w.kv_len,
+                   "cache": "int8 per-token-head affine", "replicas": R,
+                   "replica_mib": round(st.replica_bytes / 2**20, 1)},
+        "decode_us": round(dec_ms * 1e3, 3),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
+                          "tokens_per_step": tokens, "bytes": scatter_bytes(w),
+                          "note": "positions + K and V quant-scatter of the new token"},
+        "roofline": {"bound": "hbm", "kernel": "sdpa_decode_split (split-K + fused combine)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": decode_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        base, err, _ = cpu_baseline(st, st.out)
+        result["cpu_baseline"] = base
+        result["parity_max_abs_err_vs_oracle"] = err
+    if not args.no_secondary:
+        log("[bench] secondary legs")
+        sec = {}
+        sec["block_scatter_16384x128"] = leg_block_scatter()
+        log("[bench] block scatter done")
+        sec["sink_ring_decode_p6000"] = leg_sink_ring()
+        log("[bench] sink/ring done")
+        sec["long_prefill_uint4_d256"] = leg_long_prefill()
+        log("[bench] long prefill done")
+        result["secondary"] = sec
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

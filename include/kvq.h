@@ -169,8 +169,9 @@ size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int 
  * mask: NULL or fp32 [B, n_slots] with batch stride mask_stride_b (0 shares
  *   one row); values 0 or -inf.  mask_is_causal is accepted for symmetry with
  *   prefill: at Lq = 1 the causal bound is kv_len itself.
- * workspace: device buffer of kvq_sdpa_decode_workspace_bytes() bytes
- *   (contents need no initialisation).
+ * workspace: device buffer of kvq_sdpa_decode_workspace_bytes() bytes for the
+ *   per-split partial results (contents need no initialisation).  Calls that
+ *   overlap in time (different streams) need separate workspaces.
  * Supported D: 64, 128, 256; Hq / heads in {1, 2, 4, 8}. */
 kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
                            const kvq_cache* k, const kvq_cache* v,

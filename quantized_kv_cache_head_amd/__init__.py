@@ -225,6 +225,11 @@ def sdpa_decode_workspace_bytes(B, Hq, Hkv, n_slots, D) -> int:
     return int(lib().kvq_sdpa_decode_workspace_bytes(B, Hq, Hkv, n_slots, D))
 
 
+def decode_workspace(B, Hq, Hkv, n_slots, D, device="cuda"):
+    """A workspace for sdpa_decode (per-split partial results)."""
+    return torch.zeros(sdpa_decode_workspace_bytes(B, Hq, Hkv, n_slots, D), dtype=torch.uint8, device=device)
+
+
 def sdpa_decode(q, k: Cache, v: Cache, kv_len=None, mask=None, sm_scale=None, out=None,
                 out_dtype=None, workspace=None, err_flags=None, mask_is_causal=False, stream=None):
     """kvq_sdpa_decode: q [B, Hq, 1, D]; returns out [B, Hq, 1, D]."""
@@ -237,8 +242,7 @@ def sdpa_decode(q, k: Cache, v: Cache, kv_len=None, mask=None, sm_scale=None, ou
     if out is None:
         out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
     if workspace is None:
-        nb = sdpa_decode_workspace_bytes(B, Hq, k.H, k.S, D)
-        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(B, Hq, k.H, k.S, D, q.device)
     msb = 0
     if mask is not None:
         if mask.dtype != torch.float32 or not mask.is_contiguous():

@@ -144,7 +144,9 @@ kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_
     return KVQ_OK;
 }
 
-size_t decode_ws_bytes(int B, int Hq, int splits, int D) {
+// Partial outputs [B, Hq, splits, D] and (m, l) [B, Hq, splits, 2], fp32.
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int splits, int D) {
+    (void)Hkv;
     return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
 }
 
@@ -157,8 +159,8 @@ int decode_splits_any(int B, int Hkv, int S, int D) {
 }  // namespace
 
 KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D) {
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16) return 0;
-    return decode_ws_bytes(B, Hq, decode_splits_any(B, Hkv, n_slots, D), D);
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16 || Hq % Hkv) return 0;
+    return decode_ws_bytes(B, Hq, Hkv, decode_splits_any(B, Hkv, n_slots, D), D);
 }
 
 KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
@@ -172,7 +174,7 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
     const int D = k->head_dim;
     const int nsplit = kvq::decode_splits(B, k->heads, k->n_slots, D, k->qmode);
-    const size_t need = decode_ws_bytes(B, Hq, nsplit, D);
+    const size_t need = decode_ws_bytes(B, Hq, k->heads, nsplit, D);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
     kvq::DecodeLaunch L;
     L.q = q;

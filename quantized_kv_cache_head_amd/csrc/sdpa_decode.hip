@@ -24,11 +24,18 @@
 //  * p . v: fp32 FMA on v_cvt_f32_ubyte of the codes; p is folded with the
 //    row's scale, the zero point and offset are removed through one running
 //    correction per head.
-//  * Each lane keeps an online softmax (m, l) for its row group with lazy
-//    rescaling (only when a score exceeds the running max by 8 in log2
-//    units, a wave-uniform branch); the row groups, then the waves, are
-//    merged at the end and one partial (m, l, o[D]) per (b, head, split) goes
-//    to the workspace.  A combine kernel merges the splits.
+//  * Each lane keeps an online softmax (m, l) for its row group.  Rows go in
+//    blocks of NB steps: the K and V loads of a block are issued together
+//    (bytes in flight without extra waves), the block's scores stay in
+//    registers, the running max moves once per block (one unconditional
+//    rescale, no data-dependent branch), then p * v is accumulated; the
+//    row groups, then the waves, are
+//    merged at the end (common max, then a reduce-scatter of the
+//    accumulators with lane-swap permutes) and one partial (m, l, o[D]) per
+//    (b, head, split) goes to the workspace; a small combine kernel merges the
+//    splits (a separate launch: merging inside the split kernel would need a
+//    device-scope release/acquire per workgroup, which on this multi-XCD part
+//    writes back and invalidates L2).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -124,8 +131,60 @@ __device__ __forceinline__ void codes_to_f32(const uint4 w, float out[U4 ? 32 : 
     }
 }
 
+// Cross-lane helpers.  DPP controls: quad_perm [1,0,3,2] (xor 1), quad_perm
+// [2,3,0,1] (xor 2), row_half_mirror (lane i <-> 7 - i within 8), row_mirror
+// (i <-> 15 - i within 16), row_ror:8 (xor 8 within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140, DPP_ROR8 = 0x128;
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16); every lane gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+    if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+    if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+    if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
+    return v;
+}
+
+// One reduce-scatter level across lanes that differ in lane bit O (O = 32,
+// 16, 8, 4, 2): pairs (x, y) of the current value list; lanes with the bit
+// clear keep x + partner.x, lanes with it set keep y + partner.y.
+template <int O>
+__device__ __forceinline__ float rs_pair(float x, float y, int lane) {
+    if constexpr (O == 32) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (O == 16) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    } else if constexpr (O == 8) {
+        const float sx = x + dpp<DPP_ROR8>(x), sy = y + dpp<DPP_ROR8>(y);
+        return (lane & 8) ? sy : sx;
+    } else {
+        const float sx = x + __shfl_xor(x, O, 64), sy = y + __shfl_xor(y, O, 64);
+        return (lane & O) ? sy : sx;
+    }
+}
+
+// Reduce-scatter of N values per lane over the lanes that differ in bits
+// [LO, 64): afterwards lane l holds values [blk * N / K, (blk + 1) * N / K)
+// summed, K = 64 / LO groups, blk = l / LO.  The result overwrites v[0..N/K).
+template <int N, int O, int LO>
+__device__ __forceinline__ void reduce_scatter(float* v, int lane) {
+    if constexpr (O >= LO) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) v[i] = rs_pair<O>(v[i], v[i + N / 2], lane);
+        reduce_scatter<N / 2, O / 2, LO>(v, lane);
+    }
+}
+
 template <int D, bool U4, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
+    constexpr int NB = G * (U4 ? 32 : 16) >= 128 ? 2 : 4;    // steps per softmax block
     constexpr int ROWB = U4 ? D / 2 : D;
     constexpr int C = ROWB / 16;          // lanes per row
     constexpr int R = 64 / C;             // rows per wave step
@@ -133,7 +192,9 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr int NP = E / 2;             // fp16 pairs per lane
     constexpr int NL = QBF16 ? 1 : 2;     // fp16 limbs of q
     constexpr float VOFF = U4 ? 0.0f : 128.0f;      // fp32 value = code + VOFF
-    static_assert(C >= 1 && C <= 64 && (64 % C) == 0, "row must split over a power-of-two lane count");
+    constexpr int NV = G * E;                        // accumulators per lane
+    constexpr int NVR = NV / R;                      // after the row-group reduce-scatter
+    static_assert(C >= 2 && C <= 16 && (64 % C) == 0, "row must split over 2..16 lanes");
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -156,31 +217,35 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     const int j0 = split * chunk;
     const int j1 = min(j0 + chunk, kv_len);
 
-    // ---- q: this lane's E elements of each of the G heads -----------------
+    // ---- q: this lane's E elements of each of the G heads, fp16 -----------
+    // One power of two for the G heads brings max|q| into [2^14, 2^15).
     uint32_t qh[G][NL][NP];
-    float csc[G];     // sm_scale * log2(e) * 2^-k
+    float csc;        // sm_scale * log2(e) * 2^-k
     {
-        const int h0 = g * G;
+        float qv[G][E];
+        float mx = 0.0f;
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            float qv[E];
-            const int64_t off = ((int64_t)b * a.Hq + h0 + hh) * D + c * E;
+            const int64_t off = ((int64_t)b * a.Hq + g * G + hh) * D + c * E;
 #pragma unroll
-            for (int i = 0; i < E; i += 8) load8<QBF16>(a.q, off + i, &qv[i]);
-            float mx = 0.0f;
+            for (int i = 0; i < E; i += 8) load8<QBF16>(a.q, off + i, &qv[hh][i]);
 #pragma unroll
-            for (int i = 0; i < E; ++i) mx = fmaxf(mx, fabsf(qv[i]));
-            mx = wave_max_sub<C>(mx);
-            // 2^k brings max|q| into [2^14, 2^15): fp16 holds every element
-            int k = 0;
-            if (mx > 0.0f) {
-                int e;
-                frexpf(mx, &e);        // mx in [2^(e-1), 2^e)
-                k = 15 - e;
-            }
+            for (int i = 0; i < E; ++i) mx = fmaxf(mx, fabsf(qv[hh][i]));
+        }
+#pragma unroll
+        for (int o = 1; o < C; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        int k = 0;
+        if (mx > 0.0f) {
+            int e;
+            frexpf(mx, &e);
+            k = 15 - e;
+        }
+        csc = ldexpf(a.sm_scale_log2, -k);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-                const float x0 = ldexpf(qv[2 * i], k), x1 = ldexpf(qv[2 * i + 1], k);
+                const float x0 = ldexpf(qv[hh][2 * i], k), x1 = ldexpf(qv[hh][2 * i + 1], k);
                 const _Float16 h0v = (_Float16)x0, h1v = (_Float16)x1;
                 half2_t hv = {h0v, h1v};
                 qh[hh][0][i] = __builtin_bit_cast(uint32_t, hv);
@@ -190,99 +255,119 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
                     qh[hh][1][i] = __builtin_bit_cast(uint32_t, lv);
                 }
             }
-            csc[hh] = ldexpf(a.sm_scale_log2, -k);
-        }
     }
 
     // ---- streaming loop ----------------------------------------------------
-    float acc[G][E];
+    // Blocks of NB steps: all K and V loads of a block are issued together,
+    // pass A turns the K rows into scores, the running max moves once per
+    // block (one unconditional rescale), pass B accumulates p * v.
+    float acc[NV];
     float m[G], l[G], corr[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         m[hh] = -__builtin_huge_valf();
         l[hh] = 0.0f;
         corr[hh] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[hh][i] = 0.0f;
     }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
 
-    const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;   // row index base
-    const uint8_t* kbase = a.kc + plane * ROWB + c * 16;
-    const uint8_t* vbase = a.vc + plane * ROWB + c * 16;
-    const float* ksb = a.ks + plane;
-    const float* vsb = a.vs + plane;
-    const int8_t* kzb = a.kz + plane;
-    const int8_t* vzb = a.vz + plane;
+    // Uniform bases (scalar registers) + 32-bit per-lane byte offsets.
+    const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
+    const uint8_t* kbase = a.kc + plane * ROWB;
+    const uint8_t* vbase = a.vc + plane * ROWB;
+    const uint8_t* ksb = reinterpret_cast<const uint8_t*>(a.ks + plane);
+    const uint8_t* vsb = reinterpret_cast<const uint8_t*>(a.vs + plane);
+    const uint8_t* kzb = reinterpret_cast<const uint8_t*>(a.kz + plane);
+    const uint8_t* vzb = reinterpret_cast<const uint8_t*>(a.vz + plane);
     const bool has_mask = a.mask != nullptr;
-    const float* mrow = has_mask ? a.mask + (int64_t)b * a.mask_sb : nullptr;
+    const uint8_t* mrow = reinterpret_cast<const uint8_t*>(a.mask + (has_mask ? (int64_t)b * a.mask_sb : 0));
+    constexpr float NEG_INF = -__builtin_huge_valf();
 
-    for (int jb = j0 + wave * R; jb < j1; jb += STEP) {
-        const int j = jb + r;
-        const bool live = j < j1;
-        const int jl = live ? j : j1 - 1;           // clamped, always a filled row
-        const uint4 kw = *reinterpret_cast<const uint4*>(kbase + (int64_t)jl * ROWB);
-        const uint4 vw = *reinterpret_cast<const uint4*>(vbase + (int64_t)jl * ROWB);
-        const float sk = ksb[jl], sv = vsb[jl];
-        const int zk = kzb[jl], zv = vzb[jl];
-        float madd = 0.0f;
-        if (has_mask) madd = mrow[jl];
-
-        // q . (code) partial over this lane's elements, reduced over the row
-        uint32_t kh[NP];
-        codes_to_h2<U4>(kw, zoff_pair(zk, U4), kh);
-        float s[G];
+    for (int jb0 = j0 + wave * R; jb0 < j1; jb0 += NB * STEP) {
+        uint4 kq[NB], vq[NB];
+        float skq[NB], svq[NB], mq[NB];
+        int zkq[NB], zvq[NB];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float d = 0.0f;
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                d = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][i]), as_h2(kh[i]), d, false);
-                if constexpr (NL == 2) d = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][i]), as_h2(kh[i]), d, false);
-            }
-#pragma unroll
-            for (int o = C / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o, 64);
-            float sc = d * (sk * csc[hh]);
-            sc += madd * 1.4426950408889634f;
-            s[hh] = (live && madd != -__builtin_huge_valf()) ? sc : -__builtin_huge_valf();
+        for (int t = 0; t < NB; ++t) {
+            const int j = jb0 + t * STEP + r;
+            const uint32_t jc = (uint32_t)min(j, j1 - 1);           // a filled row
+            const uint32_t off = jc * ROWB + (uint32_t)c * 16;
+            kq[t] = *reinterpret_cast<const uint4*>(kbase + off);
+            vq[t] = *reinterpret_cast<const uint4*>(vbase + off);
+            skq[t] = *reinterpret_cast<const float*>(ksb + jc * 4);
+            svq[t] = *reinterpret_cast<const float*>(vsb + jc * 4);
+            zkq[t] = *reinterpret_cast<const int8_t*>(kzb + jc);
+            zvq[t] = *reinterpret_cast<const int8_t*>(vzb + jc);
+            const float madd = has_mask ? *reinterpret_cast<const float*>(mrow + jc * 4) * 1.4426950408889634f : 0.0f;
+            mq[t] = j < j1 ? madd : NEG_INF;                        // rows past the slice never count
         }
 
-        // lazy online-softmax update
-        bool upd = false;
+        // pass A: scores (log2 domain) and the block max per head
+        float sc[NB][G];
+        float mb[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) upd |= s[hh] > m[hh] + LAZY_TAU;
-        if (__any(upd)) {
+        for (int hh = 0; hh < G; ++hh) mb[hh] = NEG_INF;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            uint32_t kh[NP];
+            codes_to_h2<U4>(kq[t], zoff_pair(zkq[t], U4), kh);
+            const float ks = skq[t] * csc;
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
-                const float mn = s[hh] > m[hh] + LAZY_TAU ? s[hh] : m[hh];
-                const float al = (m[hh] == -__builtin_huge_valf()) ? 0.0f : exp2f(m[hh] - mn);
-                m[hh] = mn;
-                l[hh] *= al;
-                corr[hh] *= al;
+                float d = 0.0f;
 #pragma unroll
-                for (int i = 0; i < E; ++i) acc[hh][i] *= al;
+                for (int i = 0; i < NP; ++i) {
+                    d = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][i]), as_h2(kh[i]), d, false);
+                    if constexpr (NL == 2) d = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][i]), as_h2(kh[i]), d, false);
+                }
+                d = group_sum<C>(d);
+                sc[t][hh] = fmaf(d, ks, mq[t]);
+                mb[hh] = fmaxf(mb[hh], sc[t][hh]);
             }
         }
-        float vf[E];
-        codes_to_f32<U4>(vw, vf);
-        const float zvo = (float)zv + VOFF;
+
+        // move the running max once per block
+        float msafe[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            const float p = (s[hh] == -__builtin_huge_valf()) ? 0.0f : exp2f(s[hh] - m[hh]);
-            const float pv = p * sv;
-            l[hh] += p;
-            corr[hh] = fmaf(pv, zvo, corr[hh]);
+            const float mn = fmaxf(m[hh], mb[hh]);
+            msafe[hh] = mn == NEG_INF ? 0.0f : mn;
+            const float al = __builtin_amdgcn_exp2f(m[hh] - msafe[hh]);
+            m[hh] = mn;
+            l[hh] *= al;
+            corr[hh] *= al;
 #pragma unroll
-            for (int i = 0; i < E; ++i) acc[hh][i] = fmaf(pv, vf[i], acc[hh][i]);
+            for (int i = 0; i < E; ++i) acc[hh * E + i] *= al;
+        }
+
+        // pass B: p * v
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            float vf[E];
+            codes_to_f32<U4>(vq[t], vf);
+            const float zvo = (float)zvq[t] + VOFF;
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                const float p = __builtin_amdgcn_exp2f(sc[t][hh] - msafe[hh]);
+                const float pv = p * svq[t];
+                l[hh] += p;
+                corr[hh] = fmaf(pv, zvo, corr[hh]);
+#pragma unroll
+                for (int i = 0; i < E; ++i) acc[hh * E + i] = fmaf(pv, vf[i], acc[hh * E + i]);
+            }
         }
     }
 
     // ---- merge the R row groups of the wave --------------------------------
+    // Common max per head, rescale, then reduce-scatter the NV accumulators:
+    // lane (r, c) ends with values [r*NVR, (r+1)*NVR) of its column chunk c.
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
         float mw = m[hh];
 #pragma unroll
         for (int o = C; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
-        const float al = (m[hh] == -__builtin_huge_valf()) ? 0.0f : exp2f(m[hh] - mw);
+        const float al = (m[hh] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mw);
         float lh = l[hh] * al, ch = corr[hh] * al;
 #pragma unroll
         for (int o = C; o < 64; o <<= 1) {
@@ -290,28 +375,25 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
             ch += __shfl_xor(ch, o, 64);
         }
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            float v = acc[hh][i] * al;
-#pragma unroll
-            for (int o = C; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-            acc[hh][i] = v - ch;                      // corrected, unnormalized
-        }
+        for (int i = 0; i < E; ++i) acc[hh * E + i] *= al;
         m[hh] = mw;
         l[hh] = lh;
+        corr[hh] = ch;
     }
+    reduce_scatter<NV, 32, C>(acc, lane);
 
     // ---- merge the waves through LDS and write the partial -----------------
     __shared__ float s_o[DEC_WAVES][G][D];
     __shared__ float s_m[DEC_WAVES][G], s_l[DEC_WAVES][G];
-    if (r == 0) {
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh)
+    for (int i = 0; i < NVR; ++i) {
+        const int v = r * NVR + i;                 // value index: head v / E, element v % E
+        const int hh = v / E;
+        s_o[wave][hh][c * E + v % E] = acc[i] - corr[hh];
+    }
+    if (lane == 0) {
 #pragma unroll
-            for (int i = 0; i < E; ++i) s_o[wave][hh][c * E + i] = acc[hh][i];
-        if (c == 0) {
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
-        }
+        for (int hh = 0; hh < G; ++hh) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
@@ -322,7 +404,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         float o = 0.0f, ll = 0.0f;
 #pragma unroll
         for (int w = 0; w < DEC_WAVES; ++w) {
-            const float al = (s_m[w][hh] == -__builtin_huge_valf()) ? 0.0f : exp2f(s_m[w][hh] - mm);
+            const float al = (s_m[w][hh] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][hh] - mm);
             o = fmaf(s_o[w][hh][d], al, o);
             ll = fmaf(s_l[w][hh], al, ll);
         }
@@ -336,26 +418,46 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
 }
 
 // Merge the splits of one (b, query head): o = sum_s o_s 2^(m_s - m*) / l.
-template <int D, bool OUTBF16>
-__global__ __launch_bounds__(D) void sdpa_decode_combine(const float* part_o, const float* part_ml,
-                                                         int nsplit, void* out) {
-    const int bh = blockIdx.x;
+// The (m, l) pairs go through LDS once; the o loads are independent.
+template <int D>
+__global__ __launch_bounds__(D) void sdpa_decode_combine(const float* part_o, const float* part_ml, int nsplit,
+                                                         void* out, int out_bf16) {
+    constexpr int MAXS = 256;
+    __shared__ float s_w[MAXS];
+    __shared__ float s_inv;
+    const int64_t bh = blockIdx.x;
     const int d = threadIdx.x;
-    const float* ml = part_ml + (int64_t)bh * nsplit * 2;
-    float mm = -__builtin_huge_valf();
-    for (int s = 0; s < nsplit; ++s) mm = fmaxf(mm, ml[2 * s]);
-    float o = 0.0f, ll = 0.0f;
-    if (mm != -__builtin_huge_valf()) {
-        for (int s = 0; s < nsplit; ++s) {
-            const float ms = ml[2 * s];
-            const float al = (ms == -__builtin_huge_valf()) ? 0.0f : exp2f(ms - mm);
-            o = fmaf(part_o[((int64_t)bh * nsplit + s) * D + d], al, o);
-            ll = fmaf(ml[2 * s + 1], al, ll);
+    const float* ml = part_ml + bh * nsplit * 2;
+    if (d < 64) {
+        float mm = -__builtin_huge_valf();
+        for (int sp = d; sp < nsplit; sp += 64) mm = fmaxf(mm, ml[2 * sp]);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
+        float ll = 0.0f;
+        for (int sp = d; sp < nsplit; sp += 64) {
+            const float ms = ml[2 * sp];
+            const float w = (ms == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(ms - mm);
+            s_w[sp] = w;
+            ll = fmaf(ml[2 * sp + 1], w, ll);
         }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ll += __shfl_xor(ll, o, 64);
+        if (d == 0) s_inv = ll > 0.0f ? 1.0f / ll : 0.0f;
     }
-    const float res = ll > 0.0f ? o / ll : 0.0f;
-    if constexpr (OUTBF16) reinterpret_cast<uint16_t*>(out)[(int64_t)bh * D + d] = f32_to_bf16_rne(res);
-    else reinterpret_cast<float*>(out)[(int64_t)bh * D + d] = res;
+    __syncthreads();
+    const float* po = part_o + bh * nsplit * D + d;
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    int sp = 0;
+    for (; sp + 4 <= nsplit; sp += 4) {
+        o0 = fmaf(po[(sp + 0) * D], s_w[sp + 0], o0);
+        o1 = fmaf(po[(sp + 1) * D], s_w[sp + 1], o1);
+        o2 = fmaf(po[(sp + 2) * D], s_w[sp + 2], o2);
+        o3 = fmaf(po[(sp + 3) * D], s_w[sp + 3], o3);
+    }
+    for (; sp < nsplit; ++sp) o0 = fmaf(po[sp * D], s_w[sp], o0);
+    const float res = ((o0 + o1) + (o2 + o3)) * s_inv;
+    if (out_bf16) reinterpret_cast<uint16_t*>(out)[bh * D + d] = f32_to_bf16_rne(res);
+    else reinterpret_cast<float*>(out)[bh * D + d] = res;
 }
 
 int decode_splits(int B, int Hkv, int S, int D, int qmode) {
@@ -363,6 +465,7 @@ int decode_splits(int B, int Hkv, int S, int D, int qmode) {
     const int rows_per_step = (64 / (rowb / 16)) * DEC_WAVES;
     const int pairs = B * Hkv;
     int splits = (1024 + pairs - 1) / pairs;                        // ~4 workgroups per CU
+    if (splits > 256) splits = 256;                                  // combine stages <= 256 (m, l)
     const int max_useful = (S + rows_per_step - 1) / rows_per_step;  // at least one step each
     if (splits > max_useful) splits = max_useful;
     if (splits < 1) splits = 1;
@@ -412,19 +515,11 @@ hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
     const unsigned nbh = (unsigned)(L.B * L.Hq);
+    const int ob = L.out_bf16 ? 1 : 0;
     switch (L.D) {
-    case 64:
-        if (L.out_bf16) hipLaunchKernelGGL((sdpa_decode_combine<64, true>), dim3(nbh), dim3(64), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        else hipLaunchKernelGGL((sdpa_decode_combine<64, false>), dim3(nbh), dim3(64), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        break;
-    case 128:
-        if (L.out_bf16) hipLaunchKernelGGL((sdpa_decode_combine<128, true>), dim3(nbh), dim3(128), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        else hipLaunchKernelGGL((sdpa_decode_combine<128, false>), dim3(nbh), dim3(128), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        break;
-    default:
-        if (L.out_bf16) hipLaunchKernelGGL((sdpa_decode_combine<256, true>), dim3(nbh), dim3(256), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        else hipLaunchKernelGGL((sdpa_decode_combine<256, false>), dim3(nbh), dim3(256), 0, s, L.part_o, L.part_ml, L.nsplit, L.out);
-        break;
+    case 64: hipLaunchKernelGGL((sdpa_decode_combine<64>), dim3(nbh), dim3(64), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
+    case 128: hipLaunchKernelGGL((sdpa_decode_combine<128>), dim3(nbh), dim3(128), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
+    default: hipLaunchKernelGGL((sdpa_decode_combine<256>), dim3(nbh), dim3(256), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
     }
     return hipGetLastError();
 }
