@@ -9,13 +9,15 @@ quantize + scatter of its K and V, and decode attention over the cache
 
 The value is decode-attention HBM throughput: the algorithmic bytes the
 attention must move (codes, scales and zero points of slots [0, kv_len) plus
-q and out) divided by the decode kernel's time, measured with HIP events on
-the launch stream.  The step rotates over cache replicas whose total size is
-far above the 256 MB Infinity Cache, so the bytes come from HBM.  The line
-also carries quant-scatter Mtokens/s, the roofline record of the decode
-kernel and the CPU oracle timed on the same step.  Secondary legs time the
-other workloads (sink/ring decode, 4-bit chunked prefill on MFMA, block
-scatter).
+q and out) divided by the time of one kvq_sdpa_decode call (split kernel +
+combine kernel), measured with HIP events on the launch stream around replays
+of a HIP graph that holds one decode call per cache replica.  Every launch
+goes through HIP graphs, so host launch overhead does not leak into the GPU
+timings.  The step rotates over cache replicas whose total size is far above
+the 256 MB Infinity Cache, so the bytes come from HBM.  The line also carries
+quant-scatter Mtokens/s, the roofline record of the decode call and the CPU
+oracle timed on the same step.  Secondary legs time the other workloads
+(sink/ring decode, 4-bit chunked prefill on MFMA, block scatter).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -50,24 +52,33 @@ def i32(v):
     return torch.tensor([v], dtype=torch.int32, device=DEV)
 
 
-class EventTimer:
-    """Pairs of HIP events on the launch stream; mean milliseconds per pair."""
+def capture(fn):
+    """A HIP graph of whatever fn launches on the current stream."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                    # eager run on the side stream first
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self):
-        self.pairs = []
 
-    def start(self):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, s):
-        e = torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.pairs.append((s, e))
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs]))
+def replay_ms(g, reps: int, per_replay: int = 1) -> float:
+    """Mean milliseconds per call: HIP events around each replay of g, which
+    holds per_replay calls."""
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / per_replay
 
 
 # --------------------------------------------------------------------------
@@ -119,18 +130,17 @@ class Llama8BStep:
         self.replica_bytes = self.K[0].nbytes() + self.V[0].nbytes()
         torch.cuda.synchronize()
 
-    def step(self, r, t_scatter=None, t_decode=None):
-        K, V = self.K[r], self.V[r]
-        s = t_scatter.start() if t_scatter else None
+    def scatter(self, r):
         kvq.positions_full(self.start_pos, 1, self.w.S, self.slot)
-        kvq.quant_scatter(self.k_new, self.slot, K)
-        kvq.quant_scatter(self.v_new, self.slot, V)
-        if t_scatter:
-            t_scatter.stop(s)
-        d = t_decode.start() if t_decode else None
-        kvq.sdpa_decode(self.q, K, V, kv_len=self.kv_len, out=self.out, workspace=self.ws)
-        if t_decode:
-            t_decode.stop(d)
+        kvq.quant_scatter(self.k_new, self.slot, self.K[r])
+        kvq.quant_scatter(self.v_new, self.slot, self.V[r])
+
+    def decode(self, r):
+        kvq.sdpa_decode(self.q, self.K[r], self.V[r], kv_len=self.kv_len, out=self.out, workspace=self.ws)
+
+    def step(self, r):
+        self.scatter(r)
+        self.decode(r)
 
 
 def oracle_step(st: Llama8BStep, hk, hv, parity_out=None):
@@ -210,18 +220,13 @@ def measured_traffic():
 # Secondary legs
 # --------------------------------------------------------------------------
 
-def time_ms(fn, iters=20, warmup=3):
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / iters
+def time_ms(fn, iters=20, inner=10):
+    """Mean milliseconds per call of fn: a HIP graph of `inner` calls, replayed
+    `iters` times between HIP events."""
+    def many():
+        for _ in range(inner):
+            fn()
+    return replay_ms(capture(many), iters, inner)
 
 
 def leg_block_scatter():
@@ -234,7 +239,7 @@ def leg_block_scatter():
     for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
         caches = [kvq.Cache.empty(mode, 1, 1, w.n_slots, w.d).sentinel_fill() for _ in range(8)]
         it = iter(range(10 ** 9))
-        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8]), iters=40)
+        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8]), iters=10, inner=8)
         rb = w.d if mode == kvq.FP8E4M3_B32 else w.d // 2
         sb = (w.d // 32) * (4 if mode == kvq.FP8E4M3_B32 else 1)
         nbytes = w.bs * 4 + valid * (w.d * 2 + rb + sb)
@@ -285,8 +290,8 @@ def leg_sink_ring():
         def dec():
             kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
 
-        step_ms = time_ms(step, iters=50)
-        dec_ms = time_ms(dec, iters=50)
+        step_ms = time_ms(step, iters=10)
+        dec_ms = time_ms(dec, iters=10)
         nbytes = 2 * w.B * w.Hkv * S * (w.D + 5) + 2 * w.B * w.Hq * w.D * 2 + S * 4
         res[name] = {"step_us": round(step_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
                      "decode_gbs": round(nbytes / dec_ms / 1e6, 1), "note": "cache planes L2/MALL-warm"}
@@ -312,8 +317,8 @@ def leg_long_prefill():
         kvl = i32(end)
         out = torch.empty_like(q)
         sl = torch.arange(end - w.Lq, end, dtype=torch.int32, device=DEV)
-        sc_ms = time_ms(lambda: kvq.quant_scatter(xc, sl, K), iters=20)
-        ms = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=5, warmup=1)
+        sc_ms = time_ms(lambda: kvq.quant_scatter(xc, sl, K), iters=5)
+        ms = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=3, inner=1)
         Lq = w.Lq
         pairs = Lq * (end - Lq) + Lq * (Lq + 1) // 2
         flops = 4.0 * w.D * w.Hq * pairs
@@ -356,24 +361,42 @@ def main():
     w = st.w
     R = args.replicas
     log(f"[bench] {R} replicas x {st.replica_bytes / 2**20:.0f} MiB of cache planes")
+    # one graph per replica for the whole step, one graph with a decode call
+    # per replica and one with the scatter phase per replica
+    g_step = [capture(lambda r=r: st.step(r)) for r in range(R)]
+    g_dec = capture(lambda: [st.decode(r) for r in range(R)])
+    g_sc = capture(lambda: [st.scatter(r) for r in range(R)])
+    # a replay must give what the eager calls give
+    st.step(0)
+    torch.cuda.synchronize()
+    eager = st.out.clone()
+    g_step[0].replay()
+    torch.cuda.synchronize()
+    graph_exact = bool(torch.equal(eager, st.out))
     for i in range(args.warmup):
-        st.step(i % R)
+        g_step[i % R].replay()
     torch.cuda.synchronize()
 
-    t_sc, t_dec = EventTimer(), EventTimer()
+    # timed region: K whole steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(args.steps):
-        st.step(i % R, t_sc, t_dec)
+        g_step[i % R].replay()
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
-    dec_ms = t_dec.mean_ms()
-    sc_ms = t_sc.mean_ms()
+    step_ev_ms = ev0.elapsed_time(ev1) / args.steps
+    # per-phase times on the same stream: decode calls and scatter phases
+    reps = max(args.steps // R, 4)
+    dec_ms = replay_ms(g_dec, reps, R)
+    sc_ms = replay_ms(g_sc, reps, R)
     gbs = decode_bytes(w) / dec_ms / 1e6
     tokens = w.B
     log(f"[bench] decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), scatter+positions {sc_ms * 1e3:.2f} us, "
-        f"step {ms_per_step * 1e3:.2f} us")
+        f"step {ms_per_step * 1e3:.2f} us (events {step_ev_ms * 1e3:.2f} us), graph replay exact: {graph_exact}")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -402,11 +425,13 @@ def main():
                    "cache": "int8 per-token-head affine", "replicas": R,
                    "replica_mib": round(st.replica_bytes / 2**20, 1)},
         "decode_us": round(dec_ms * 1e3, 3),
+        "step_us_events": round(step_ev_ms * 1e3, 3),
+        "graph_replay_bitexact": graph_exact,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
                           "tokens_per_step": tokens, "bytes": scatter_bytes(w),
                           "note": "positions + K and V quant-scatter of the new token"},
-        "roofline": {"bound": "hbm", "kernel": "sdpa_decode_split (split-K + fused combine)",
+        "roofline": {"bound": "hbm", "kernel": "kvq_sdpa_decode (sdpa_decode_split + sdpa_decode_combine)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": decode_bytes(w)},

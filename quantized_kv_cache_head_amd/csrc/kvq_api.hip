@@ -150,9 +150,9 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int splits, int D) {
     return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
 }
 
-int decode_splits_any(int B, int Hkv, int S, int D) {
-    const int a = kvq::decode_splits(B, Hkv, S, D, KVQ_INT8_TH);
-    const int b = kvq::decode_splits(B, Hkv, S, D, KVQ_UINT4_TH);
+int decode_splits_any(int B, int Hq, int Hkv, int S, int D) {
+    const int a = kvq::decode_splits(B, Hq, Hkv, S, D, KVQ_INT8_TH);
+    const int b = kvq::decode_splits(B, Hq, Hkv, S, D, KVQ_UINT4_TH);
     return a > b ? a : b;
 }
 
@@ -160,7 +160,7 @@ int decode_splits_any(int B, int Hkv, int S, int D) {
 
 KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16 || Hq % Hkv) return 0;
-    return decode_ws_bytes(B, Hq, Hkv, decode_splits_any(B, Hkv, n_slots, D), D);
+    return decode_ws_bytes(B, Hq, Hkv, decode_splits_any(B, Hq, Hkv, n_slots, D), D);
 }
 
 KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
@@ -173,7 +173,7 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
     if (st != KVQ_OK) return st;
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
     const int D = k->head_dim;
-    const int nsplit = kvq::decode_splits(B, k->heads, k->n_slots, D, k->qmode);
+    const int nsplit = kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode);
     const size_t need = decode_ws_bytes(B, Hq, k->heads, nsplit, D);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
     kvq::DecodeLaunch L;

@@ -150,6 +150,28 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
+// Max / sum over all 64 lanes (every lane gets the result).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<DPP_XOR1>(v));
+    v = fmaxf(v, dpp<DPP_XOR2>(v));
+    v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+    v = fmaxf(v, dpp<DPP_ROR8>(v));
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<DPP_XOR1>(v);
+    v += dpp<DPP_XOR2>(v);
+    v += dpp<DPP_HALF_MIRROR>(v);
+    v += dpp<DPP_ROR8>(v);
+    auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 // One reduce-scatter level across lanes that differ in lane bit O (O = 32,
 // 16, 8, 4, 2): pairs (x, y) of the current value list; lanes with the bit
 // clear keep x + partner.x, lanes with it set keep y + partner.y.
@@ -182,237 +204,374 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
     }
 }
 
+// Geometry of the split kernel, shared by the kernel and the host's choice of
+// the split count.  K pass: KB code bytes per lane (32 when the fp16 q pairs
+// for them fit 64 registers, else 16), CK lanes per row, RK rows per wave
+// step; V pass: 16 code bytes per lane, CV lanes per row, RV rows per step.
+// A split holds at most rows_max rows (scores in LDS); rows_max is a multiple
+// of both workgroup steps.
+struct DecGeom {
+    int rowb, kb, ck, rk, cv, rv, stepk, stepv, stepm, rows_max;
+};
+__host__ __device__ constexpr DecGeom dec_geom(int D, bool u4, int G) {
+    const int rowb = u4 ? D / 2 : D;
+    const int kb = (G * 32 * (u4 ? 2 : 1) <= 128 && rowb >= 64) ? 32 : 16;
+    const int ck = rowb / kb, rk = 64 / ck;
+    const int cv = rowb / 16, rv = 64 / cv;
+    const int stepk = rk * DEC_WAVES, stepv = rv * DEC_WAVES;
+    const int rows_max = 4096 / G < 1024 ? 4096 / G : 1024;
+    return DecGeom{rowb, kb, ck, rk, cv, rv, stepk, stepv, stepk > stepv ? stepk : stepv, rows_max};
+}
+
+// Sum over aligned groups of N lanes (N = 2, 4, 8, 16) valid in the first
+// lane of each group (every level folds into one v_add_f32_dpp).  After the
+// two quad levels, row_half_mirror makes lane 0 of an 8-group read lane 7,
+// which holds the quad sum of lanes 4..7; row_ror:8 (a rotation by half a
+// row, the same in either direction) then adds the other 8-group.
+template <int N>
+__device__ __forceinline__ float group_sum_first(float v) {
+    if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+    if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+    if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+    if constexpr (N >= 16) v += dpp<DPP_ROR8>(v);
+    return v;
+}
+
+// Pointers into global memory.  Keeping the address space explicit makes the
+// compiler emit global_load (counted by vmcnt only) instead of flat_load, which
+// also counts against lgkmcnt: with flat loads in flight every wait for an LDS
+// access would drain the whole prefetch queue.
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
+
+// Wave-uniform global base pointer (held in SGPRs).
+template <typename T>
+__device__ __forceinline__ gptr<T> uniform_ptr(const T* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (gptr<T>)(((uint64_t)hi << 32) | lo);
+}
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16(gptr<uint8_t> base, uint32_t off) {
+    const u32x4_t v = *(gptr<u32x4_t>)(base + off);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+#ifndef KVQ_DEC_PD
+#define KVQ_DEC_PD 3
+#endif
+
 template <int D, bool U4, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
-    constexpr int NB = G * (U4 ? 32 : 16) >= 128 ? 2 : 4;    // steps per softmax block
-    constexpr int ROWB = U4 ? D / 2 : D;
-    constexpr int C = ROWB / 16;          // lanes per row
-    constexpr int R = 64 / C;             // rows per wave step
-    constexpr int E = U4 ? 32 : 16;       // elements per lane
-    constexpr int NP = E / 2;             // fp16 pairs per lane
-    constexpr int NL = QBF16 ? 1 : 2;     // fp16 limbs of q
+    constexpr DecGeom GM = dec_geom(D, U4, G);
+    constexpr int ROWB = GM.rowb;
+    constexpr int EPB = U4 ? 2 : 1;                  // elements per code byte
+    constexpr int KB = GM.kb, CK = GM.ck, RK = GM.rk;
+    constexpr int NPK = KB * EPB / 2;                // fp16 pairs per lane, K pass
+    constexpr int CV = GM.cv, RV = GM.rv;
+    constexpr int EV = 16 * EPB;                     // elements per lane, V pass
+    constexpr int NL = QBF16 ? 1 : 2;                // fp16 limbs of q
     constexpr float VOFF = U4 ? 0.0f : 128.0f;      // fp32 value = code + VOFF
-    constexpr int NV = G * E;                        // accumulators per lane
-    constexpr int NVR = NV / R;                      // after the row-group reduce-scatter
-    static_assert(C >= 2 && C <= 16 && (64 % C) == 0, "row must split over 2..16 lanes");
+    constexpr int NV = G * EV;                       // accumulators per lane
+    constexpr int NVR = NV / RV;                     // after the row-group reduce-scatter
+    constexpr int STEPK = GM.stepk, STEPV = GM.stepv, STEPM = GM.stepm;
+    constexpr int PD = KVQ_DEC_PD;                   // ring depth (steps in flight)
+    constexpr int ROWS_MAX = GM.rows_max;
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr float LOG2E = 1.4426950408889634f;
+    static_assert(CK >= 1 && CK <= 16 && CV >= 2 && CV <= 16, "row split");
+    static_assert(ROWS_MAX % STEPM == 0, "rows_max must hold whole steps");
 
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int c = lane % C;
-    const int r = lane / C;
+    __shared__ float s_row[ROWS_MAX * G];           // scores, then p * scale_v
+    __shared__ float2 s_meta[ROWS_MAX];             // (scale_v, zp_v + VOFF) per row
+    __shared__ uint32_t s_q[G][NL][D / 2];          // q in fp16 pairs
+    __shared__ float s_red[DEC_WAVES][G];
+    __shared__ float s_mx[G], s_l[G], s_corr[G];
+    __shared__ float s_o[DEC_WAVES][G][D];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int split = blockIdx.x;
     const int nsplit = gridDim.x;
     const int g = blockIdx.y;
     const int b = blockIdx.z;
 
+    // ---- q loads go out first ---------------------------------------------
+    constexpr int NQ = G * D;                        // q elements of the group
+    constexpr int QPT = ((NQ + 511) / 512) * 2;      // per thread, even
+    float qv[QPT];
+    {
+        const int64_t qoff = ((int64_t)b * a.Hq + g * G) * D;
+#pragma unroll
+        for (int u = 0; u < QPT; ++u) {
+            const int e = min(tid * QPT + u, NQ - 1);
+            if constexpr (QBF16) qv[u] = bf16_lo(reinterpret_cast<const uint16_t*>(a.q)[qoff + e]);
+            else qv[u] = reinterpret_cast<const float*>(a.q)[qoff + e];
+            qv[u] = tid * QPT + u < NQ ? qv[u] : 0.0f;
+        }
+    }
+
     // ---- kv_len and this workgroup's slice --------------------------------
     int kv_len = a.kv_len ? *a.kv_len : a.S;
     if (kv_len < 1 || kv_len > a.S) {
-        if (a.err && split == 0 && g == 0 && b == 0 && threadIdx.x == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
+        if (a.err && split == 0 && g == 0 && b == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
         kv_len = kv_len < 1 ? 1 : a.S;
     }
-    constexpr int STEP = R * DEC_WAVES;
     int chunk = (kv_len + nsplit - 1) / nsplit;
-    chunk = (chunk + STEP - 1) / STEP * STEP;
+    chunk = (chunk + STEPM - 1) / STEPM * STEPM;    // <= ROWS_MAX by the host's split count
     const int j0 = split * chunk;
-    const int j1 = min(j0 + chunk, kv_len);
+    const int j1 = min(j0 + chunk, kv_len);          // j1 - 1 is a valid row even when empty
+    const int n = max(j1 - j0, 0);
 
-    // ---- q: this lane's E elements of each of the G heads, fp16 -----------
-    // One power of two for the G heads brings max|q| into [2^14, 2^15).
-    uint32_t qh[G][NL][NP];
+    const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
+    const gptr<uint8_t> kbase = uniform_ptr(a.kc + plane * ROWB);
+    const gptr<uint8_t> vbase = uniform_ptr(a.vc + plane * ROWB);
+    const gptr<float> ksb = uniform_ptr(a.ks + plane);
+    const gptr<float> vsb = uniform_ptr(a.vs + plane);
+    const gptr<int8_t> kzb = uniform_ptr(a.kz + plane);
+    const gptr<int8_t> vzb = uniform_ptr(a.vz + plane);
+    const bool has_mask = a.mask != nullptr;
+    // without a mask the mask load reads the key scales (any valid row) and
+    // its value is dropped
+    const gptr<float> mrow = has_mask ? uniform_ptr(a.mask + (int64_t)b * a.mask_sb) : ksb;
+
+    // K pass geometry: lane (rk, ck); rows j0 + (t * DEC_WAVES + wave) * RK + rk
+    const int ck = lane % CK, rk = lane / CK;
+    const int twk = n > wave * RK ? (n - wave * RK + STEPK - 1) / STEPK : 0;
+    // V pass geometry: lane (rv, cv)
+    const int cv = lane % CV, rv = lane / CV;
+    const int twv = n > wave * RV ? (n - wave * RV + STEPV - 1) / STEPV : 0;
+
+    auto krow = [&](int t) { return (uint32_t)min(j0 + (t * DEC_WAVES + wave) * RK + rk, j1 - 1); };
+    auto vrow = [&](int t) { return (uint32_t)min(j0 + (t * DEC_WAVES + wave) * RV + rv, j1 - 1); };
+
+    // ---- K ring: codes and per-row metadata of PD steps ---------------------
+    // Every slot is consumed before it is reloaded (codes after their
+    // conversion, metadata after the step's LDS stores), so a reload targets
+    // the same registers: a copy at the loop edge would wait for the load.
+    uint4 kbuf[PD][KB / 16];
+    int kzr[PD], vzr[PD];
+    float ksr[PD], mkr[PD], vsr[PD];
+    auto fetch_codes = [&](int u, int t) {
+        const uint32_t j = krow(t);
+#pragma unroll
+        for (int c = 0; c < KB / 16; ++c) kbuf[u][c] = load16(kbase, j * ROWB + (uint32_t)ck * KB + 16 * c);
+    };
+    auto fetch_meta = [&](int u, int t) {
+        const uint32_t j = krow(t);
+        kzr[u] = kzb[j];
+        ksr[u] = ksb[j];
+        mkr[u] = mrow[j];
+        vsr[u] = vsb[j];
+        vzr[u] = vzb[j];
+    };
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+        fetch_codes(u, min(u, max(twk - 1, 0)));
+        fetch_meta(u, min(u, max(twk - 1, 0)));
+    }
+
+    // ---- q in fp16, converted cooperatively --------------------------------
+    // k = 0 when max|q| lies in [2^-8, 2^15); otherwise one power of two for
+    // the G heads brings it into [2^14, 2^15).  A power-of-two rescale changes
+    // no rounding, so both give the same result.
     float csc;        // sm_scale * log2(e) * 2^-k
     {
-        float qv[G][E];
         float mx = 0.0f;
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const int64_t off = ((int64_t)b * a.Hq + g * G + hh) * D + c * E;
-#pragma unroll
-            for (int i = 0; i < E; i += 8) load8<QBF16>(a.q, off + i, &qv[hh][i]);
-#pragma unroll
-            for (int i = 0; i < E; ++i) mx = fmaxf(mx, fabsf(qv[hh][i]));
-        }
-#pragma unroll
-        for (int o = 1; o < C; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        for (int u = 0; u < QPT; ++u) mx = fmaxf(mx, fabsf(qv[u]));
+        mx = wave_max(mx);
+        if (lane == 0) s_red[wave][0] = mx;
+        __syncthreads();
+        mx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
         int k = 0;
-        if (mx > 0.0f) {
-            int e;
-            frexpf(mx, &e);
-            k = 15 - e;
+        if (mx > 0.0f && !(mx >= 0x1p-8f && mx < 0x1p15f)) {
+            int ex;
+            frexpf(mx, &ex);
+            k = 15 - ex;
         }
         csc = ldexpf(a.sm_scale_log2, -k);
+        static_assert(QPT % 2 == 0, "q pairs");
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const float x0 = ldexpf(qv[hh][2 * i], k), x1 = ldexpf(qv[hh][2 * i + 1], k);
+        for (int u = 0; u < QPT; u += 2) {
+            const int e = tid * QPT + u;
+            if (e < NQ) {
+                const float x0 = ldexpf(qv[u], k), x1 = ldexpf(qv[u + 1], k);
                 const _Float16 h0v = (_Float16)x0, h1v = (_Float16)x1;
                 half2_t hv = {h0v, h1v};
-                qh[hh][0][i] = __builtin_bit_cast(uint32_t, hv);
+                const int hh = e / D, pr = (e % D) / 2;
+                s_q[hh][0][pr] = __builtin_bit_cast(uint32_t, hv);
                 if constexpr (NL == 2) {
-                    const _Float16 l0 = (_Float16)(x0 - (float)h0v), l1 = (_Float16)(x1 - (float)h1v);
-                    half2_t lv = {l0, l1};
-                    qh[hh][1][i] = __builtin_bit_cast(uint32_t, lv);
+                    half2_t lv = {(_Float16)(x0 - (float)h0v), (_Float16)(x1 - (float)h1v)};
+                    s_q[hh][NL - 1][pr] = __builtin_bit_cast(uint32_t, lv);
                 }
             }
+        }
+    }
+    __syncthreads();                                  // s_q ready
+    uint32_t qh[G][NL][NPK];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int l2 = 0; l2 < NL; ++l2)
+#pragma unroll
+            for (int i = 0; i < NPK; ++i) qh[hh][l2][i] = s_q[hh][l2][ck * NPK + i];
+
+    // ---- pass 1: scores (log2 units, mask added) and V metadata into LDS -----
+    // Steps past this wave's rows run on clamped rows and store nothing.
+    for (int t0 = 0; t0 < twk; t0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int t = t0 + u;
+            uint32_t kh[NPK];
+            const uint32_t zo = zoff_pair(kzr[u], U4);
+#pragma unroll
+            for (int c = 0; c < KB / 16; ++c) codes_to_h2<U4>(kbuf[u][c], zo, kh + c * (NPK / (KB / 16)));
+            __builtin_amdgcn_sched_barrier(0);      // keep the reload after the conversion
+            fetch_codes(u, min(t + PD, twk - 1));
+            float d[G];
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) {
+                float x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][0]), as_h2(kh[0]), 0.0f, false);
+                if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][0]), as_h2(kh[0]), x, false);
+#pragma unroll
+                for (int i = 1; i < NPK; ++i) {
+                    x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][i]), as_h2(kh[i]), x, false);
+                    if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][i]), as_h2(kh[i]), x, false);
+                }
+                d[hh] = group_sum_first<CK>(x);
+            }
+            const int i = (t * DEC_WAVES + wave) * RK + rk;
+            if (ck == 0 && i < n) {
+                const float ks = ksr[u] * csc;
+                const float madd = has_mask ? mkr[u] * LOG2E : 0.0f;
+#pragma unroll
+                for (int hh = 0; hh < G; ++hh) s_row[i * G + hh] = fmaf(d[hh], ks, madd);
+                s_meta[i] = make_float2(vsr[u], (float)vzr[u] + VOFF);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_meta(u, min(t + PD, twk - 1));
+        }
     }
 
-    // ---- streaming loop ----------------------------------------------------
-    // Blocks of NB steps: all K and V loads of a block are issued together,
-    // pass A turns the K rows into scores, the running max moves once per
-    // block (one unconditional rescale), pass B accumulates p * v.
-    float acc[NV];
-    float m[G], l[G], corr[G];
+    // ---- V ring: the first loads go out before the barrier --------------------
+    uint4 vbuf[PD];
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        m[hh] = -__builtin_huge_valf();
-        l[hh] = 0.0f;
-        corr[hh] = 0.0f;
+    for (int u = 0; u < PD; ++u)
+        vbuf[u] = load16(vbase, vrow(min(u, max(twv - 1, 0))) * ROWB + (uint32_t)cv * 16);
+    __syncthreads();                                  // all scores in LDS
+
+    // ---- middle pass: per head, max, p * scale_v, l, zero-point correction ----
+    // wave w owns heads [(w / WPH) * HPW, + HPW) and rows (w % WPH) * 64 + lane
+    // + 64 * WPH * u of the slice
+    constexpr int WPH = DEC_WAVES / G >= 1 ? DEC_WAVES / G : 1;   // waves per head
+    constexpr int HPW = G / DEC_WAVES >= 1 ? G / DEC_WAVES : 1;   // heads per wave
+    {
+        const int h_first = (wave / WPH) * HPW;
+        const int r_first = (wave % WPH) * 64 + lane;
+        float mloc[HPW];
+#pragma unroll
+        for (int hx = 0; hx < HPW; ++hx) mloc[hx] = NEG_INF;
+        for (int i = r_first; i < n; i += 64 * WPH) {
+#pragma unroll
+            for (int hx = 0; hx < HPW; ++hx) mloc[hx] = fmaxf(mloc[hx], s_row[i * G + h_first + hx]);
+        }
+        float msafe[HPW];
+#pragma unroll
+        for (int hx = 0; hx < HPW; ++hx) {
+            float mm = wave_max(mloc[hx]);
+            if constexpr (WPH > 1) {
+                if (lane == 0) s_red[wave][hx] = mm;
+                __syncthreads();
+                mm = NEG_INF;
+#pragma unroll
+                for (int w = 0; w < WPH; ++w) mm = fmaxf(mm, s_red[(wave / WPH) * WPH + w][hx]);
+                __syncthreads();
+            }
+            if ((wave % WPH) == 0 && lane == 0) s_mx[h_first + hx] = mm;
+            msafe[hx] = mm == NEG_INF ? 0.0f : mm;
+        }
+        float lsum[HPW], csum[HPW];
+#pragma unroll
+        for (int hx = 0; hx < HPW; ++hx) { lsum[hx] = 0.0f; csum[hx] = 0.0f; }
+        for (int i = r_first; i < n; i += 64 * WPH) {
+            const float2 mt = s_meta[i];
+#pragma unroll
+            for (int hx = 0; hx < HPW; ++hx) {
+                const int hh = h_first + hx;
+                const float p = __builtin_amdgcn_exp2f(s_row[i * G + hh] - msafe[hx]);
+                const float pv = p * mt.x;
+                lsum[hx] += p;
+                csum[hx] = fmaf(pv, mt.y, csum[hx]);
+                s_row[i * G + hh] = pv;
+            }
+        }
+#pragma unroll
+        for (int hx = 0; hx < HPW; ++hx) {
+            const float lw = wave_sum(lsum[hx]), cw = wave_sum(csum[hx]);
+            if (lane == 0) { s_red[wave][hx] = lw; s_o[wave][hx][0] = cw; }
+        }
     }
+    __syncthreads();                                  // p * scale_v and per-wave sums ready
+    if (tid < G) {
+        const int w0 = (tid / HPW) * WPH, hx = tid % HPW;
+        float lv = 0.0f, cvv = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WPH; ++w) { lv += s_red[w0 + w][hx]; cvv += s_o[w0 + w][hx][0]; }
+        s_l[tid] = lv;
+        s_corr[tid] = cvv;
+    }
+
+    // ---- pass 2: acc += (p * scale_v) * (code + VOFF) ---------------------------
+    // Steps past the slice read a clamped LDS row and use p = 0.
+    float acc[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-
-    // Uniform bases (scalar registers) + 32-bit per-lane byte offsets.
-    const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
-    const uint8_t* kbase = a.kc + plane * ROWB;
-    const uint8_t* vbase = a.vc + plane * ROWB;
-    const uint8_t* ksb = reinterpret_cast<const uint8_t*>(a.ks + plane);
-    const uint8_t* vsb = reinterpret_cast<const uint8_t*>(a.vs + plane);
-    const uint8_t* kzb = reinterpret_cast<const uint8_t*>(a.kz + plane);
-    const uint8_t* vzb = reinterpret_cast<const uint8_t*>(a.vz + plane);
-    const bool has_mask = a.mask != nullptr;
-    const uint8_t* mrow = reinterpret_cast<const uint8_t*>(a.mask + (has_mask ? (int64_t)b * a.mask_sb : 0));
-    constexpr float NEG_INF = -__builtin_huge_valf();
-
-    for (int jb0 = j0 + wave * R; jb0 < j1; jb0 += NB * STEP) {
-        uint4 kq[NB], vq[NB];
-        float skq[NB], svq[NB], mq[NB];
-        int zkq[NB], zvq[NB];
+    const int i_last = max(n - 1, 0);
+    for (int t0 = 0; t0 < twv; t0 += PD) {
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            const int j = jb0 + t * STEP + r;
-            const uint32_t jc = (uint32_t)min(j, j1 - 1);           // a filled row
-            const uint32_t off = jc * ROWB + (uint32_t)c * 16;
-            kq[t] = *reinterpret_cast<const uint4*>(kbase + off);
-            vq[t] = *reinterpret_cast<const uint4*>(vbase + off);
-            skq[t] = *reinterpret_cast<const float*>(ksb + jc * 4);
-            svq[t] = *reinterpret_cast<const float*>(vsb + jc * 4);
-            zkq[t] = *reinterpret_cast<const int8_t*>(kzb + jc);
-            zvq[t] = *reinterpret_cast<const int8_t*>(vzb + jc);
-            const float madd = has_mask ? *reinterpret_cast<const float*>(mrow + jc * 4) * 1.4426950408889634f : 0.0f;
-            mq[t] = j < j1 ? madd : NEG_INF;                        // rows past the slice never count
-        }
-
-        // pass A: scores (log2 domain) and the block max per head
-        float sc[NB][G];
-        float mb[G];
+        for (int u = 0; u < PD; ++u) {
+            const int t = t0 + u;
+            float vf[EV];
+            codes_to_f32<U4>(vbuf[u], vf);
+            __builtin_amdgcn_sched_barrier(0);      // keep the reload after the conversion
+            vbuf[u] = load16(vbase, vrow(min(t + PD, twv - 1)) * ROWB + (uint32_t)cv * 16);
+            // rows past the slice read the last row (finite) and weigh it by 0
+            const int i = (t * DEC_WAVES + wave) * RV + rv;
+            const float live = i < n ? 1.0f : 0.0f;
+            const int ic = min(i, i_last);
+            float pv[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) mb[hh] = NEG_INF;
+            for (int hh = 0; hh < G; ++hh) pv[hh] = s_row[ic * G + hh] * live;
 #pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            uint32_t kh[NP];
-            codes_to_h2<U4>(kq[t], zoff_pair(zkq[t], U4), kh);
-            const float ks = skq[t] * csc;
+            for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                float d = 0.0f;
-#pragma unroll
-                for (int i = 0; i < NP; ++i) {
-                    d = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][i]), as_h2(kh[i]), d, false);
-                    if constexpr (NL == 2) d = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][i]), as_h2(kh[i]), d, false);
-                }
-                d = group_sum<C>(d);
-                sc[t][hh] = fmaf(d, ks, mq[t]);
-                mb[hh] = fmaxf(mb[hh], sc[t][hh]);
-            }
-        }
-
-        // move the running max once per block
-        float msafe[G];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float mn = fmaxf(m[hh], mb[hh]);
-            msafe[hh] = mn == NEG_INF ? 0.0f : mn;
-            const float al = __builtin_amdgcn_exp2f(m[hh] - msafe[hh]);
-            m[hh] = mn;
-            l[hh] *= al;
-            corr[hh] *= al;
-#pragma unroll
-            for (int i = 0; i < E; ++i) acc[hh * E + i] *= al;
-        }
-
-        // pass B: p * v
-#pragma unroll
-        for (int t = 0; t < NB; ++t) {
-            float vf[E];
-            codes_to_f32<U4>(vq[t], vf);
-            const float zvo = (float)zvq[t] + VOFF;
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                const float p = __builtin_amdgcn_exp2f(sc[t][hh] - msafe[hh]);
-                const float pv = p * svq[t];
-                l[hh] += p;
-                corr[hh] = fmaf(pv, zvo, corr[hh]);
-#pragma unroll
-                for (int i = 0; i < E; ++i) acc[hh * E + i] = fmaf(pv, vf[i], acc[hh * E + i]);
-            }
+                for (int e = 0; e < EV; ++e) acc[hh * EV + e] = fmaf(pv[hh], vf[e], acc[hh * EV + e]);
         }
     }
 
-    // ---- merge the R row groups of the wave --------------------------------
-    // Common max per head, rescale, then reduce-scatter the NV accumulators:
-    // lane (r, c) ends with values [r*NVR, (r+1)*NVR) of its column chunk c.
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        float mw = m[hh];
-#pragma unroll
-        for (int o = C; o < 64; o <<= 1) mw = fmaxf(mw, __shfl_xor(mw, o, 64));
-        const float al = (m[hh] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(m[hh] - mw);
-        float lh = l[hh] * al, ch = corr[hh] * al;
-#pragma unroll
-        for (int o = C; o < 64; o <<= 1) {
-            lh += __shfl_xor(lh, o, 64);
-            ch += __shfl_xor(ch, o, 64);
-        }
-#pragma unroll
-        for (int i = 0; i < E; ++i) acc[hh * E + i] *= al;
-        m[hh] = mw;
-        l[hh] = lh;
-        corr[hh] = ch;
-    }
-    reduce_scatter<NV, 32, C>(acc, lane);
-
-    // ---- merge the waves through LDS and write the partial -----------------
-    __shared__ float s_o[DEC_WAVES][G][D];
-    __shared__ float s_m[DEC_WAVES][G], s_l[DEC_WAVES][G];
+    // ---- merge: row groups (reduce-scatter), then waves, then the partial -------
+    reduce_scatter<NV, 32, CV>(acc, lane);
+    __syncthreads();                                  // s_o (used for sums above) free again
 #pragma unroll
     for (int i = 0; i < NVR; ++i) {
-        const int v = r * NVR + i;                 // value index: head v / E, element v % E
-        const int hh = v / E;
-        s_o[wave][hh][c * E + v % E] = acc[i] - corr[hh];
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) { s_m[wave][hh] = m[hh]; s_l[wave][hh] = l[hh]; }
+        const int v = rv * NVR + i;                    // head v / EV, element v % EV
+        s_o[wave][v / EV][cv * EV + v % EV] = acc[i];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    for (int idx = tid; idx < G * D; idx += 256) {
         const int hh = idx / D, d = idx % D;
-        float mm = -__builtin_huge_valf();
+        float o = 0.0f;
 #pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) mm = fmaxf(mm, s_m[w][hh]);
-        float o = 0.0f, ll = 0.0f;
-#pragma unroll
-        for (int w = 0; w < DEC_WAVES; ++w) {
-            const float al = (s_m[w][hh] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][hh] - mm);
-            o = fmaf(s_o[w][hh][d], al, o);
-            ll = fmaf(s_l[w][hh], al, ll);
-        }
+        for (int w = 0; w < DEC_WAVES; ++w) o += s_o[w][hh][d];
         const int64_t ph = ((int64_t)b * a.Hq + g * G + hh) * nsplit + split;
-        a.part_o[ph * D + d] = o;
+        a.part_o[ph * D + d] = o - s_corr[hh];
         if (d == 0) {
-            a.part_ml[ph * 2] = mm;
-            a.part_ml[ph * 2 + 1] = ll;
+            a.part_ml[ph * 2] = s_mx[hh];
+            a.part_ml[ph * 2 + 1] = s_l[hh];
         }
     }
 }
@@ -460,14 +619,16 @@ __global__ __launch_bounds__(D) void sdpa_decode_combine(const float* part_o, co
     else reinterpret_cast<float*>(out)[bh * D + d] = res;
 }
 
-int decode_splits(int B, int Hkv, int S, int D, int qmode) {
-    const int rowb = qmode == QM_UINT4_TH ? D / 2 : D;
-    const int rows_per_step = (64 / (rowb / 16)) * DEC_WAVES;
+int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode) {
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH, Hq / Hkv);
     const int pairs = B * Hkv;
-    int splits = (1024 + pairs - 1) / pairs;                        // ~4 workgroups per CU
-    if (splits > 256) splits = 256;                                  // combine stages <= 256 (m, l)
-    const int max_useful = (S + rows_per_step - 1) / rows_per_step;  // at least one step each
+    int splits = (1024 + pairs - 1) / pairs;                          // ~4 workgroups per CU
+    const int max_useful = (S + gm.stepm - 1) / gm.stepm;             // at least one step each
     if (splits > max_useful) splits = max_useful;
+    // every split, rounded up to whole steps, must fit the LDS row buffer:
+    // ceil(S / splits) <= rows_max suffices because rows_max holds whole steps
+    const int need = (S + gm.rows_max - 1) / gm.rows_max;
+    if (splits < need) splits = need;
     if (splits < 1) splits = 1;
     return splits;
 }
