@@ -153,7 +153,10 @@ kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int
                           int Lq, int sink_size, int window, float* mask_out, void* stream);
 
 /* Workspace bytes kvq_sdpa_decode needs for these sizes (partial softmax
- * states of the split-K pass).  0 on invalid sizes. */
+ * states of the split-K pass).  It is an upper bound valid on any device and
+ * for either affine cache mode (the split count of a launch depends on how
+ * many workgroups the device keeps resident); needs no device.  0 on invalid
+ * sizes. */
 size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D);
 
 /* Decode attention (Lq = 1) over quantized K/V caches ([ABADDON]

@@ -151,8 +151,8 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int splits, int D) {
 }
 
 int decode_splits_any(int B, int Hq, int Hkv, int S, int D) {
-    const int a = kvq::decode_splits(B, Hq, Hkv, S, D, KVQ_INT8_TH);
-    const int b = kvq::decode_splits(B, Hq, Hkv, S, D, KVQ_UINT4_TH);
+    const int a = kvq::decode_splits_max(B, Hq, Hkv, S, D, KVQ_INT8_TH);
+    const int b = kvq::decode_splits_max(B, Hq, Hkv, S, D, KVQ_UINT4_TH);
     return a > b ? a : b;
 }
 
@@ -173,7 +173,7 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
     if (st != KVQ_OK) return st;
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
     const int D = k->head_dim;
-    const int nsplit = kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode);
+    const int nsplit = kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
     const size_t need = decode_ws_bytes(B, Hq, k->heads, nsplit, D);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
     kvq::DecodeLaunch L;

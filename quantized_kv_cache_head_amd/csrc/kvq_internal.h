@@ -47,7 +47,8 @@ struct DecodeLaunch {
     int32_t* err;
 };
 
-int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode);
+int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode);
+int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16);
 hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s);
 
 struct PrefillLaunch {

@@ -8,34 +8,38 @@
 // happens in registers and is never materialized.
 //
 // Mapping on gfx950:
-//  * grid (splits, Hkv, B); a 256-thread workgroup owns one (b, kv head g)
-//    and one contiguous slice of [0, kv_len) whose length is derived on the
-//    device from kv_len, so the launch shape is fixed across steps.
+//  * grid (splits, Hkv, B); a 256-thread workgroup (4 waves) owns one
+//    (b, kv head g) and one contiguous slice of [0, kv_len), derived on the
+//    device from kv_len, so the launch shape is fixed across steps.  The split
+//    count keeps every workgroup resident in one round (the VGPR and LDS use
+//    of the instantiation decides how many fit per CU).
 //  * The G = Hq/Hkv query heads of a KV head are processed together: every
 //    K/V byte is read from HBM once for all of them.
-//  * A KV row of ROWB bytes is split over C = ROWB/16 lanes, 16 bytes per
-//    lane (one dwordx4 load for K, one for V); a wave covers R = 64/C rows
-//    per step and the 4 waves of the workgroup read adjacent rows.
-//  * q . k: codes become exact fp16 integers (code - zp) (a byte permute under
-//    the fp16 exponent of 1024, then one packed fp16 subtraction) and are
-//    multiplied with q (rescaled by a power of two into fp16 range; exact for
-//    bf16 q) by v_dot2_f32_f16 with fp32 accumulation.  fp32 q uses a hi + lo
-//    pair of fp16 limbs.
-//  * p . v: fp32 FMA on v_cvt_f32_ubyte of the codes; p is folded with the
-//    row's scale, the zero point and offset are removed through one running
-//    correction per head.
-//  * Each lane keeps an online softmax (m, l) for its row group.  Rows go in
-//    blocks of NB steps: the K and V loads of a block are issued together
-//    (bytes in flight without extra waves), the block's scores stay in
-//    registers, the running max moves once per block (one unconditional
-//    rescale, no data-dependent branch), then p * v is accumulated; the
-//    row groups, then the waves, are
-//    merged at the end (common max, then a reduce-scatter of the
-//    accumulators with lane-swap permutes) and one partial (m, l, o[D]) per
-//    (b, head, split) goes to the workspace; a small combine kernel merges the
-//    splits (a separate launch: merging inside the split kernel would need a
-//    device-scope release/acquire per workgroup, which on this multi-XCD part
-//    writes back and invalidates L2).
+//  * Per-row metadata of the slice (scales, zero points, mask) is loaded once,
+//    cooperatively, into LDS.
+//  * Pass 1 (q . k): a K row is split over CK lanes of KB bytes each; codes
+//    become exact fp16 integers (code - zp) (a byte permute under the fp16
+//    exponent of 1024, then one packed fp16 subtraction) and meet q (rescaled
+//    by a power of two into fp16 range, exact for bf16 q; fp32 q uses a
+//    hi + lo pair of fp16 limbs) in v_dot2_f32_f16 with fp32 accumulation.
+//    Row dots go to LDS.  The codes stream through a register ring of PD
+//    steps that is refilled right after each slot is converted.
+//  * Middle pass (per head, from LDS): score = dot * scale_k * sm_scale *
+//    log2(e) + mask, the slice maximum m, p = 2^(score - m), l = sum p, and
+//    p * scale_v back to LDS; the zero points enter through one correction
+//    sum per head, sum p * scale_v * (zp + offset).
+//  * Pass 2 (p . v): a V row is split over CV lanes of 16 bytes; fp32 FMA of
+//    p * scale_v on v_cvt_f32_ubyte of the codes; the first PDV steps of the
+//    V ring are issued before the middle pass so the V stream overlaps it.
+//  * Merge: a reduce-scatter of the accumulators across the row groups of a
+//    wave (lane-swap permutes and DPP), then the waves through LDS; one
+//    partial (m, l, o[D]) per (b, head, split) goes to the workspace.  A small
+//    combine kernel merges the splits (a separate launch: merging inside the
+//    split kernel would need a device-scope release/acquire per workgroup,
+//    which on this multi-XCD part writes back and invalidates L2).
+//  * Loads use global (not flat) addressing so that waits for LDS never wait
+//    for loads in flight, and the ring loops have no data-dependent branches:
+//    steps past a wave's rows run on a clamped row and store nothing.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -60,7 +64,7 @@ struct DecodeArgs {
 };
 
 constexpr int DEC_WAVES = 4;
-constexpr float LAZY_TAU = 8.0f;   // rescale threshold in log2 units
+constexpr int DEC_CHUNK_ALIGN = 32;   // split slices start on multiples of 32 rows
 
 __device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
 
@@ -219,7 +223,7 @@ __host__ __device__ constexpr DecGeom dec_geom(int D, bool u4, int G) {
     const int ck = rowb / kb, rk = 64 / ck;
     const int cv = rowb / 16, rv = 64 / cv;
     const int stepk = rk * DEC_WAVES, stepv = rv * DEC_WAVES;
-    const int rows_max = 4096 / G < 1024 ? 4096 / G : 1024;
+    const int rows_max = G <= 4 ? 1024 : 512;
     return DecGeom{rowb, kb, ck, rk, cv, rv, stepk, stepv, stepk > stepv ? stepk : stepv, rows_max};
 }
 
@@ -262,6 +266,9 @@ __device__ __forceinline__ uint4 load16(gptr<uint8_t> base, uint32_t off) {
 #ifndef KVQ_DEC_PD
 #define KVQ_DEC_PD 3
 #endif
+#ifndef KVQ_DEC_PDV
+#define KVQ_DEC_PDV 4
+#endif
 
 template <int D, bool U4, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
@@ -277,15 +284,18 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr int NV = G * EV;                       // accumulators per lane
     constexpr int NVR = NV / RV;                     // after the row-group reduce-scatter
     constexpr int STEPK = GM.stepk, STEPV = GM.stepv, STEPM = GM.stepm;
-    constexpr int PD = KVQ_DEC_PD;                   // ring depth (steps in flight)
+    constexpr int PD = KVQ_DEC_PD;                   // K ring depth (steps in flight)
+    constexpr int PDV = KVQ_DEC_PDV;                 // V ring depth: issued before the middle pass
     constexpr int ROWS_MAX = GM.rows_max;
+    constexpr int RPT = ROWS_MAX / 256;              // metadata rows per thread
     constexpr float NEG_INF = -__builtin_huge_valf();
     constexpr float LOG2E = 1.4426950408889634f;
     static_assert(CK >= 1 && CK <= 16 && CV >= 2 && CV <= 16, "row split");
-    static_assert(ROWS_MAX % STEPM == 0, "rows_max must hold whole steps");
+    static_assert(ROWS_MAX % DEC_CHUNK_ALIGN == 0 && ROWS_MAX % 256 == 0, "rows_max alignment");
 
-    __shared__ float s_row[ROWS_MAX * G];           // scores, then p * scale_v
-    __shared__ float2 s_meta[ROWS_MAX];             // (scale_v, zp_v + VOFF) per row
+    __shared__ float s_row[ROWS_MAX * G];           // q.k dots, scores, then p * scale_v
+    __shared__ float4 s_meta[ROWS_MAX];             // (scale_k, mask, scale_v, zp_v + VOFF)
+    __shared__ uint32_t s_kzo[ROWS_MAX];            // fp16 pair of the key zero-point offset
     __shared__ uint32_t s_q[G][NL][D / 2];          // q in fp16 pairs
     __shared__ float s_red[DEC_WAVES][G];
     __shared__ float s_mx[G], s_l[G], s_corr[G];
@@ -321,10 +331,11 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         kv_len = kv_len < 1 ? 1 : a.S;
     }
     int chunk = (kv_len + nsplit - 1) / nsplit;
-    chunk = (chunk + STEPM - 1) / STEPM * STEPM;    // <= ROWS_MAX by the host's split count
+    chunk = (chunk + DEC_CHUNK_ALIGN - 1) / DEC_CHUNK_ALIGN * DEC_CHUNK_ALIGN;   // <= ROWS_MAX (host)
     const int j0 = split * chunk;
     const int j1 = min(j0 + chunk, kv_len);          // j1 - 1 is a valid row even when empty
     const int n = max(j1 - j0, 0);
+    const int i_last = max(n - 1, 0);                // slice-relative clamp for LDS rows
 
     const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
     const gptr<uint8_t> kbase = uniform_ptr(a.kc + plane * ROWB);
@@ -338,6 +349,19 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     // its value is dropped
     const gptr<float> mrow = has_mask ? uniform_ptr(a.mask + (int64_t)b * a.mask_sb) : ksb;
 
+    // ---- per-row metadata of the slice: one row per thread and round --------
+    float m_ks[RPT], m_mk[RPT], m_vs[RPT];
+    int m_kz[RPT], m_vz[RPT];
+#pragma unroll
+    for (int u = 0; u < RPT; ++u) {
+        const uint32_t j = (uint32_t)min(j0 + tid + 256 * u, j1 - 1);
+        m_ks[u] = ksb[j];
+        m_mk[u] = mrow[j];
+        m_vs[u] = vsb[j];
+        m_kz[u] = kzb[j];
+        m_vz[u] = vzb[j];
+    }
+
     // K pass geometry: lane (rk, ck); rows j0 + (t * DEC_WAVES + wave) * RK + rk
     const int ck = lane % CK, rk = lane / CK;
     const int twk = n > wave * RK ? (n - wave * RK + STEPK - 1) / STEPK : 0;
@@ -348,33 +372,19 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     auto krow = [&](int t) { return (uint32_t)min(j0 + (t * DEC_WAVES + wave) * RK + rk, j1 - 1); };
     auto vrow = [&](int t) { return (uint32_t)min(j0 + (t * DEC_WAVES + wave) * RV + rv, j1 - 1); };
 
-    // ---- K ring: codes and per-row metadata of PD steps ---------------------
-    // Every slot is consumed before it is reloaded (codes after their
-    // conversion, metadata after the step's LDS stores), so a reload targets
-    // the same registers: a copy at the loop edge would wait for the load.
+    // ---- K ring: the first PD steps' codes go out before any arithmetic -------
+    // Every slot is consumed (converted) before it is reloaded, so a reload
+    // targets the same registers: a copy at the loop edge would wait for it.
     uint4 kbuf[PD][KB / 16];
-    int kzr[PD], vzr[PD];
-    float ksr[PD], mkr[PD], vsr[PD];
     auto fetch_codes = [&](int u, int t) {
         const uint32_t j = krow(t);
 #pragma unroll
         for (int c = 0; c < KB / 16; ++c) kbuf[u][c] = load16(kbase, j * ROWB + (uint32_t)ck * KB + 16 * c);
     };
-    auto fetch_meta = [&](int u, int t) {
-        const uint32_t j = krow(t);
-        kzr[u] = kzb[j];
-        ksr[u] = ksb[j];
-        mkr[u] = mrow[j];
-        vsr[u] = vsb[j];
-        vzr[u] = vzb[j];
-    };
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-        fetch_codes(u, min(u, max(twk - 1, 0)));
-        fetch_meta(u, min(u, max(twk - 1, 0)));
-    }
+    for (int u = 0; u < PD; ++u) fetch_codes(u, min(u, max(twk - 1, 0)));
 
-    // ---- q in fp16, converted cooperatively --------------------------------
+    // ---- q in fp16, converted cooperatively; metadata into LDS ----------------
     // k = 0 when max|q| lies in [2^-8, 2^15); otherwise one power of two for
     // the G heads brings it into [2^14, 2^15).  A power-of-two rescale changes
     // no rounding, so both give the same result.
@@ -385,6 +395,12 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         for (int u = 0; u < QPT; ++u) mx = fmaxf(mx, fabsf(qv[u]));
         mx = wave_max(mx);
         if (lane == 0) s_red[wave][0] = mx;
+#pragma unroll
+        for (int u = 0; u < RPT; ++u) {
+            const int i = tid + 256 * u;
+            s_meta[i] = make_float4(m_ks[u], has_mask ? m_mk[u] * LOG2E : 0.0f, m_vs[u], (float)m_vz[u] + VOFF);
+            s_kzo[i] = zoff_pair(m_kz[u], U4);
+        }
         __syncthreads();
         mx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
         int k = 0;
@@ -411,7 +427,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
             }
         }
     }
-    __syncthreads();                                  // s_q ready
+    __syncthreads();                                  // s_q, s_meta, s_kzo ready
     uint32_t qh[G][NL][NPK];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -420,64 +436,89 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < NPK; ++i) qh[hh][l2][i] = s_q[hh][l2][ck * NPK + i];
 
-    // ---- pass 1: scores (log2 units, mask added) and V metadata into LDS -----
-    // Steps past this wave's rows run on clamped rows and store nothing.
-    for (int t0 = 0; t0 < twk; t0 += PD) {
+    // ---- pass 1: q . (code - zp) per row into LDS -----------------------------
+    auto k_step = [&](int u, int t, bool reload) {
+        const int i = (t * DEC_WAVES + wave) * RK + rk;
+        const uint32_t zo = s_kzo[min(i, i_last)];
+        uint32_t kh[NPK];
 #pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int t = t0 + u;
-            uint32_t kh[NPK];
-            const uint32_t zo = zoff_pair(kzr[u], U4);
-#pragma unroll
-            for (int c = 0; c < KB / 16; ++c) codes_to_h2<U4>(kbuf[u][c], zo, kh + c * (NPK / (KB / 16)));
-            __builtin_amdgcn_sched_barrier(0);      // keep the reload after the conversion
+        for (int c = 0; c < KB / 16; ++c) codes_to_h2<U4>(kbuf[u][c], zo, kh + c * (NPK / (KB / 16)));
+        if (reload) {
+            __builtin_amdgcn_sched_barrier(0);        // keep the reload after the conversion
             fetch_codes(u, min(t + PD, twk - 1));
-            float d[G];
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) {
-                float x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][0]), as_h2(kh[0]), 0.0f, false);
-                if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][0]), as_h2(kh[0]), x, false);
-#pragma unroll
-                for (int i = 1; i < NPK; ++i) {
-                    x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][i]), as_h2(kh[i]), x, false);
-                    if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][i]), as_h2(kh[i]), x, false);
-                }
-                d[hh] = group_sum_first<CK>(x);
-            }
-            const int i = (t * DEC_WAVES + wave) * RK + rk;
-            if (ck == 0 && i < n) {
-                const float ks = ksr[u] * csc;
-                const float madd = has_mask ? mkr[u] * LOG2E : 0.0f;
-#pragma unroll
-                for (int hh = 0; hh < G; ++hh) s_row[i * G + hh] = fmaf(d[hh], ks, madd);
-                s_meta[i] = make_float2(vsr[u], (float)vzr[u] + VOFF);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            fetch_meta(u, min(t + PD, twk - 1));
         }
-    }
-
-    // ---- V ring: the first loads go out before the barrier --------------------
-    uint4 vbuf[PD];
+        float d[G];
 #pragma unroll
-    for (int u = 0; u < PD; ++u)
-        vbuf[u] = load16(vbase, vrow(min(u, max(twv - 1, 0))) * ROWB + (uint32_t)cv * 16);
-    __syncthreads();                                  // all scores in LDS
+        for (int hh = 0; hh < G; ++hh) {
+            float x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][0]), as_h2(kh[0]), 0.0f, false);
+            if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][0]), as_h2(kh[0]), x, false);
+#pragma unroll
+            for (int e = 1; e < NPK; ++e) {
+                x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][e]), as_h2(kh[e]), x, false);
+                if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][e]), as_h2(kh[e]), x, false);
+            }
+            d[hh] = group_sum_first<CK>(x);
+        }
+        if (ck == 0 && i < n) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh) s_row[i * G + hh] = d[hh];
+        }
+    };
+    int t0 = 0;
+    for (; t0 + PD <= twk; t0 += PD) {               // whole ring rounds
+#pragma unroll
+        for (int u = 0; u < PD; ++u) k_step(u, t0 + u, true);
+    }
+#pragma unroll
+    for (int u = 0; u < PD - 1; ++u)                 // the rest: already in the ring
+        if (t0 + u < twk) k_step(u, t0 + u, false);
 
-    // ---- middle pass: per head, max, p * scale_v, l, zero-point correction ----
+    // ---- V ring: the first PDV steps go out before the barrier, so the V
+    // stream runs while the middle pass computes
+    uint4 vbuf[PDV];
+#pragma unroll
+    for (int u = 0; u < PDV; ++u)
+        vbuf[u] = load16(vbase, vrow(min(u, max(twv - 1, 0))) * ROWB + (uint32_t)cv * 16);
+    __syncthreads();                                  // all dots in LDS
+
+    // ---- middle pass: per head, scores, max, p * scale_v, l, zp correction ----
     // wave w owns heads [(w / WPH) * HPW, + HPW) and rows (w % WPH) * 64 + lane
     // + 64 * WPH * u of the slice
     constexpr int WPH = DEC_WAVES / G >= 1 ? DEC_WAVES / G : 1;   // waves per head
     constexpr int HPW = G / DEC_WAVES >= 1 ? G / DEC_WAVES : 1;   // heads per wave
     {
+        // rows go in groups of MB per lane: the LDS reads of a group are issued
+        // together (clamped to the last row; rows past the slice are masked)
+        constexpr int MB = 4;
+        constexpr int RS = 64 * WPH;                  // row stride between a lane's rows
         const int h_first = (wave / WPH) * HPW;
         const int r_first = (wave % WPH) * 64 + lane;
         float mloc[HPW];
 #pragma unroll
         for (int hx = 0; hx < HPW; ++hx) mloc[hx] = NEG_INF;
-        for (int i = r_first; i < n; i += 64 * WPH) {
+        for (int i0 = r_first; i0 < n; i0 += MB * RS) {
+            float2 mt[MB];
+            float dv[MB][HPW];
 #pragma unroll
-            for (int hx = 0; hx < HPW; ++hx) mloc[hx] = fmaxf(mloc[hx], s_row[i * G + h_first + hx]);
+            for (int u = 0; u < MB; ++u) {
+                const int ii = min(i0 + u * RS, i_last);
+                const float4 m4 = s_meta[ii];
+                mt[u] = make_float2(m4.x * csc, m4.y);
+#pragma unroll
+                for (int hx = 0; hx < HPW; ++hx) dv[u][hx] = s_row[ii * G + h_first + hx];
+            }
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                const int i = i0 + u * RS;
+                if (i < n) {
+#pragma unroll
+                    for (int hx = 0; hx < HPW; ++hx) {
+                        const float sc = fmaf(dv[u][hx], mt[u].x, mt[u].y);
+                        s_row[i * G + h_first + hx] = sc;
+                        mloc[hx] = fmaxf(mloc[hx], sc);
+                    }
+                }
+            }
         }
         float msafe[HPW];
 #pragma unroll
@@ -497,16 +538,30 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         float lsum[HPW], csum[HPW];
 #pragma unroll
         for (int hx = 0; hx < HPW; ++hx) { lsum[hx] = 0.0f; csum[hx] = 0.0f; }
-        for (int i = r_first; i < n; i += 64 * WPH) {
-            const float2 mt = s_meta[i];
+        for (int i0 = r_first; i0 < n; i0 += MB * RS) {
+            float2 mt[MB];
+            float sv[MB][HPW];
 #pragma unroll
-            for (int hx = 0; hx < HPW; ++hx) {
-                const int hh = h_first + hx;
-                const float p = __builtin_amdgcn_exp2f(s_row[i * G + hh] - msafe[hx]);
-                const float pv = p * mt.x;
-                lsum[hx] += p;
-                csum[hx] = fmaf(pv, mt.y, csum[hx]);
-                s_row[i * G + hh] = pv;
+            for (int u = 0; u < MB; ++u) {
+                const int ii = min(i0 + u * RS, i_last);
+                const float4 m4 = s_meta[ii];
+                mt[u] = make_float2(m4.z, m4.w);
+#pragma unroll
+                for (int hx = 0; hx < HPW; ++hx) sv[u][hx] = s_row[ii * G + h_first + hx];
+            }
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                const int i = i0 + u * RS;
+                if (i < n) {
+#pragma unroll
+                    for (int hx = 0; hx < HPW; ++hx) {
+                        const float p = __builtin_amdgcn_exp2f(sv[u][hx] - msafe[hx]);
+                        const float pv = p * mt[u].x;
+                        lsum[hx] += p;
+                        csum[hx] = fmaf(pv, mt[u].y, csum[hx]);
+                        s_row[i * G + h_first + hx] = pv;
+                    }
+                }
             }
         }
 #pragma unroll
@@ -526,40 +581,44 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     }
 
     // ---- pass 2: acc += (p * scale_v) * (code + VOFF) ---------------------------
-    // Steps past the slice read a clamped LDS row and use p = 0.
     float acc[NV];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
-    const int i_last = max(n - 1, 0);
-    for (int t0 = 0; t0 < twv; t0 += PD) {
-#pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int t = t0 + u;
-            float vf[EV];
-            codes_to_f32<U4>(vbuf[u], vf);
-            __builtin_amdgcn_sched_barrier(0);      // keep the reload after the conversion
-            vbuf[u] = load16(vbase, vrow(min(t + PD, twv - 1)) * ROWB + (uint32_t)cv * 16);
-            // rows past the slice read the last row (finite) and weigh it by 0
-            const int i = (t * DEC_WAVES + wave) * RV + rv;
-            const float live = i < n ? 1.0f : 0.0f;
-            const int ic = min(i, i_last);
-            float pv[G];
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh) pv[hh] = s_row[ic * G + hh] * live;
-#pragma unroll
-            for (int hh = 0; hh < G; ++hh)
-#pragma unroll
-                for (int e = 0; e < EV; ++e) acc[hh * EV + e] = fmaf(pv[hh], vf[e], acc[hh * EV + e]);
+    for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
+    auto v_step = [&](int u, int t, bool reload) {
+        float vf[EV];
+        codes_to_f32<U4>(vbuf[u], vf);
+        if (reload) {
+            __builtin_amdgcn_sched_barrier(0);        // keep the reload after the conversion
+            vbuf[u] = load16(vbase, vrow(min(t + PDV, twv - 1)) * ROWB + (uint32_t)cv * 16);
         }
+        // rows past the slice read the last row (finite) and weigh it by 0
+        const int i = (t * DEC_WAVES + wave) * RV + rv;
+        const float live = i < n ? 1.0f : 0.0f;
+        const int ic = min(i, i_last);
+        float pv[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) pv[hh] = s_row[ic * G + hh] * live;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int e = 0; e < EV; ++e) acc[hh * EV + e] = fmaf(pv[hh], vf[e], acc[hh * EV + e]);
+    };
+    t0 = 0;
+    for (; t0 + PDV <= twv; t0 += PDV) {
+#pragma unroll
+        for (int u = 0; u < PDV; ++u) v_step(u, t0 + u, true);
     }
+#pragma unroll
+    for (int u = 0; u < PDV - 1; ++u)
+        if (t0 + u < twv) v_step(u, t0 + u, false);
 
     // ---- merge: row groups (reduce-scatter), then waves, then the partial -------
     reduce_scatter<NV, 32, CV>(acc, lane);
     __syncthreads();                                  // s_o (used for sums above) free again
 #pragma unroll
-    for (int i = 0; i < NVR; ++i) {
-        const int v = rv * NVR + i;                    // head v / EV, element v % EV
-        s_o[wave][v / EV][cv * EV + v % EV] = acc[i];
+    for (int e = 0; e < NVR; ++e) {
+        const int v = rv * NVR + e;                    // head v / EV, element v % EV
+        s_o[wave][v / EV][cv * EV + v % EV] = acc[e];
     }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += 256) {
@@ -576,61 +635,130 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     }
 }
 
-// Merge the splits of one (b, query head): o = sum_s o_s 2^(m_s - m*) / l.
-// The (m, l) pairs go through LDS once; the o loads are independent.
+// Merge the splits of one (b, query head): o = sum_s o_s 2^(m_s - m*) / l
+// with l = sum_s l_s 2^(m_s - m*).  The splits go in chunks of CH whose o and
+// (m, l) loads are all issued before any arithmetic (one memory round trip
+// per chunk); a running maximum rescales the sums between chunks.  A row
+// with no visible key (every m_s = -inf) gives 0.
 template <int D>
-__global__ __launch_bounds__(D) void sdpa_decode_combine(const float* part_o, const float* part_ml, int nsplit,
-                                                         void* out, int out_bf16) {
-    constexpr int MAXS = 256;
-    __shared__ float s_w[MAXS];
-    __shared__ float s_inv;
+__global__ __launch_bounds__(D) void sdpa_decode_combine(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml, int nsplit,
+                                                         void* __restrict__ out, int out_bf16) {
+    constexpr int CH = 16;
+    constexpr float NEG_INF = -__builtin_huge_valf();
     const int64_t bh = blockIdx.x;
     const int d = threadIdx.x;
-    const float* ml = part_ml + bh * nsplit * 2;
-    if (d < 64) {
-        float mm = -__builtin_huge_valf();
-        for (int sp = d; sp < nsplit; sp += 64) mm = fmaxf(mm, ml[2 * sp]);
+    const gptr<float> po = uniform_ptr(part_o + bh * nsplit * D);
+    const gptr<float> pml = uniform_ptr(part_ml + bh * nsplit * 2);
+    float m = NEG_INF, l = 0.0f, acc = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += CH) {
+        float mv[CH], lv[CH], ov[CH];
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mm = fmaxf(mm, __shfl_xor(mm, o, 64));
-        float ll = 0.0f;
-        for (int sp = d; sp < nsplit; sp += 64) {
-            const float ms = ml[2 * sp];
-            const float w = (ms == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(ms - mm);
-            s_w[sp] = w;
-            ll = fmaf(ml[2 * sp + 1], w, ll);
+        for (int u = 0; u < CH; ++u) {
+            const uint32_t sp = (uint32_t)min(s0 + u, nsplit - 1);
+            mv[u] = pml[2 * sp];
+            lv[u] = pml[2 * sp + 1];
+            ov[u] = po[sp * D + d];
         }
+        __builtin_amdgcn_sched_barrier(0);            // every load of the chunk is issued first
+        float mn = m;
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) ll += __shfl_xor(ll, o, 64);
-        if (d == 0) s_inv = ll > 0.0f ? 1.0f / ll : 0.0f;
+        for (int u = 0; u < CH; ++u)
+            if (s0 + u < nsplit) mn = fmaxf(mn, mv[u]);
+        const float r = m == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m - mn);
+        acc *= r;
+        l *= r;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const bool live = s0 + u < nsplit && mv[u] != NEG_INF;
+            const float w = live ? __builtin_amdgcn_exp2f(mv[u] - mn) : 0.0f;
+            acc = fmaf(w, ov[u], acc);
+            l = fmaf(w, lv[u], l);
+        }
+        m = mn;
     }
-    __syncthreads();
-    const float* po = part_o + bh * nsplit * D + d;
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-    int sp = 0;
-    for (; sp + 4 <= nsplit; sp += 4) {
-        o0 = fmaf(po[(sp + 0) * D], s_w[sp + 0], o0);
-        o1 = fmaf(po[(sp + 1) * D], s_w[sp + 1], o1);
-        o2 = fmaf(po[(sp + 2) * D], s_w[sp + 2], o2);
-        o3 = fmaf(po[(sp + 3) * D], s_w[sp + 3], o3);
-    }
-    for (; sp < nsplit; ++sp) o0 = fmaf(po[sp * D], s_w[sp], o0);
-    const float res = ((o0 + o1) + (o2 + o3)) * s_inv;
+    const float res = l > 0.0f ? acc / l : 0.0f;
     if (out_bf16) reinterpret_cast<uint16_t*>(out)[bh * D + d] = f32_to_bf16_rne(res);
     else reinterpret_cast<float*>(out)[bh * D + d] = res;
 }
 
-int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode) {
+// Upper bound on the split count (sizes the workspace without a device):
+// enough splits for 4096 resident workgroups, and at least enough that every
+// slice fits the LDS row buffer.
+int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode) {
     const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH, Hq / Hkv);
     const int pairs = B * Hkv;
-    int splits = (1024 + pairs - 1) / pairs;                          // ~4 workgroups per CU
-    const int max_useful = (S + gm.stepm - 1) / gm.stepm;             // at least one step each
+    const int max_useful = (S + DEC_CHUNK_ALIGN - 1) / DEC_CHUNK_ALIGN;
+    int splits = (4096 + pairs - 1) / pairs;
     if (splits > max_useful) splits = max_useful;
-    // every split, rounded up to whole steps, must fit the LDS row buffer:
-    // ceil(S / splits) <= rows_max suffices because rows_max holds whole steps
+    const int need = (S + gm.rows_max - 1) / gm.rows_max;   // ceil(S / splits) <= rows_max
+    return splits > need ? splits : need;
+}
+
+template <int D, bool U4, int G, bool QBF16>
+static const void* split_kernel() { return reinterpret_cast<const void*>(&sdpa_decode_split<D, U4, G, QBF16>); }
+
+static const void* split_kernel_for(int D, bool u4, int G, bool qbf16) {
+#define KVQ_SK(DD, UU)                                                                          \
+    switch (G) {                                                                                \
+    case 1: return qbf16 ? split_kernel<DD, UU, 1, true>() : split_kernel<DD, UU, 1, false>(); \
+    case 2: return qbf16 ? split_kernel<DD, UU, 2, true>() : split_kernel<DD, UU, 2, false>(); \
+    case 4: return qbf16 ? split_kernel<DD, UU, 4, true>() : split_kernel<DD, UU, 4, false>(); \
+    default: return qbf16 ? split_kernel<DD, UU, 8, true>() : split_kernel<DD, UU, 8, false>(); \
+    }
+    if (D == 64) { if (u4) { KVQ_SK(64, true) } else { KVQ_SK(64, false) } }
+    if (D == 128) { if (u4) { KVQ_SK(128, true) } else { KVQ_SK(128, false) } }
+    if (u4) { KVQ_SK(256, true) } else { KVQ_SK(256, false) }
+#undef KVQ_SK
+}
+
+// Workgroups of one split-kernel instantiation that fit on the current device
+// at once: per CU, the smaller of the VGPR limit (512 registers per lane of a
+// SIMD in granules of 8; a 4-wave workgroup puts one wave on each SIMD) and
+// the LDS limit, times the CU count.  0 when the runtime cannot tell.
+static int resident_workgroups(int D, bool u4, int G, bool qbf16) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    const int key = ((D == 64 ? 0 : D == 128 ? 1 : 2) * 2 + (u4 ? 1 : 0)) * 8 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3) * 2 +
+                    (qbf16 ? 1 : 0);
+    static int cache[64][48];                         // 0 = not known yet; benign races
+    int v = cache[dev][key];
+    if (v > 0) return v;
+    hipFuncAttributes fa;
+    int cus = 0, lds_cu = 0;
+    if (hipFuncGetAttributes(&fa, split_kernel_for(D, u4, G, qbf16)) != hipSuccess || fa.numRegs <= 0 ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        lds_cu <= 0)
+        lds_cu = 160 * 1024;
+    const int granule = (fa.numRegs + 7) / 8 * 8;
+    int per_cu = 512 / granule;
+    if (per_cu > 8) per_cu = 8;
+    if (fa.sharedSizeBytes > 0) {
+        const int by_lds = lds_cu / (int)fa.sharedSizeBytes;
+        if (by_lds < per_cu) per_cu = by_lds;
+    }
+    if (per_cu < 1) per_cu = 1;
+    v = per_cu * cus;
+    cache[dev][key] = v;
+    return v;
+}
+
+// Split count of a launch: as many splits as keep every workgroup resident in
+// one round (a second, partly filled round would run with little latency
+// hiding), within [rows fit in LDS, decode_splits_max].
+int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16) {
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH, Hq / Hkv);
+    const int pairs = B * Hkv;
+    const int hi = decode_splits_max(B, Hq, Hkv, S, D, qmode);
     const int need = (S + gm.rows_max - 1) / gm.rows_max;
+    int resident = resident_workgroups(D, qmode == QM_UINT4_TH, Hq / Hkv, qbf16);
+    if (resident <= 0) resident = 1024;
+    int splits = resident / pairs;
     if (splits < need) splits = need;
-    if (splits < 1) splits = 1;
-    return splits;
+    if (splits > hi) splits = hi;
+    return splits < 1 ? 1 : splits;
 }
 
 template <int D, bool U4, int G, bool QBF16>

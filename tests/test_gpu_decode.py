@@ -140,3 +140,16 @@ def test_decode_kv_len_out_of_range_is_clamped_and_flagged():
     torch.cuda.synchronize()
     assert int(err.item()) == kvq.FLAG_KVLEN
     check_attention(out, oracle.sdpa(q, K[1], V[1], S), "clamped")
+
+
+def test_decode_many_splits():
+    """One (batch, KV head) pair over a long cache: the split count grows to
+    hundreds, so the combine walks many chunks of splits."""
+    B, Hkv, G, S, D = 1, 1, 4, 16384, 128
+    kv_len = 16000
+    say(f"decode many splits S={S} kv_len={kv_len}")
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, kv_len, seed=21)
+    q = wl.to_bf16_values(np.random.default_rng(21).standard_normal((B, Hkv * G, 1, D)).astype(np.float32))
+    ref = oracle.sdpa(q, K[1], V[1], kv_len)
+    for od in (torch.bfloat16, torch.float32):
+        check_attention(run_decode(q, K, V, kv_len, out_dtype=od), ref, f"many splits out {od}")
