@@ -1,0 +1,211 @@
+"""The five workloads at their full sizes, HIP path against the oracle.
+
+Every cache write is compared byte for byte; attention is held to the
+attention gate (fp32 output within 2e-3 of the fp64 oracle, bf16 output
+within 2e-3 plus half a bf16 ulp).  The long-context prefill compares 64
+sampled query rows (all heads) per chunk, including every tile boundary, since
+the oracle's full fp64 pass over 2048 rows x 131072 keys would take minutes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_kv_cache_head_amd as kvq
+import quantized_kv_cache_head_amd.workloads as wl
+from _gpu import DEV, assert_cache_equal, check_attention, dev_input, new_pair, say
+
+pytestmark = pytest.mark.gpu
+
+
+def i32(v):
+    return torch.tensor([v], dtype=torch.int32, device=DEV)
+
+
+def test_tiny_prefill_then_decode_steps():
+    """Tiny full-context int8 cache: 64-token causal prefill (fp32), then 32
+    decode steps at positions 64..95, each checked."""
+    w = wl.TINY
+    say("tiny: prefill 64 + 32 decode steps")
+    dk, hk = new_pair(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    dv, hv = new_pair(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    q, k, v = wl.tiny_prefill(w)
+    slots = np.arange(w.prefill, dtype=np.int32)
+    sd = torch.from_numpy(slots).to(DEV)
+    kvq.quant_scatter(dev_input(k, False), sd, dk)
+    kvq.quant_scatter(dev_input(v, False), sd, dv)
+    oracle.quant_scatter(hk, k, slots)
+    oracle.quant_scatter(hv, v, slots)
+    torch.cuda.synchronize()
+    assert_cache_equal(dk, hk, "tiny prefill K")
+    assert_cache_equal(dv, hv, "tiny prefill V")
+    out = kvq.sdpa_prefill(dev_input(q, False), dk, dv, kv_len=i32(w.prefill), causal=True,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attention(out, oracle.sdpa(q, hk, hv, w.prefill, causal=True), "tiny prefill")
+
+    slot = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
+    for p in range(w.prefill, w.prefill + w.decode_steps):
+        q, k, v = wl.tiny_decode(p, w)
+        kvq.positions_full(i32(p), 1, w.S, slot)
+        kvq.quant_scatter(dev_input(k, False), slot, dk)
+        kvq.quant_scatter(dev_input(v, False), slot, dv)
+        sm, flags = oracle.positions_full(p, 1, w.S)
+        assert flags == 0 and sm[0] == p
+        oracle.quant_scatter(hk, k, sm)
+        oracle.quant_scatter(hv, v, sm)
+        out = kvq.sdpa_decode(dev_input(q, False), dk, dv, kv_len=i32(p + 1), out_dtype=torch.float32,
+                              workspace=ws)
+        torch.cuda.synchronize()
+        assert int(slot.item()) == p
+        check_attention(out, oracle.sdpa(q, hk, hv, p + 1), f"tiny decode p={p}")
+    assert_cache_equal(dk, hk, "tiny final K")
+    assert_cache_equal(dv, hv, "tiny final V")
+
+
+def test_llama8b_decode_layer_full():
+    """Llama-3-8B-shaped layer: history 0..4094 and the new token at 4095
+    quantized on both sides (bit-exact), then decode over kv_len 4096."""
+    w = wl.LLAMA8B
+    say("llama8b decode layer: full size")
+    k, v = wl.llama8b_kv(w)
+    q = wl.llama8b_q(w)
+    hist = w.kv_len - 1
+    dk, hk = new_pair(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    dv, hv = new_pair(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    slots = np.arange(hist, dtype=np.int32)
+    sd = torch.from_numpy(slots).to(DEV)
+    kvq.quant_scatter(dev_input(k[:, :, :hist], True), sd, dk)
+    kvq.quant_scatter(dev_input(v[:, :, :hist], True), sd, dv)
+    oracle.quant_scatter(hk, k[:, :, :hist], slots, parallel=True)
+    oracle.quant_scatter(hv, v[:, :, :hist], slots, parallel=True)
+    slot = torch.empty(1, dtype=torch.int32, device=DEV)
+    kvq.positions_full(i32(hist), 1, w.S, slot)
+    kvq.quant_scatter(dev_input(k[:, :, hist:], True), slot, dk)
+    kvq.quant_scatter(dev_input(v[:, :, hist:], True), slot, dv)
+    sm, flags = oracle.positions_full(hist, 1, w.S)
+    assert flags == 0
+    oracle.quant_scatter(hk, k[:, :, hist:], sm)
+    oracle.quant_scatter(hv, v[:, :, hist:], sm)
+    torch.cuda.synchronize()
+    assert_cache_equal(dk, hk, "llama8b K")
+    assert_cache_equal(dv, hv, "llama8b V")
+    ref = oracle.sdpa(q, hk, hv, w.kv_len)
+    for od in (torch.bfloat16, torch.float32):
+        out = kvq.sdpa_decode(dev_input(q, True), dk, dv, kv_len=i32(w.kv_len), out_dtype=od)
+        torch.cuda.synchronize()
+        check_attention(out, ref, f"llama8b decode out {od}")
+
+
+CHECKPOINTS = (0, 3, 4, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 6000)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("layout", ["sink", "ring"])
+def test_sink_ring_stream(layout):
+    """Decode through positions 0..6000 of a sink (4 + 2044) or ring (1024)
+    cache: positions, quant-scatter and cache_positions every step (checked
+    at the checkpoints), mask and attention at the checkpoints."""
+    w = wl.SINKRING
+    sink, window = (w.sink, w.window) if layout == "sink" else (0, w.ring_window)
+    S = sink + window
+    say(f"{layout} stream: S={S} positions 0..{w.last_pos}")
+    dk, hk = new_pair(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+    dv, hv = new_pair(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+    cp_dev = torch.full((S,), -1, dtype=torch.int32, device=DEV)
+    cp = np.full(S, -1, np.int32)
+    slot = torch.empty(1, dtype=torch.int32, device=DEV)
+    mask_dev = torch.empty((1, S), dtype=torch.float32, device=DEV)
+    ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, S, w.D)
+    for p in range(w.last_pos + 1):
+        q, k, v = wl.sinkring_step(p, w)
+        start = i32(p)
+        if sink:
+            kvq.positions_with_sink(start, 1, sink, window, slot, cp_dev)
+        else:
+            kvq.positions_ring(start, 1, window, slot, cp_dev)
+        kvq.quant_scatter(dev_input(k, True), slot, dk)
+        kvq.quant_scatter(dev_input(v, True), slot, dv)
+        sm = oracle.positions_sink(p, 1, sink, window, cp)
+        oracle.quant_scatter(hk, k, sm)
+        oracle.quant_scatter(hv, v, sm)
+        if p not in CHECKPOINTS:
+            continue
+        say(f"{layout} checkpoint p={p}")
+        kvq.build_mask(cp_dev, start, 1, sink, window, mask_dev)
+        kv_len = min(p + 1, S)
+        outs = [kvq.sdpa_decode(dev_input(q, True), dk, dv, kv_len=i32(kv_len), mask=mask_dev, out_dtype=od,
+                                workspace=ws) for od in (torch.bfloat16, torch.float32)]
+        torch.cuda.synchronize()
+        assert int(slot.item()) == int(sm[0]), (p, int(slot.item()), int(sm[0]))
+        assert np.array_equal(cp_dev.cpu().numpy(), cp), f"cache_positions differ at p={p}"
+        mask = oracle.build_mask(cp, p, 1, sink, window)
+        assert np.array_equal(mask_dev.cpu().numpy(), mask), f"mask differs at p={p}"
+        assert_cache_equal(dk, hk, f"{layout} K p={p}")
+        assert_cache_equal(dv, hv, f"{layout} V p={p}")
+        ref = oracle.sdpa(q, hk, hv, kv_len, mask=mask)
+        for out in outs:
+            check_attention(out, ref, f"{layout} decode p={p} out {out.dtype}")
+
+
+def _tile_rows(Lq, n, seed):
+    """Query rows: the ends and every boundary of 32- and 64-row tiles that a
+    spread of offsets hits, then seeded fill-up to n rows."""
+    fixed = {0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 255, 256, 511, 512, 1023, 1024,
+             1535, 1536, 2015, 2016, 2046, 2047}
+    fixed = {r for r in fixed if r < Lq}
+    rest = np.random.default_rng(seed).choice(sorted(set(range(Lq)) - fixed), size=n - len(fixed), replace=False)
+    return np.array(sorted(fixed | set(int(r) for r in rest)), np.int32)
+
+
+@pytest.mark.timeout(900)
+def test_long_prefill_4bit_sampled_rows():
+    """4-bit cache of 131072 slots (D 256, 16 KV heads) written block by
+    block on both sides (bit-exact), then causal chunked prefill of the
+    2048-row chunks ending at 65536 and 131072; 64 query rows x 32 heads per
+    chunk against the oracle."""
+    w = wl.LONGPREFILL
+    say("long prefill: filling the 4-bit cache")
+    dk, hk = new_pair(kvq.UINT4_TH, w.B, w.Hkv, w.S, w.D)
+    dv, hv = new_pair(kvq.UINT4_TH, w.B, w.Hkv, w.S, w.D)
+    for blk in range(w.S // w.Lq):
+        k, v = wl.longprefill_block(blk, w)
+        slots = np.arange(blk * w.Lq, (blk + 1) * w.Lq, dtype=np.int32)
+        sd = torch.from_numpy(slots).to(DEV)
+        kvq.quant_scatter(dev_input(k, True), sd, dk)
+        kvq.quant_scatter(dev_input(v, True), sd, dv)
+        oracle.quant_scatter(hk, k, slots, parallel=True)
+        oracle.quant_scatter(hv, v, slots, parallel=True)
+    torch.cuda.synchronize()
+    assert_cache_equal(dk, hk, "long prefill K")
+    assert_cache_equal(dv, hv, "long prefill V")
+    rows_r = _tile_rows(w.Lq, 64, seed=4)
+    hh, rr = np.meshgrid(np.arange(w.Hq), rows_r, indexing="ij")
+    rows = np.stack([np.zeros(hh.size, np.int32), hh.ravel(), rr.ravel()], axis=1).astype(np.int32)
+    for end in w.chunk_ends:
+        say(f"long prefill: chunk ending at {end}")
+        q = wl.longprefill_q(end, w)
+        out = kvq.sdpa_prefill(dev_input(q, True), dk, dv, kv_len=i32(end), causal=True)
+        torch.cuda.synchronize()
+        got = out[0][torch.from_numpy(rows[:, 1]).long().to(DEV), torch.from_numpy(rows[:, 2]).long().to(DEV)]
+        ref = oracle.sdpa(q, hk, hv, end, causal=True, rows=rows)
+        check_attention(got, ref, f"long prefill kv_len {end}")
+
+
+@pytest.mark.parametrize("qmode", [kvq.FP8E4M3_B32, kvq.MXFP4_B32])
+def test_block_scatter_full(qmode):
+    """x [16384, 128] bf16 with 1% outliers x20 into a 65536-slot block cache,
+    1638 slots skipped: every byte of the cache against the oracle."""
+    w = wl.BLOCKSCATTER
+    say(f"block scatter full size, qmode {qmode}")
+    x, slots = wl.blockscatter_inputs(w)
+    dc, hc = new_pair(qmode, 1, 1, w.n_slots, w.d)
+    kvq.quant_scatter(dev_input(x[None, None], True), torch.from_numpy(slots).to(DEV), dc)
+    oracle.quant_scatter(hc, x[None, None], slots, parallel=True)
+    torch.cuda.synchronize()
+    assert_cache_equal(dc, hc, f"block scatter qmode {qmode}")
+    # the skipped tokens' slots were never written (still the sentinel)
+    written = np.zeros(w.n_slots, bool)
+    written[slots[slots >= 0]] = True
+    codes = dc.codes.cpu().numpy().reshape(w.n_slots, -1)
+    assert (codes[~written] == 0xA5).all()
