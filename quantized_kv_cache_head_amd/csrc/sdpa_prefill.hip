@@ -87,6 +87,22 @@ __device__ __forceinline__ void dq_dword(uint32_t w, uint32_t off, uint32_t* out
     }
 }
 
+// 4-bit codes with fewer operations: 8 codes (one dword, element 2i in the
+// low nibble of byte i) -> 4 fp16 pairs (code - zp) in the order
+// (e0,e2) (e4,e6) (e1,e3) (e5,e7): the low and the high nibbles are each
+// placed under the fp16 exponent of 1024 by one byte permute with a 0x64
+// constant word.  Element order within each group of 8 is therefore
+// U4_ORDER[p] for position p; q takes the same order for q . k, and the V^T
+// transpose undoes it.
+__device__ constexpr int U4_ORDER[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+__device__ __forceinline__ void dq_dword_u4p(uint32_t w, uint32_t off, uint32_t* out) {
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    out[0] = h2_sub(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u), off);
+    out[1] = h2_sub(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u), off);
+    out[2] = h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u), off);
+    out[3] = h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u), off);
+}
+
 __device__ __forceinline__ uint32_t zp_pair(int zp, bool u4) {
     // fp16 of (1024 + 128 + zp) for int8 (codes enter as 1024 + (c + 128)),
     // (1024 + zp) for 4-bit; exact integers below 2048.
@@ -107,6 +123,13 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 v_lds[D * VPITCH];
     __shared__ float c_lds[PF_BN];         // key scale * softmax scale (0 past kv_len)
     __shared__ float sv_lds[PF_BN];        // value scale (0 past kv_len)
+    // raw code tiles (K rows then V rows), double-buffered: the next tile's
+    // bytes stream in with global_load_lds while this tile is computed
+    constexpr int RAWB = 2 * PF_BN * ROWB;
+    __shared__ __attribute__((aligned(16))) uint8_t raw_lds[2][RAWB];
+    // per-key metadata of a tile, double-buffered: (k scale, v scale, k zp, v zp)
+    __shared__ float mks_lds[2][PF_BN], mvs_lds[2][PF_BN];
+    __shared__ int mkz_lds[2][PF_BN], mvz_lds[2][PF_BN];
     __shared__ float red_lds[4];
 
     const int tid = threadIdx.x;
@@ -187,7 +210,7 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
             half8_t hi, lo;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = q_live[qb] ? ldexpf(v[e], qk) : 0.0f;
+                const float x = q_live[qb] ? ldexpf(v[U4 ? U4_ORDER[e] : e], qk) : 0.0f;
                 hi[e] = (_Float16)x;
                 lo[e] = (_Float16)(x - (float)hi[e]);
             }
@@ -214,8 +237,72 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
     const int n_tiles = (loop_end + PF_BN - 1) / PF_BN;
     const int diag_lo = qpos0 + r0;        // keys <= this are visible to every row of the tile
 
+    // Asynchronous copy of tile tt's K and V code rows into raw_lds[buf]: a
+    // workgroup-wide step moves 256 x 16 bytes; lane l of wave w in step i
+    // fills bytes i*4096 + w*1024 + l*16 of the tile (rows past the cache end
+    // read the last row: they are masked).
+    constexpr int TILEB = PF_BN * ROWB;                // bytes of a K (or V) tile
+    constexpr int RSTEPS = (TILEB + 4095) / 4096;     // steps per K (or V) tile
+    static_assert(TILEB % 4096 == 0 || TILEB < 4096, "raw tile steps");
+    auto fetch_raw = [&](int tt, int buf) {
+        const int jt = tt * PF_BN;
+#pragma unroll
+        for (int i = 0; i < RSTEPS; ++i) {
+            const int off = i * 4096 + tid * 16;
+            if (TILEB < 4096 && off >= TILEB) continue;   // whole waves past a small tile
+
+            const int key = off / ROWB, col = off % ROWB;
+            const int64_t j = min(jt + key, a.S - 1);
+            __attribute__((address_space(3))) void* lk =
+                (__attribute__((address_space(3))) void*)(raw_lds[buf] + i * 4096 + wave * 1024);
+            __attribute__((address_space(3))) void* lv =
+                (__attribute__((address_space(3))) void*)(raw_lds[buf] + PF_BN * ROWB + i * 4096 + wave * 1024);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kcodes + j * ROWB + col),
+                                             lk, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vcodes + j * ROWB + col),
+                                             lv, 16, 0, 0);
+        }
+    };
+    // per-key metadata of tile tt: loaded into registers (threads < 64), stored
+    // to the metadata buffer later, when the loads have landed
+    float mk_s = 0.0f, mv_s = 0.0f;
+    int mk_z = 0, mv_z = 0;
+    auto fetch_meta = [&](int tt) {
+        if (tid < PF_BN) {
+            const int j = min(tt * PF_BN + tid, a.S - 1);
+            mk_s = a.ks[plane + j];
+            mv_s = a.vs[plane + j];
+            mk_z = a.kz[plane + j];
+            mv_z = a.vz[plane + j];
+        }
+    };
+    auto store_meta = [&](int buf) {
+        if (tid < PF_BN) {
+            mks_lds[buf][tid] = mk_s;
+            mvs_lds[buf][tid] = mv_s;
+            mkz_lds[buf][tid] = mk_z;
+            mvz_lds[buf][tid] = mv_z;
+        }
+    };
+    if (n_tiles > 0) {
+        fetch_meta(0);
+        fetch_raw(0, 0);
+        store_meta(0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
     for (int t = 0; t < n_tiles; ++t) {
         const int j0 = t * PF_BN;
+        const int cur = t & 1;
+        // the next tile's metadata, then its code rows, go out first (the
+        // metadata is waited for below without waiting for the code rows)
+        if (t + 1 < n_tiles) {
+            fetch_meta(t + 1);
+            fetch_raw(t + 1, cur ^ 1);
+        }
+        const uint8_t* rk = raw_lds[cur];
+        const uint8_t* rv = raw_lds[cur] + PF_BN * ROWB;
         // ---------------- stage: dequantize K and V^T into LDS ----------------
         {
             constexpr int CPR = ROWB / 16;                 // 16-byte chunks per K row
@@ -223,14 +310,20 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
 #pragma unroll
             for (int c = tid; c < NCH; c += 256) {
                 const int kk = c / CPR, ch = c % CPR;
-                const int j = min(j0 + kk, a.S - 1);
-                const uint4 w = *reinterpret_cast<const uint4*>(kcodes + (int64_t)j * ROWB + ch * 16);
-                const uint32_t off = zp_pair(a.kz[plane + j], U4);
+                const uint4 w = *reinterpret_cast<const uint4*>(rk + kk * ROWB + ch * 16);
+                const uint32_t off = zp_pair(mkz_lds[cur][kk], U4);
                 uint32_t hv[U4 ? 16 : 8];
-                dq_dword<U4>(w.x, off, hv + 0 * (U4 ? 4 : 2));
-                dq_dword<U4>(w.y, off, hv + 1 * (U4 ? 4 : 2));
-                dq_dword<U4>(w.z, off, hv + 2 * (U4 ? 4 : 2));
-                dq_dword<U4>(w.w, off, hv + 3 * (U4 ? 4 : 2));
+                if constexpr (U4) {
+                    dq_dword_u4p(w.x, off, hv + 0);
+                    dq_dword_u4p(w.y, off, hv + 4);
+                    dq_dword_u4p(w.z, off, hv + 8);
+                    dq_dword_u4p(w.w, off, hv + 12);
+                } else {
+                    dq_dword<false>(w.x, off, hv + 0);
+                    dq_dword<false>(w.y, off, hv + 2);
+                    dq_dword<false>(w.z, off, hv + 4);
+                    dq_dword<false>(w.w, off, hv + 6);
+                }
                 uint4* dst = reinterpret_cast<uint4*>(k_lds + kk * KPITCH + ch * (U4 ? 32 : 16));
 #pragma unroll
                 for (int i = 0; i < (U4 ? 4 : 2); ++i) dst[i] = make_uint4(hv[4 * i], hv[4 * i + 1], hv[4 * i + 2], hv[4 * i + 3]);
@@ -240,40 +333,46 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
             for (int u = tid; u < 8 * NDG; u += 256) {
                 const int dg = u % NDG, kg = u / NDG;       // kg = kbk*4 + h*2 + s
                 const int kbk = kg >> 2, hh = (kg >> 1) & 1, s = kg & 1;
-                uint32_t pr[8][4];                          // per key: 4 fp16 pairs (d, d+1)
+                uint32_t pr[8][4];                          // per key: 4 fp16 pairs
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int k32 = (2 * s + (e >> 2)) * 8 + hh * 4 + (e & 3);
-                    const int j = min(j0 + kbk * 32 + k32, a.S - 1);
-                    const uint32_t off = zp_pair(a.vz[plane + j], U4);
-                    const uint8_t* src = vcodes + (int64_t)j * ROWB + (U4 ? dg * 4 : dg * 8);
+                    const int k64 = kbk * 32 + (2 * s + (e >> 2)) * 8 + hh * 4 + (e & 3);
+                    const uint32_t off = zp_pair(mvz_lds[cur][k64], U4);
+                    const uint8_t* src = rv + k64 * ROWB + (U4 ? dg * 4 : dg * 8);
                     if constexpr (U4) {
-                        dq_dword<true>(*reinterpret_cast<const uint32_t*>(src), off, pr[e]);
+                        dq_dword_u4p(*reinterpret_cast<const uint32_t*>(src), off, pr[e]);
                     } else {
                         const uint2 w2 = *reinterpret_cast<const uint2*>(src);
                         dq_dword<false>(w2.x, off, pr[e]);
                         dq_dword<false>(w2.y, off, pr[e] + 2);
                     }
                 }
-                const int pos = kbk * 32 + hh * 16 + s * 8;
+                // 16-byte chunk of the V^T row, XOR-swizzled by the row's group of
+                // 8 so that the 32 lanes of a store (rows 8 apart) spread over the
+                // banks; the PV operand read applies the same swizzle
+                const int chunk = (kbk * 32 + hh * 16 + s * 8) / 8;
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
-                    // gather element dd of each of the 8 keys: half (dd & 1) of pair dd/2
-                    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+                    // gather element dd of each of the 8 keys: int8 pairs hold
+                    // (dd, dd+1); 4-bit pairs hold the U4_ORDER arrangement
+                    const int pq = U4 ? ((dd & 1) * 2 + (dd >> 2)) : (dd >> 1);
+                    const int ph = U4 ? ((dd >> 1) & 1) : (dd & 1);
+                    const uint32_t sel = ph ? 0x07060302u : 0x05040100u;
                     uint32_t o4[4];
 #pragma unroll
                     for (int e2 = 0; e2 < 4; ++e2)
-                        o4[e2] = __builtin_amdgcn_perm(pr[2 * e2 + 1][dd >> 1], pr[2 * e2][dd >> 1], sel);
-                    *reinterpret_cast<uint4*>(v_lds + (dg * 8 + dd) * VPITCH + pos) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+                        o4[e2] = __builtin_amdgcn_perm(pr[2 * e2 + 1][pq], pr[2 * e2][pq], sel);
+                    *reinterpret_cast<uint4*>(v_lds + (dg * 8 + dd) * VPITCH + (chunk ^ (dg & 7)) * 8) =
+                        make_uint4(o4[0], o4[1], o4[2], o4[3]);
                 }
             }
             if (tid < PF_BN) {
                 const int j = j0 + tid;
                 const bool in = j < kv_len;
-                const int jc = min(j, a.S - 1);
-                c_lds[tid] = in ? a.ks[plane + jc] * rs : 0.0f;
-                sv_lds[tid] = in ? a.vs[plane + jc] : 0.0f;
+                c_lds[tid] = in ? mks_lds[cur][tid] * rs : 0.0f;
+                sv_lds[tid] = in ? mvs_lds[cur][tid] : 0.0f;
             }
+            if (t + 1 < n_tiles) store_meta(cur ^ 1);
         }
         __syncthreads();
 
@@ -325,7 +424,7 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
                 const bool upd = tmax > m_run[qb] + PF_TAU;
                 if (__any(upd)) {
                     const float mn = upd ? tmax : m_run[qb];
-                    const float al = (m_run[qb] == -__builtin_huge_valf()) ? 0.0f : exp2f(m_run[qb] - mn);
+                    const float al = (m_run[qb] == -__builtin_huge_valf()) ? 0.0f : __builtin_amdgcn_exp2f(m_run[qb] - mn);
                     m_run[qb] = mn;
                     l_run[qb] *= al;
 #pragma unroll
@@ -333,7 +432,9 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
 #pragma unroll
                         for (int i = 0; i < 16; ++i) o_acc[db][qb][i] *= al;
                 }
-                const float mcur = m_run[qb];
+                // a masked score is -inf and gives p = 2^-inf = 0; msafe keeps
+                // -inf - (-inf) out of a row that has seen no key yet
+                const float msafe = m_run[qb] == -__builtin_huge_valf() ? 0.0f : m_run[qb];
                 float lsum = 0.0f;
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
@@ -343,14 +444,22 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
                         const float4 s4 = *reinterpret_cast<const float4*>(sv_lds + kbk * 32 + (sb * 2 + e4) * 8 + hl * 4);
                         const float svv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) {
+                        for (int ii = 0; ii < 4; ii += 2) {
                             const int e = e4 * 4 + ii;
-                            const float xv = st[qb][sb * 8 + e];
-                            const float p = (xv == -__builtin_huge_valf()) ? 0.0f : exp2f(xv - mcur);
-                            lsum += p;
-                            const float pv = p * svv[ii];
-                            ph[e] = (_Float16)pv;
-                            plo[e] = (_Float16)(pv - (float)ph[e]);
+                            const float p0 = __builtin_amdgcn_exp2f(st[qb][sb * 8 + e] - msafe);
+                            const float p1 = __builtin_amdgcn_exp2f(st[qb][sb * 8 + e + 1] - msafe);
+                            lsum += p0 + p1;
+                            const float pv0 = p0 * svv[ii], pv1 = p1 * svv[ii + 1];
+                            // hi limb rounded toward zero, lo limb = the exact fp32 remainder in fp16
+                            const half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv0, pv1));
+                            ph[e] = h2[0];
+                            ph[e + 1] = h2[1];
+                            if constexpr (PL == 2) {
+                                const half2_t l2 = __builtin_bit_cast(
+                                    half2_t, __builtin_amdgcn_cvt_pkrtz(pv0 - (float)h2[0], pv1 - (float)h2[1]));
+                                plo[e] = l2[0];
+                                plo[e + 1] = l2[1];
+                            }
                         }
                     }
                     pb[sb][qb][0] = ph;
@@ -364,8 +473,9 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
             for (int db = 0; db < NDB; ++db) {
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
+                    const int vrow = db * 32 + l32;
                     const half8_t av = *reinterpret_cast<const half8_t*>(
-                        v_lds + (db * 32 + l32) * VPITCH + kbk * 32 + hl * 16 + sb * 8);
+                        v_lds + vrow * VPITCH + (((kbk * 32 + hl * 16 + sb * 8) / 8) ^ ((vrow >> 3) & 7)) * 8);
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -374,6 +484,7 @@ __global__ __launch_bounds__(256, 1) void sdpa_prefill_mfma(PrefillArgs a) {
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(0);                // the next tile's code rows have landed
         __syncthreads();
     }
 
