@@ -120,6 +120,18 @@ kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, in
                              const int32_t* slot_mapping, int64_t slot_stride_b,
                              const kvq_cache* cache, int32_t* err_flags, void* stream);
 
+/* The K and V update of one step in a single launch ([PR24473] writes new
+ * keys and values into their two caches through the same slot indices):
+ * exactly kvq_quant_scatter(xk, ..., k_cache) followed by
+ * kvq_quant_scatter(xv, ..., v_cache).  xk and xv share dtype, sizes and
+ * strides; the two caches must have the same mode and sizes (else
+ * KVQ_ERR_SHAPE).  Bad slots set KVQ_FLAG_SLOT_RANGE as above. */
+kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                const int32_t* slot_mapping, int64_t slot_stride_b,
+                                const kvq_cache* k_cache, const kvq_cache* v_cache,
+                                int32_t* err_flags, void* stream);
+
 /* Write slots for positions p = *start_pos + t, t in [0, T), attention-sink
  * layout ([PR24473]): n_slots = sink_size + window, slot = p for p < sink_size,
  * else sink_size + (p - sink_size) mod window.  slot_mapping_out: int32 [T].

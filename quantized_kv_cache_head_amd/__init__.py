@@ -31,7 +31,7 @@ FLAG_SLOT_RANGE, FLAG_KVLEN, FLAG_POS_CAPACITY = 1, 2, 4
 NO_CAUSAL_SKIP = 1
 
 EXPORTS = (
-    "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_positions_with_sink",
+    "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_quant_scatter_kv", "kvq_positions_with_sink",
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_prefill",
 )
@@ -67,6 +67,8 @@ def lib():
         L.kvq_cache_bytes.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
         L.kvq_quant_scatter.restype = _I
         L.kvq_quant_scatter.argtypes = [_P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, _P, _P]
+        L.kvq_quant_scatter_kv.restype = _I
+        L.kvq_quant_scatter_kv.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, _CP, _P, _P]
         L.kvq_positions_with_sink.restype = _I
         L.kvq_positions_with_sink.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P]
         L.kvq_positions_ring.restype = _I
@@ -192,6 +194,23 @@ def quant_scatter(x: torch.Tensor, slot_mapping: torch.Tensor, cache: Cache, err
     _check("kvq_quant_scatter", lib().kvq_quant_scatter(
         _ptr(x), _dtype_code(x), B, H, T, D, x.stride(0), x.stride(1), x.stride(2),
         _ptr(slot_mapping), ssb, ctypes.byref(c), _ptr(err_flags), _stream(stream)))
+
+
+def quant_scatter_kv(xk: torch.Tensor, xv: torch.Tensor, slot_mapping: torch.Tensor, k_cache: Cache, v_cache: Cache,
+                     err_flags=None, stream=None):
+    """kvq_quant_scatter_kv: the K and V update of one step in one launch; xk and
+    xv are [B, H, T, D] with the same dtype, shape and strides."""
+    _need_cuda(xk, xv, slot_mapping, err_flags)
+    if xk.dim() != 4 or xk.stride(3) != 1 or xk.shape != xv.shape or xk.stride() != xv.stride() or xk.dtype != xv.dtype:
+        raise ValueError("xk and xv must be [B, H, T, D] with D contiguous, equal shapes, strides and dtype")
+    if slot_mapping.dtype != torch.int32 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int32")
+    B, H, T, D = xk.shape
+    ssb = 0 if slot_mapping.dim() == 1 else slot_mapping.stride(0)
+    kc, vc = k_cache.struct(), v_cache.struct()
+    _check("kvq_quant_scatter_kv", lib().kvq_quant_scatter_kv(
+        _ptr(xk), _ptr(xv), _dtype_code(xk), B, H, T, D, xk.stride(0), xk.stride(1), xk.stride(2),
+        _ptr(slot_mapping), ssb, ctypes.byref(kc), ctypes.byref(vc), _ptr(err_flags), _stream(stream)))
 
 
 def positions_with_sink(start_pos, T, sink_size, window, slot_mapping_out, cache_positions, err_flags=None, stream=None):

@@ -87,6 +87,31 @@ KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, i
                                               err_flags, reinterpret_cast<hipStream_t>(stream)));
 }
 
+KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                        int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                        const int32_t* slot_mapping, int64_t slot_stride_b, const kvq_cache* k_cache,
+                                        const kvq_cache* v_cache, int32_t* err_flags, void* stream) {
+    kvq_status st = check_cache(k_cache);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(v_cache)) != KVQ_OK) return st;
+    if (k_cache->qmode != v_cache->qmode || k_cache->batch != v_cache->batch || k_cache->heads != v_cache->heads ||
+        k_cache->n_slots != v_cache->n_slots || k_cache->head_dim != v_cache->head_dim)
+        return KVQ_ERR_SHAPE;
+    if (x_dtype != KVQ_F32 && x_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (T < 0 || B != k_cache->batch || H != k_cache->heads || D != k_cache->head_dim) return KVQ_ERR_SHAPE;
+    if (T == 0) return KVQ_OK;
+    if (!xk || !xv || !slot_mapping) return KVQ_ERR_NULL;
+    if (stride_b < 0 || stride_h < 0 || stride_t < 0 || slot_stride_b < 0) return KVQ_ERR_SHAPE;
+    const int64_t vec = x_dtype == KVQ_BF16 ? 8 : 4;
+    if (!aligned(xk, 16) || !aligned(xv, 16) || stride_b % vec || stride_h % vec || stride_t % vec)
+        return KVQ_ERR_SHAPE;
+    return from_hip(kvq::launch_quant_scatter_kv(
+        k_cache->qmode, x_dtype == KVQ_BF16, xk, xv, B, H, T, D, stride_b, stride_h, stride_t, slot_mapping,
+        slot_stride_b, k_cache->n_slots, reinterpret_cast<uint8_t*>(k_cache->codes), k_cache->scales, k_cache->zps,
+        reinterpret_cast<uint8_t*>(v_cache->codes), v_cache->scales, v_cache->zps, err_flags,
+        reinterpret_cast<hipStream_t>(stream)));
+}
+
 KVQ_API kvq_status kvq_positions_with_sink(const int32_t* start_pos, int T, int sink_size, int window,
                                            int32_t* slot_mapping_out, int32_t* cache_positions,
                                            int32_t* err_flags, void* stream) {

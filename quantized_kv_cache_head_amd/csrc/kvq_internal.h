@@ -18,6 +18,11 @@ hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int 
                                 int64_t ssb, int n_slots, uint8_t* codes, void* scales,
                                 int8_t* zps, int32_t* err, hipStream_t s);
 
+hipError_t launch_quant_scatter_kv(int qmode, bool bf16, const void* xk, const void* xv, int B, int H, int T, int D,
+                                   int64_t sb, int64_t sh, int64_t st, const int32_t* slots, int64_t ssb,
+                                   int n_slots, uint8_t* kcodes, void* kscales, int8_t* kzps, uint8_t* vcodes,
+                                   void* vscales, int8_t* vzps, int32_t* err, hipStream_t s);
+
 hipError_t launch_positions_sink(const int32_t* start_pos, int T, int sink, int window, int32_t* slot_out,
                                  int32_t* cache_positions, int32_t* err, hipStream_t s);
 hipError_t launch_positions_full(const int32_t* start_pos, int T, int capacity, int32_t* slot_out,

@@ -49,8 +49,12 @@ __device__ __forceinline__ void row_coords(const ScatterArgs& a, int64_t row, in
     b = (int)(bh / a.H);
 }
 
+// Kernels take two argument sets and serve the one blockIdx.y picks (K and V
+// of one update in a single launch; a single cache passes the same set twice
+// and launches one grid row).
 template <int L, int NP, bool BF16, bool U4>
-__global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a) {
+__global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, ScatterArgs a1) {
+    const ScatterArgs a = blockIdx.y ? a1 : a0;
     constexpr int QMIN = U4 ? 0 : -128;
     constexpr int QMAX = U4 ? 15 : 127;
     const int lane = threadIdx.x & 63;
@@ -129,7 +133,8 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a) {
 }
 
 template <bool BF16, bool MX>
-__global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a) {
+__global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, ScatterArgs a1) {
+    const ScatterArgs a = blockIdx.y ? a1 : a0;
     const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int qi = (int)(gl & 3);                  // lane within the 32-block
     const int64_t blk = gl >> 2;
@@ -188,45 +193,61 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a) {
 }
 
 template <int L, int NP, bool BF16, bool U4>
-static hipError_t launch_affine(const ScatterArgs& a, hipStream_t s) {
+static hipError_t launch_affine(const ScatterArgs& a, const ScatterArgs& a1, int n, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.H * a.T;
     const int64_t rows_per_block = 4 * (64 / L);
     const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((quant_scatter_affine<L, NP, BF16, U4>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((quant_scatter_affine<L, NP, BF16, U4>), dim3((unsigned)blocks, (unsigned)n), dim3(256), 0, s,
+                       a, a1);
     return hipGetLastError();
 }
 
 template <bool BF16, bool U4>
-static hipError_t dispatch_affine(const ScatterArgs& a, hipStream_t s) {
+static hipError_t dispatch_affine(const ScatterArgs& a, const ScatterArgs& a1, int n, hipStream_t s) {
     switch (a.D) {
-    case 64: return launch_affine<8, 1, BF16, U4>(a, s);
-    case 128: return launch_affine<16, 1, BF16, U4>(a, s);
-    case 256: return launch_affine<32, 1, BF16, U4>(a, s);
-    case 512: return launch_affine<64, 1, BF16, U4>(a, s);
+    case 64: return launch_affine<8, 1, BF16, U4>(a, a1, n, s);
+    case 128: return launch_affine<16, 1, BF16, U4>(a, a1, n, s);
+    case 256: return launch_affine<32, 1, BF16, U4>(a, a1, n, s);
+    case 512: return launch_affine<64, 1, BF16, U4>(a, a1, n, s);
     default:
-        if (a.D <= 1024) return launch_affine<64, 2, BF16, U4>(a, s);
-        if (a.D <= 2048) return launch_affine<64, 4, BF16, U4>(a, s);
-        return launch_affine<64, 16, BF16, U4>(a, s);
+        if (a.D <= 1024) return launch_affine<64, 2, BF16, U4>(a, a1, n, s);
+        if (a.D <= 2048) return launch_affine<64, 4, BF16, U4>(a, a1, n, s);
+        return launch_affine<64, 16, BF16, U4>(a, a1, n, s);
     }
+}
+
+// One or two caches (n = 1 or 2) of the same mode and sizes in one launch.
+static hipError_t launch_scatter_n(int qmode, bool bf16, const ScatterArgs& a, const ScatterArgs& a1, int n,
+                                   hipStream_t s) {
+    if (qmode == QM_INT8_TH) return bf16 ? dispatch_affine<true, false>(a, a1, n, s) : dispatch_affine<false, false>(a, a1, n, s);
+    if (qmode == QM_UINT4_TH) return bf16 ? dispatch_affine<true, true>(a, a1, n, s) : dispatch_affine<false, true>(a, a1, n, s);
+    const int64_t lanes = (int64_t)a.B * a.H * a.T * (a.D / 8);
+    const dim3 grid((unsigned)((lanes + 255) / 256), (unsigned)n);
+    if (qmode == QM_FP8E4M3_B32) {
+        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, false>), grid, dim3(256), 0, s, a, a1);
+        else hipLaunchKernelGGL((quant_scatter_block<false, false>), grid, dim3(256), 0, s, a, a1);
+    } else {
+        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, true>), grid, dim3(256), 0, s, a, a1);
+        else hipLaunchKernelGGL((quant_scatter_block<false, true>), grid, dim3(256), 0, s, a, a1);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,
                                 int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
                                 int64_t ssb, int n_slots, uint8_t* codes, void* scales,
                                 int8_t* zps, int32_t* err, hipStream_t s) {
-    ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err};
-    if (qmode == QM_INT8_TH) return bf16 ? dispatch_affine<true, false>(a, s) : dispatch_affine<false, false>(a, s);
-    if (qmode == QM_UINT4_TH) return bf16 ? dispatch_affine<true, true>(a, s) : dispatch_affine<false, true>(a, s);
-    const int64_t lanes = (int64_t)B * H * T * (D / 8);
-    const unsigned blocks = (unsigned)((lanes + 255) / 256);
-    if (qmode == QM_FP8E4M3_B32) {
-        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, false>), dim3(blocks), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((quant_scatter_block<false, false>), dim3(blocks), dim3(256), 0, s, a);
-    } else {
-        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, true>), dim3(blocks), dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((quant_scatter_block<false, true>), dim3(blocks), dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
+    const ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err};
+    return launch_scatter_n(qmode, bf16, a, a, 1, s);
+}
+
+hipError_t launch_quant_scatter_kv(int qmode, bool bf16, const void* xk, const void* xv, int B, int H, int T, int D,
+                                   int64_t sb, int64_t sh, int64_t st, const int32_t* slots, int64_t ssb,
+                                   int n_slots, uint8_t* kcodes, void* kscales, int8_t* kzps, uint8_t* vcodes,
+                                   void* vscales, int8_t* vzps, int32_t* err, hipStream_t s) {
+    const ScatterArgs ak{xk, B, H, T, D, sb, sh, st, slots, ssb, n_slots, kcodes, kscales, kzps, err};
+    const ScatterArgs av{xv, B, H, T, D, sb, sh, st, slots, ssb, n_slots, vcodes, vscales, vzps, err};
+    return launch_scatter_n(qmode, bf16, ak, av, 2, s);
 }
 
 }  // namespace kvq

@@ -84,6 +84,14 @@ def test_host_validation_errors(kvq):
     # affine cache without zero points
     cz, keep2 = _fake_cache(kvq, zps=False)
     assert L.kvq_quant_scatter(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(cz), None, s) == 1
+    # K+V update: the two caches must agree in mode and sizes
+    cv_other, keep5 = _fake_cache(kvq, S=32)
+    assert L.kvq_quant_scatter_kv(None, None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c),
+                                  ctypes.byref(cv_other), None, s) == 2
+    assert L.kvq_quant_scatter_kv(None, None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c),
+                                  ctypes.byref(c), None, s) == 1
+    assert L.kvq_quant_scatter_kv(None, None, 1, 1, 2, 0, 64, 0, 0, 64, None, 0, ctypes.byref(c),
+                                  ctypes.byref(c), None, s) == 0
     # positions: window must be >= 1, T >= 0
     assert L.kvq_positions_with_sink(None, 4, 4, 0, None, None, None, s) == 2
     assert L.kvq_positions_ring(None, -1, 8, None, None, None, s) == 2

@@ -107,3 +107,29 @@ def test_scatter_empty_call_is_noop():
     kvq.quant_scatter(x, torch.zeros((1, 0), dtype=torch.int32, device=DEV), dc)
     torch.cuda.synchronize()
     assert_cache_equal(dc, hc, "empty")
+
+
+@pytest.mark.parametrize("qmode", MODES)
+def test_scatter_kv_single_launch(qmode):
+    """kvq_quant_scatter_kv writes K and V exactly as two kvq_quant_scatter
+    calls would (both against the oracle, bit-exact), including skipped and
+    out-of-range slots."""
+    B, H, T, D, S = 2, 3, 9, 128, 40
+    say(f"scatter kv qmode={qmode}")
+    rng = np.random.default_rng(qmode + 77)
+    xk = wl.to_bf16_values(rng.standard_normal((B, H, T, D)).astype(np.float32) * 3)
+    xv = wl.to_bf16_values(rng.standard_normal((B, H, T, D)).astype(np.float32))
+    slots = rng.permutation(S)[:B * T].reshape(B, T).astype(np.int32)
+    slots[0, 2] = -1
+    slots[1, 5] = S + 3          # out of range: skipped and flagged
+    dk, hk = new_pair(qmode, B, H, S, D)
+    dv, hv = new_pair(qmode, B, H, S, D)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvq.quant_scatter_kv(dev_input(xk, True), dev_input(xv, True), torch.from_numpy(slots).to(DEV), dk, dv,
+                         err_flags=err)
+    oracle.quant_scatter(hk, xk, slots)
+    oracle.quant_scatter(hv, xv, slots)
+    torch.cuda.synchronize()
+    assert_cache_equal(dk, hk, "kv scatter K")
+    assert_cache_equal(dv, hv, "kv scatter V")
+    assert int(err.item()) & 1

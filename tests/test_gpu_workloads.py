@@ -124,8 +124,7 @@ def test_sink_ring_stream(layout):
             kvq.positions_with_sink(start, 1, sink, window, slot, cp_dev)
         else:
             kvq.positions_ring(start, 1, window, slot, cp_dev)
-        kvq.quant_scatter(dev_input(k, True), slot, dk)
-        kvq.quant_scatter(dev_input(v, True), slot, dv)
+        kvq.quant_scatter_kv(dev_input(k, True), dev_input(v, True), slot, dk, dv)
         sm = oracle.positions_sink(p, 1, sink, window, cp)
         oracle.quant_scatter(hk, k, sm)
         oracle.quant_scatter(hv, v, sm)
