@@ -287,11 +287,10 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr int PD = KVQ_DEC_PD;                   // K ring depth (steps in flight)
     constexpr int PDV = KVQ_DEC_PDV;                 // V ring depth: issued before the middle pass
     constexpr int ROWS_MAX = GM.rows_max;
-    constexpr int RPT = ROWS_MAX / 256;              // metadata rows per thread
     constexpr float NEG_INF = -__builtin_huge_valf();
     constexpr float LOG2E = 1.4426950408889634f;
     static_assert(CK >= 1 && CK <= 16 && CV >= 2 && CV <= 16, "row split");
-    static_assert(ROWS_MAX % DEC_CHUNK_ALIGN == 0 && ROWS_MAX % 256 == 0, "rows_max alignment");
+    static_assert(ROWS_MAX % DEC_CHUNK_ALIGN == 0 && ROWS_MAX <= 4 * 256, "rows_max: 4 metadata rows per thread");
 
     __shared__ float s_row[ROWS_MAX * G];           // q.k dots, scores, then p * scale_v
     __shared__ float4 s_meta[ROWS_MAX];             // (scale_k, mask, scale_v, zp_v + VOFF)
@@ -345,21 +344,42 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     const gptr<int8_t> kzb = uniform_ptr(a.kz + plane);
     const gptr<int8_t> vzb = uniform_ptr(a.vz + plane);
     const bool has_mask = a.mask != nullptr;
-    // without a mask the mask load reads the key scales (any valid row) and
-    // its value is dropped
     const gptr<float> mrow = has_mask ? uniform_ptr(a.mask + (int64_t)b * a.mask_sb) : ksb;
 
-    // ---- per-row metadata of the slice: one row per thread and round --------
-    float m_ks[RPT], m_mk[RPT], m_vs[RPT];
-    int m_kz[RPT], m_vz[RPT];
+    // ---- per-row metadata of the slice: 4 consecutive rows per thread --------
+    // Only threads whose rows start inside the slice load, with one 16-byte
+    // (scales, mask) or 4-byte (zero points) load per array when the base
+    // pointers and the plane length keep those aligned (slices start on
+    // multiples of 32 rows, so then the 4 rows never pass row S - 1); else row
+    // by row, clamped.  Rows past the slice are loaded but never used.
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const int r4 = tid * 4;
+    const bool meta_live = r4 < n;
+    const bool meta_vec = (a.S & 3) == 0 &&
+                          ((reinterpret_cast<uintptr_t>(a.ks) | reinterpret_cast<uintptr_t>(a.vs)) & 15) == 0 &&
+                          ((reinterpret_cast<uintptr_t>(a.kz) | reinterpret_cast<uintptr_t>(a.vz)) & 3) == 0 &&
+                          (!has_mask || ((reinterpret_cast<uintptr_t>(a.mask) & 15) == 0 && (a.mask_sb & 3) == 0));
+    f32x4_t m_ks = {0.0f, 0.0f, 0.0f, 0.0f}, m_mk = m_ks, m_vs = m_ks;
+    uint32_t m_kz = 0, m_vz = 0;
+    if (meta_live) {
+        const uint32_t j = (uint32_t)(j0 + r4);
+        if (meta_vec) {
+            m_ks = *(gptr<f32x4_t>)(ksb + j);
+            m_vs = *(gptr<f32x4_t>)(vsb + j);
+            if (has_mask) m_mk = *(gptr<f32x4_t>)(mrow + j);
+            m_kz = *(gptr<uint32_t>)(kzb + j);
+            m_vz = *(gptr<uint32_t>)(vzb + j);
+        } else {
 #pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-        const uint32_t j = (uint32_t)min(j0 + tid + 256 * u, j1 - 1);
-        m_ks[u] = ksb[j];
-        m_mk[u] = mrow[j];
-        m_vs[u] = vsb[j];
-        m_kz[u] = kzb[j];
-        m_vz[u] = vzb[j];
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t je = (uint32_t)min((int)j + e, j1 - 1);
+                m_ks[e] = ksb[je];
+                m_vs[e] = vsb[je];
+                if (has_mask) m_mk[e] = mrow[je];
+                m_kz |= (uint32_t)(uint8_t)kzb[je] << (8 * e);
+                m_vz |= (uint32_t)(uint8_t)vzb[je] << (8 * e);
+            }
+        }
     }
 
     // K pass geometry: lane (rk, ck); rows j0 + (t * DEC_WAVES + wave) * RK + rk
@@ -395,11 +415,13 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         for (int u = 0; u < QPT; ++u) mx = fmaxf(mx, fabsf(qv[u]));
         mx = wave_max(mx);
         if (lane == 0) s_red[wave][0] = mx;
+        if (meta_live) {
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) {
-            const int i = tid + 256 * u;
-            s_meta[i] = make_float4(m_ks[u], has_mask ? m_mk[u] * LOG2E : 0.0f, m_vs[u], (float)m_vz[u] + VOFF);
-            s_kzo[i] = zoff_pair(m_kz[u], U4);
+            for (int e = 0; e < 4; ++e) {
+                const int zk = (int)(int8_t)(m_kz >> (8 * e)), zv = (int)(int8_t)(m_vz >> (8 * e));
+                s_meta[r4 + e] = make_float4(m_ks[e], has_mask ? m_mk[e] * LOG2E : 0.0f, m_vs[e], (float)zv + VOFF);
+                s_kzo[r4 + e] = zoff_pair(zk, U4);
+            }
         }
         __syncthreads();
         mx = fmaxf(fmaxf(s_red[0][0], s_red[1][0]), fmaxf(s_red[2][0], s_red[3][0]));
