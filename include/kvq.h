@@ -166,7 +166,7 @@ kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int
 
 /* Workspace bytes kvq_sdpa_decode needs for these sizes (partial softmax
  * states of the split-K pass).  It is an upper bound valid on any device and
- * for either affine cache mode (the split count of a launch depends on how
+ * for every cache mode (the split count of a launch depends on how
  * many workgroups the device keeps resident); needs no device.  0 on invalid
  * sizes. */
 size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D);
@@ -176,9 +176,11 @@ size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int 
  * ring/sink caches):
  *   out[b, h, 0, :] = softmax_j(sm_scale * q[b,h,0,:] . k_hat[b,g,j,:] + mask[b,j]) v_hat[b,g,j,:]
  * over j in [0, kv_len), g = h / (Hq / Hkv), k_hat / v_hat dequantized on the
- * fly ((code - zp) * scale).  A row with no visible key gives 0.
+ * fly: (code - zp) * scale for the affine modes, decode(code) * scale of the
+ * element's 32-element block for FP8E4M3_B32 and MXFP4_B32 (the read side of
+ * [IQC]'s per-block write).  A row with no visible key gives 0.
  * q: [B, Hq, 1, D] (q_dtype); out: [B, Hq, 1, D] (out_dtype).
- * k, v: INT8_TH or UINT4_TH caches with equal sizes; Hq % heads == 0.
+ * k, v: caches of one mode (any of the four) with equal sizes; Hq % heads == 0.
  * kv_len: device int32 scalar or NULL (= n_slots); a value outside
  *   [1, n_slots] is clamped and sets KVQ_FLAG_KVLEN.
  * mask: NULL or fp32 [B, n_slots] with batch stride mask_stride_b (0 shares

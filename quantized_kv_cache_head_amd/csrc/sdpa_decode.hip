@@ -31,6 +31,13 @@
 //  * Pass 2 (p . v): a V row is split over CV lanes of 16 bytes; fp32 FMA of
 //    p * scale_v on v_cvt_f32_ubyte of the codes; the first PDV steps of the
 //    V ring are issued before the middle pass so the V stream overlaps it.
+//  * Block caches (FP8-E4M3 with an fp32 scale, MX-FP4 with an E8M0 scale,
+//    per 32 elements: the IndexerQuantCache operator page's per-block
+//    format): codes become exact fp16 / fp32 values through the gfx950
+//    conversion instructions; a 16-byte chunk of a lane lies inside one
+//    block, so the block scale travels in the load ring with the codes and
+//    multiplies the chunk's partial q . k (pass 1) or p (pass 2).  Rows carry
+//    no scale or zero point of their own.
 //  * Merge: a reduce-scatter of the accumulators across the row groups of a
 //    wave (lane-swap permutes and DPP), then the waves through LDS; one
 //    partial (m, l, o[D]) per (b, head, split) goes to the workspace.  A small
@@ -133,6 +140,56 @@ __device__ __forceinline__ void codes_to_f32(const uint4 w, float out[U4 ? 32 : 
             }
         }
     }
+}
+
+// Block-quantized codes (FP8-E4M3FN, or FP4-E2M1 two per byte with element
+// 2i in the low nibble of byte i) to exact fp16 pairs / fp32 values in
+// element order, with the gfx950 conversion instructions at scale 1: every
+// E4M3 and E2M1 value is exactly representable in fp16.  The per-block scale
+// is applied afterwards, in fp32.
+template <bool F4>
+__device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[F4 ? 16 : 8]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (!F4) {
+            out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, false));
+            out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, true));
+        } else {
+            out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 0));
+            out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 1));
+            out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 2));
+            out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 3));
+        }
+    }
+}
+
+template <bool F4>
+__device__ __forceinline__ void blk_to_f32(const uint4 w, float out[F4 ? 32 : 16]) {
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (!F4) {
+            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], false);
+            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], true);
+            out[4 * i] = lo[0]; out[4 * i + 1] = lo[1]; out[4 * i + 2] = hi[0]; out[4 * i + 3] = hi[1];
+        } else {
+            const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 0);
+            const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 1);
+            const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 2);
+            const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 3);
+            out[8 * i + 0] = v0[0]; out[8 * i + 1] = v0[1]; out[8 * i + 2] = v1[0]; out[8 * i + 3] = v1[1];
+            out[8 * i + 4] = v2[0]; out[8 * i + 5] = v2[1]; out[8 * i + 6] = v3[0]; out[8 * i + 7] = v3[1];
+        }
+    }
+}
+
+// A block scale as loaded (fp32 bits, or an E8M0 byte) to its fp32 value;
+// E8M0 b is 2^(b - 127), b = 0 being the subnormal 2^-127.
+template <bool F4>
+__device__ __forceinline__ float blk_scale(uint32_t raw) {
+    if constexpr (F4) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
+    else return __uint_as_float(raw);
 }
 
 // Cross-lane helpers.  DPP controls: quad_perm [1,0,3,2] (xor 1), quad_perm
@@ -270,8 +327,13 @@ __device__ __forceinline__ uint4 load16(gptr<uint8_t> base, uint32_t off) {
 #define KVQ_DEC_PDV 4
 #endif
 
-template <int D, bool U4, int G, bool QBF16>
+template <int D, int QM, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
+    constexpr bool BLK = QM == QM_FP8E4M3_B32 || QM == QM_MXFP4_B32;   // per-32 block scales, no zero point
+    constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
+    constexpr bool F4 = QM == QM_MXFP4_B32;
+    constexpr int SPR = D / 32;                      // block scales per row
+    constexpr int SCB = F4 ? 1 : 4;                  // bytes per block scale
     constexpr DecGeom GM = dec_geom(D, U4, G);
     constexpr int ROWB = GM.rowb;
     constexpr int EPB = U4 ? 2 : 1;                  // elements per code byte
@@ -280,7 +342,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr int CV = GM.cv, RV = GM.rv;
     constexpr int EV = 16 * EPB;                     // elements per lane, V pass
     constexpr int NL = QBF16 ? 1 : 2;                // fp16 limbs of q
-    constexpr float VOFF = U4 ? 0.0f : 128.0f;      // fp32 value = code + VOFF
+    constexpr float VOFF = (U4 || BLK) ? 0.0f : 128.0f;   // fp32 value = code + VOFF
     constexpr int NV = G * EV;                       // accumulators per lane
     constexpr int NVR = NV / RV;                     // after the row-group reduce-scatter
     constexpr int STEPK = GM.stepk, STEPV = GM.stepv, STEPM = GM.stepm;
@@ -343,6 +405,9 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     const gptr<float> vsb = uniform_ptr(a.vs + plane);
     const gptr<int8_t> kzb = uniform_ptr(a.kz + plane);
     const gptr<int8_t> vzb = uniform_ptr(a.vz + plane);
+    // block caches: scale planes [B, Hkv, S, D / 32] of fp32 (FP8) or E8M0 bytes
+    const gptr<uint8_t> kscb = uniform_ptr(reinterpret_cast<const uint8_t*>(a.ks) + plane * SPR * SCB);
+    const gptr<uint8_t> vscb = uniform_ptr(reinterpret_cast<const uint8_t*>(a.vs) + plane * SPR * SCB);
     const bool has_mask = a.mask != nullptr;
     const gptr<float> mrow = has_mask ? uniform_ptr(a.mask + (int64_t)b * a.mask_sb) : ksb;
 
@@ -356,29 +421,37 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     const int r4 = tid * 4;
     const bool meta_live = r4 < n;
     const bool meta_vec = (a.S & 3) == 0 &&
-                          ((reinterpret_cast<uintptr_t>(a.ks) | reinterpret_cast<uintptr_t>(a.vs)) & 15) == 0 &&
-                          ((reinterpret_cast<uintptr_t>(a.kz) | reinterpret_cast<uintptr_t>(a.vz)) & 3) == 0 &&
+                          (BLK || (((reinterpret_cast<uintptr_t>(a.ks) | reinterpret_cast<uintptr_t>(a.vs)) & 15) == 0 &&
+                                   ((reinterpret_cast<uintptr_t>(a.kz) | reinterpret_cast<uintptr_t>(a.vz)) & 3) == 0)) &&
                           (!has_mask || ((reinterpret_cast<uintptr_t>(a.mask) & 15) == 0 && (a.mask_sb & 3) == 0));
     f32x4_t m_ks = {0.0f, 0.0f, 0.0f, 0.0f}, m_mk = m_ks, m_vs = m_ks;
     uint32_t m_kz = 0, m_vz = 0;
     if (meta_live) {
         const uint32_t j = (uint32_t)(j0 + r4);
         if (meta_vec) {
-            m_ks = *(gptr<f32x4_t>)(ksb + j);
-            m_vs = *(gptr<f32x4_t>)(vsb + j);
+            if constexpr (!BLK) {
+                m_ks = *(gptr<f32x4_t>)(ksb + j);
+                m_vs = *(gptr<f32x4_t>)(vsb + j);
+                m_kz = *(gptr<uint32_t>)(kzb + j);
+                m_vz = *(gptr<uint32_t>)(vzb + j);
+            }
             if (has_mask) m_mk = *(gptr<f32x4_t>)(mrow + j);
-            m_kz = *(gptr<uint32_t>)(kzb + j);
-            m_vz = *(gptr<uint32_t>)(vzb + j);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t je = (uint32_t)min((int)j + e, j1 - 1);
-                m_ks[e] = ksb[je];
-                m_vs[e] = vsb[je];
+                if constexpr (!BLK) {
+                    m_ks[e] = ksb[je];
+                    m_vs[e] = vsb[je];
+                    m_kz |= (uint32_t)(uint8_t)kzb[je] << (8 * e);
+                    m_vz |= (uint32_t)(uint8_t)vzb[je] << (8 * e);
+                }
                 if (has_mask) m_mk[e] = mrow[je];
-                m_kz |= (uint32_t)(uint8_t)kzb[je] << (8 * e);
-                m_vz |= (uint32_t)(uint8_t)vzb[je] << (8 * e);
             }
+        }
+        if constexpr (BLK) {                         // scales live per block, applied in the passes
+            m_ks = f32x4_t{1.0f, 1.0f, 1.0f, 1.0f};
+            m_vs = m_ks;
         }
     }
 
@@ -395,11 +468,21 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     // ---- K ring: the first PD steps' codes go out before any arithmetic -------
     // Every slot is consumed (converted) before it is reloaded, so a reload
     // targets the same registers: a copy at the loop edge would wait for it.
+    // Block caches: the scale of each 16-byte chunk's block rides in the ring
+    // with the codes (16 bytes hold 16 FP8 or 32 FP4 elements, so a chunk
+    // never straddles two 32-element blocks).
     uint4 kbuf[PD][KB / 16];
+    uint32_t ksr[PD][KB / 16];
     auto fetch_codes = [&](int u, int t) {
         const uint32_t j = krow(t);
 #pragma unroll
-        for (int c = 0; c < KB / 16; ++c) kbuf[u][c] = load16(kbase, j * ROWB + (uint32_t)ck * KB + 16 * c);
+        for (int c = 0; c < KB / 16; ++c) {
+            kbuf[u][c] = load16(kbase, j * ROWB + (uint32_t)ck * KB + 16 * c);
+            if constexpr (BLK) {
+                const uint32_t gi = j * SPR + (uint32_t)((ck * KB + 16 * c) * EPB) / 32;
+                ksr[u][c] = F4 ? (uint32_t)kscb[gi] : *(gptr<uint32_t>)(kscb + gi * SCB);
+            }
+        }
     };
 #pragma unroll
     for (int u = 0; u < PD; ++u) fetch_codes(u, min(u, max(twk - 1, 0)));
@@ -461,10 +544,20 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     // ---- pass 1: q . (code - zp) per row into LDS -----------------------------
     auto k_step = [&](int u, int t, bool reload) {
         const int i = (t * DEC_WAVES + wave) * RK + rk;
-        const uint32_t zo = s_kzo[min(i, i_last)];
+        constexpr int NC = KB / 16, PPC = NPK / NC;   // 16-byte chunks, fp16 pairs per chunk
         uint32_t kh[NPK];
+        float kscale[NC];
+        if constexpr (BLK) {
 #pragma unroll
-        for (int c = 0; c < KB / 16; ++c) codes_to_h2<U4>(kbuf[u][c], zo, kh + c * (NPK / (KB / 16)));
+            for (int c = 0; c < NC; ++c) {
+                blk_to_h2<F4>(kbuf[u][c], kh + c * PPC);
+                kscale[c] = blk_scale<F4>(ksr[u][c]);
+            }
+        } else {
+            const uint32_t zo = s_kzo[min(i, i_last)];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) codes_to_h2<U4>(kbuf[u][c], zo, kh + c * PPC);
+        }
         if (reload) {
             __builtin_amdgcn_sched_barrier(0);        // keep the reload after the conversion
             fetch_codes(u, min(t + PD, twk - 1));
@@ -472,12 +565,28 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         float d[G];
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            float x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][0]), as_h2(kh[0]), 0.0f, false);
-            if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][0]), as_h2(kh[0]), x, false);
+            float x;
+            if constexpr (BLK) {
+                // per chunk: q . codes, times the chunk's block scale
+                x = 0.0f;
 #pragma unroll
-            for (int e = 1; e < NPK; ++e) {
-                x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][e]), as_h2(kh[e]), x, false);
-                if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][e]), as_h2(kh[e]), x, false);
+                for (int c = 0; c < NC; ++c) {
+                    float xc = 0.0f;
+#pragma unroll
+                    for (int e = c * PPC; e < (c + 1) * PPC; ++e) {
+                        xc = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][e]), as_h2(kh[e]), xc, false);
+                        if constexpr (NL == 2) xc = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][e]), as_h2(kh[e]), xc, false);
+                    }
+                    x = fmaf(xc, kscale[c], x);
+                }
+            } else {
+                x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][0]), as_h2(kh[0]), 0.0f, false);
+                if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][0]), as_h2(kh[0]), x, false);
+#pragma unroll
+                for (int e = 1; e < NPK; ++e) {
+                    x = __builtin_amdgcn_fdot2(as_h2(qh[hh][0][e]), as_h2(kh[e]), x, false);
+                    if constexpr (NL == 2) x = __builtin_amdgcn_fdot2(as_h2(qh[hh][1][e]), as_h2(kh[e]), x, false);
+                }
             }
             d[hh] = group_sum_first<CK>(x);
         }
@@ -498,9 +607,17 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     // ---- V ring: the first PDV steps go out before the barrier, so the V
     // stream runs while the middle pass computes
     uint4 vbuf[PDV];
+    uint32_t vsr[PDV];                                // block caches: the chunk's block scale
+    auto fetch_v = [&](int u, int t) {
+        const uint32_t j = vrow(t);
+        vbuf[u] = load16(vbase, j * ROWB + (uint32_t)cv * 16);
+        if constexpr (BLK) {
+            const uint32_t gi = j * SPR + (uint32_t)(cv * 16 * EPB) / 32;
+            vsr[u] = F4 ? (uint32_t)vscb[gi] : *(gptr<uint32_t>)(vscb + gi * SCB);
+        }
+    };
 #pragma unroll
-    for (int u = 0; u < PDV; ++u)
-        vbuf[u] = load16(vbase, vrow(min(u, max(twv - 1, 0))) * ROWB + (uint32_t)cv * 16);
+    for (int u = 0; u < PDV; ++u) fetch_v(u, min(u, max(twv - 1, 0)));
     __syncthreads();                                  // all dots in LDS
 
     // ---- middle pass: per head, scores, max, p * scale_v, l, zp correction ----
@@ -608,14 +725,20 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     for (int e = 0; e < NV; ++e) acc[e] = 0.0f;
     auto v_step = [&](int u, int t, bool reload) {
         float vf[EV];
-        codes_to_f32<U4>(vbuf[u], vf);
+        float live_sc = 1.0f;
+        if constexpr (BLK) {
+            blk_to_f32<F4>(vbuf[u], vf);
+            live_sc = blk_scale<F4>(vsr[u]);
+        } else {
+            codes_to_f32<U4>(vbuf[u], vf);
+        }
         if (reload) {
             __builtin_amdgcn_sched_barrier(0);        // keep the reload after the conversion
-            vbuf[u] = load16(vbase, vrow(min(t + PDV, twv - 1)) * ROWB + (uint32_t)cv * 16);
+            fetch_v(u, min(t + PDV, twv - 1));
         }
         // rows past the slice read the last row (finite) and weigh it by 0
         const int i = (t * DEC_WAVES + wave) * RV + rv;
-        const float live = i < n ? 1.0f : 0.0f;
+        const float live = i < n ? live_sc : 0.0f;
         const int ic = min(i, i_last);
         float pv[G];
 #pragma unroll
@@ -708,7 +831,7 @@ __global__ __launch_bounds__(D) void sdpa_decode_combine(const float* __restrict
 // enough splits for 4096 resident workgroups, and at least enough that every
 // slice fits the LDS row buffer.
 int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode) {
-    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH, Hq / Hkv);
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32, Hq / Hkv);
     const int pairs = B * Hkv;
     const int max_useful = (S + DEC_CHUNK_ALIGN - 1) / DEC_CHUNK_ALIGN;
     int splits = (4096 + pairs - 1) / pairs;
@@ -717,20 +840,28 @@ int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode) {
     return splits > need ? splits : need;
 }
 
-template <int D, bool U4, int G, bool QBF16>
-static const void* split_kernel() { return reinterpret_cast<const void*>(&sdpa_decode_split<D, U4, G, QBF16>); }
+template <int D, int QM, int G, bool QBF16>
+static const void* split_kernel() { return reinterpret_cast<const void*>(&sdpa_decode_split<D, QM, G, QBF16>); }
 
-static const void* split_kernel_for(int D, bool u4, int G, bool qbf16) {
-#define KVQ_SK(DD, UU)                                                                          \
+static const void* split_kernel_for(int D, int qm, int G, bool qbf16) {
+#define KVQ_SK(DD, QQ)                                                                          \
     switch (G) {                                                                                \
-    case 1: return qbf16 ? split_kernel<DD, UU, 1, true>() : split_kernel<DD, UU, 1, false>(); \
-    case 2: return qbf16 ? split_kernel<DD, UU, 2, true>() : split_kernel<DD, UU, 2, false>(); \
-    case 4: return qbf16 ? split_kernel<DD, UU, 4, true>() : split_kernel<DD, UU, 4, false>(); \
-    default: return qbf16 ? split_kernel<DD, UU, 8, true>() : split_kernel<DD, UU, 8, false>(); \
+    case 1: return qbf16 ? split_kernel<DD, QQ, 1, true>() : split_kernel<DD, QQ, 1, false>(); \
+    case 2: return qbf16 ? split_kernel<DD, QQ, 2, true>() : split_kernel<DD, QQ, 2, false>(); \
+    case 4: return qbf16 ? split_kernel<DD, QQ, 4, true>() : split_kernel<DD, QQ, 4, false>(); \
+    default: return qbf16 ? split_kernel<DD, QQ, 8, true>() : split_kernel<DD, QQ, 8, false>(); \
     }
-    if (D == 64) { if (u4) { KVQ_SK(64, true) } else { KVQ_SK(64, false) } }
-    if (D == 128) { if (u4) { KVQ_SK(128, true) } else { KVQ_SK(128, false) } }
-    if (u4) { KVQ_SK(256, true) } else { KVQ_SK(256, false) }
+#define KVQ_SKD(DD)                                          \
+    switch (qm) {                                            \
+    case QM_INT8_TH: { KVQ_SK(DD, QM_INT8_TH) }              \
+    case QM_UINT4_TH: { KVQ_SK(DD, QM_UINT4_TH) }            \
+    case QM_FP8E4M3_B32: { KVQ_SK(DD, QM_FP8E4M3_B32) }      \
+    default: { KVQ_SK(DD, QM_MXFP4_B32) }                    \
+    }
+    if (D == 64) { KVQ_SKD(64) }
+    if (D == 128) { KVQ_SKD(128) }
+    KVQ_SKD(256)
+#undef KVQ_SKD
 #undef KVQ_SK
 }
 
@@ -738,17 +869,17 @@ static const void* split_kernel_for(int D, bool u4, int G, bool qbf16) {
 // at once: per CU, the smaller of the VGPR limit (512 registers per lane of a
 // SIMD in granules of 8; a 4-wave workgroup puts one wave on each SIMD) and
 // the LDS limit, times the CU count.  0 when the runtime cannot tell.
-static int resident_workgroups(int D, bool u4, int G, bool qbf16) {
+static int resident_workgroups(int D, int qm, int G, bool qbf16) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    const int key = ((D == 64 ? 0 : D == 128 ? 1 : 2) * 2 + (u4 ? 1 : 0)) * 8 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3) * 2 +
+    const int key = ((D == 64 ? 0 : D == 128 ? 1 : 2) * 4 + (qm & 3)) * 8 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3) * 2 +
                     (qbf16 ? 1 : 0);
-    static int cache[64][48];                         // 0 = not known yet; benign races
+    static int cache[64][96];                         // 0 = not known yet; benign races
     int v = cache[dev][key];
     if (v > 0) return v;
     hipFuncAttributes fa;
     int cus = 0, lds_cu = 0;
-    if (hipFuncGetAttributes(&fa, split_kernel_for(D, u4, G, qbf16)) != hipSuccess || fa.numRegs <= 0 ||
+    if (hipFuncGetAttributes(&fa, split_kernel_for(D, qm, G, qbf16)) != hipSuccess || fa.numRegs <= 0 ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
@@ -771,11 +902,11 @@ static int resident_workgroups(int D, bool u4, int G, bool qbf16) {
 // one round (a second, partly filled round would run with little latency
 // hiding), within [rows fit in LDS, decode_splits_max].
 int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16) {
-    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH, Hq / Hkv);
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32, Hq / Hkv);
     const int pairs = B * Hkv;
     const int hi = decode_splits_max(B, Hq, Hkv, S, D, qmode);
     const int need = (S + gm.rows_max - 1) / gm.rows_max;
-    int resident = resident_workgroups(D, qmode == QM_UINT4_TH, Hq / Hkv, qbf16);
+    int resident = resident_workgroups(D, qmode, Hq / Hkv, qbf16);
     if (resident <= 0) resident = 1024;
     int splits = resident / pairs;
     if (splits < need) splits = need;
@@ -783,45 +914,49 @@ int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16) {
     return splits < 1 ? 1 : splits;
 }
 
-template <int D, bool U4, int G, bool QBF16>
-static hipError_t launch_split(const DecodeArgs& a, int nsplit, bool has_mask, hipStream_t s) {
-    (void)has_mask;
+template <int D, int QM, int G, bool QBF16>
+static hipError_t launch_split(const DecodeArgs& a, int nsplit, hipStream_t s) {
     const dim3 grid(nsplit, a.Hkv, a.B);
-    hipLaunchKernelGGL((sdpa_decode_split<D, U4, G, QBF16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((sdpa_decode_split<D, QM, G, QBF16>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <int D, bool U4, bool QBF16>
-static hipError_t dispatch_g(const DecodeArgs& a, int G, int nsplit, bool has_mask, hipStream_t s) {
+template <int D, int QM, bool QBF16>
+static hipError_t dispatch_g(const DecodeArgs& a, int G, int nsplit, hipStream_t s) {
     switch (G) {
-    case 1: return launch_split<D, U4, 1, QBF16>(a, nsplit, has_mask, s);
-    case 2: return launch_split<D, U4, 2, QBF16>(a, nsplit, has_mask, s);
-    case 4: return launch_split<D, U4, 4, QBF16>(a, nsplit, has_mask, s);
-    case 8: return launch_split<D, U4, 8, QBF16>(a, nsplit, has_mask, s);
+    case 1: return launch_split<D, QM, 1, QBF16>(a, nsplit, s);
+    case 2: return launch_split<D, QM, 2, QBF16>(a, nsplit, s);
+    case 4: return launch_split<D, QM, 4, QBF16>(a, nsplit, s);
+    case 8: return launch_split<D, QM, 8, QBF16>(a, nsplit, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int D, bool U4>
-static hipError_t dispatch_q(const DecodeArgs& a, bool qbf16, int G, int nsplit, bool has_mask, hipStream_t s) {
-    return qbf16 ? dispatch_g<D, U4, true>(a, G, nsplit, has_mask, s)
-                 : dispatch_g<D, U4, false>(a, G, nsplit, has_mask, s);
+template <int D, int QM>
+static hipError_t dispatch_q(const DecodeArgs& a, bool qbf16, int G, int nsplit, hipStream_t s) {
+    return qbf16 ? dispatch_g<D, QM, true>(a, G, nsplit, s) : dispatch_g<D, QM, false>(a, G, nsplit, s);
+}
+
+template <int D>
+static hipError_t dispatch_m(const DecodeArgs& a, int qmode, bool qbf16, int G, int nsplit, hipStream_t s) {
+    switch (qmode) {
+    case QM_INT8_TH: return dispatch_q<D, QM_INT8_TH>(a, qbf16, G, nsplit, s);
+    case QM_UINT4_TH: return dispatch_q<D, QM_UINT4_TH>(a, qbf16, G, nsplit, s);
+    case QM_FP8E4M3_B32: return dispatch_q<D, QM_FP8E4M3_B32>(a, qbf16, G, nsplit, s);
+    case QM_MXFP4_B32: return dispatch_q<D, QM_MXFP4_B32>(a, qbf16, G, nsplit, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s) {
     DecodeArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len,
                  L.mask, L.mask_sb, L.sm_scale * 1.4426950408889634f, L.part_o, L.part_ml, L.err};
     const int G = L.Hq / L.Hkv;
-    const bool u4 = L.qmode == QM_UINT4_TH;
-    const bool has_mask = L.mask != nullptr;
     hipError_t e;
     switch (L.D) {
-    case 64: e = u4 ? dispatch_q<64, true>(a, L.q_bf16, G, L.nsplit, has_mask, s)
-                    : dispatch_q<64, false>(a, L.q_bf16, G, L.nsplit, has_mask, s); break;
-    case 128: e = u4 ? dispatch_q<128, true>(a, L.q_bf16, G, L.nsplit, has_mask, s)
-                     : dispatch_q<128, false>(a, L.q_bf16, G, L.nsplit, has_mask, s); break;
-    case 256: e = u4 ? dispatch_q<256, true>(a, L.q_bf16, G, L.nsplit, has_mask, s)
-                     : dispatch_q<256, false>(a, L.q_bf16, G, L.nsplit, has_mask, s); break;
+    case 64: e = dispatch_m<64>(a, L.qmode, L.q_bf16, G, L.nsplit, s); break;
+    case 128: e = dispatch_m<128>(a, L.qmode, L.q_bf16, G, L.nsplit, s); break;
+    case 256: e = dispatch_m<256>(a, L.qmode, L.q_bf16, G, L.nsplit, s); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -98,11 +98,17 @@ def test_host_validation_errors(kvq):
     assert L.kvq_positions_full(None, 4, 0, None, None, None, s) == 2
     assert L.kvq_positions_full(None, 4, 16, None, None, None, s) == 1
     assert L.kvq_build_mask(None, 0, None, 1, 0, 4, None, s) == 2
-    # attention: block-mode caches are rejected as unsupported, never degraded
+    # block-mode caches: decode takes them (here it stops at the missing
+    # workspace); prefill rejects them as unsupported, never degraded
     cb, keep3 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
     q = ctypes.c_void_p(c.codes)
     assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(cb), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
-                             None, 0, None, s) == 4
+                             None, 0, None, s) == 5
+    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 8, ctypes.byref(cb), ctypes.byref(cb), None, None, 1, 0, 0.1, q, 1,
+                              None, s) == 4
+    # K and V caches in different modes
+    assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
+                             None, 0, None, s) == 3
     # Hq not a multiple of the KV heads
     assert L.kvq_sdpa_decode(q, 1, 1, 3, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
                              None, 0, None, s) == 2
