@@ -206,8 +206,8 @@ kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
  * is bit-identical).  mask: NULL or fp32 [Lq, n_slots] shared over the batch
  * (0 / -inf).  q: [B, Hq, Lq, D] (q_dtype); out: [B, Hq, Lq, D] (out_dtype).
  * kv_len: device int32 scalar or NULL (= n_slots), clamped to [Lq, n_slots]
- * with KVQ_FLAG_KVLEN.  Supported: INT8_TH or UINT4_TH, D in {64, 128, 256},
- * Hq / heads in {1, 2, 4, 8}, Lq >= 1. */
+ * with KVQ_FLAG_KVLEN.  Dequantization as in kvq_sdpa_decode.  Supported: any
+ * cache mode, D in {64, 128, 256}, Hq / heads in {1, 2, 4, 8}, Lq >= 1. */
 kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq,
                             const kvq_cache* k, const kvq_cache* v,
                             const int32_t* kv_len, const float* mask, int mask_is_causal,

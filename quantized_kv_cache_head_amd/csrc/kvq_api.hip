@@ -148,7 +148,7 @@ KVQ_API kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, c
 namespace {
 
 kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v,
-                           void* out, int out_dtype, bool block_ok) {
+                           void* out, int out_dtype) {
     kvq_status st = check_cache(k);
     if (st != KVQ_OK) return st;
     st = check_cache(v);
@@ -157,7 +157,6 @@ kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_
     if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
         return KVQ_ERR_DTYPE;
     if (k->qmode != v->qmode) return KVQ_ERR_DTYPE;
-    if (!block_ok && !is_affine(k->qmode)) return KVQ_ERR_UNSUPPORTED;   // no block-mode prefill
     if (k->batch != v->batch || k->heads != v->heads || k->n_slots != v->n_slots || k->head_dim != v->head_dim)
         return KVQ_ERR_SHAPE;
     if (B != k->batch || Hq <= 0 || Hq % k->heads != 0) return KVQ_ERR_SHAPE;
@@ -194,7 +193,7 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
                                    int out_dtype, void* workspace, size_t workspace_bytes, int32_t* err_flags,
                                    void* stream) {
     (void)mask_is_causal;   // at Lq = 1 the causal bound equals kv_len
-    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype, true);
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
     const int D = k->head_dim;
@@ -233,7 +232,7 @@ KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, i
                                     const kvq_cache* v, const int32_t* kv_len, const float* mask,
                                     int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
                                     int32_t* err_flags, void* stream) {
-    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype, false);
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (Lq < 1 || Lq > k->n_slots) return KVQ_ERR_SHAPE;
     if (flags & ~KVQ_NO_CAUSAL_SKIP) return KVQ_ERR_UNSUPPORTED;

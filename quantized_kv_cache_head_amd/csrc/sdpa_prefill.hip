@@ -31,6 +31,13 @@
 //    one barrier per tile.
 //  * Workgroups of one KV head are placed on the same XCD so its K/V stream
 //    is shared through that XCD's L2.
+//  * Block caches (FP8-E4M3 / MX-FP4 with a scale per 32 elements, the
+//    IndexerQuantCache operator page's format): the codes become exact fp16
+//    through the gfx950 conversions.  One QK k-step of 32 d is exactly one
+//    scale block, so each block's partial S^T is scaled per key in fp32 and
+//    summed; V^T rows stay in d order so a 16-row output block lies in one
+//    scale block, and P enters that block's PV product scaled by the keys'
+//    V scales of that block.  Raw rows are read below kv_len only.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -118,10 +125,35 @@ __device__ __forceinline__ int pf_col(int k) { return ((k & 15) >> 2) * 8 + (k >
 // 16-byte chunk swizzles: K rows by key, V^T rows by row.
 __device__ __forceinline__ int pf_ksw(int key) { return key & 7; }
 __device__ __forceinline__ int pf_vsw(int row) { return (row >> 1) & 3; }
+// V^T rows of block caches are in natural d order (a 16-row MFMA block then
+// lies inside one 32-element scale block); the stage writes 8 consecutive
+// rows per thread, so the swizzle follows the row's group of 8.
+__device__ __forceinline__ int pf_vswb(int row) { return (row >> 3) & 3; }
 
-template <int D, bool U4, int QL, int PL>
+// FP8-E4M3 (4 per dword) or FP4-E2M1 (8 per dword, element 2i in the low
+// nibble of byte i) codes to exact fp16 pairs in element order (gfx950
+// conversions at scale 1).
+template <bool F4>
+__device__ __forceinline__ void blk_dword(uint32_t w, uint32_t* out) {
+    if constexpr (!F4) {
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+    } else {
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+        out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+        out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+    }
+}
+
+template <int D, int QM, int QL, int PL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sdpa_prefill_mfma(PrefillArgs a) {
+    constexpr bool BLK = QM == QM_FP8E4M3_B32 || QM == QM_MXFP4_B32;   // per-32 block scales
+    constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
+    constexpr bool F4 = QM == QM_MXFP4_B32;
+    constexpr bool PERM = QM == QM_UINT4_TH;         // affine 4-bit: U4_ORDER element order
+    constexpr int NG = D / 32;                       // scale blocks per row (= QK k-steps)
     constexpr int BN = PF_BN;
     constexpr int ROWB = U4 ? D / 2 : D;
     constexpr int NDS = D / 32;            // QK MFMA k-steps (32 d each)
@@ -143,6 +175,11 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) float c_a[BN], c_b[BN], s_a[BN], s_b[BN];
     __shared__ float mks_lds[2][BN], mvs_lds[2][BN];
     __shared__ int mkz_lds[2][BN], mvz_lds[2][BN];
+    // block caches: block scales [group][key] as fetched (double buffer by
+    // tile parity) and as used by a tile's products (double buffer by slot)
+    constexpr int NBS = BLK ? NG * BN : 1;
+    __shared__ float bks_lds[2][NBS], bvs_lds[2][NBS];
+    __shared__ __attribute__((aligned(16))) float bk_a[NBS], bk_b[NBS], bv_a[NBS], bv_b[NBS];
     __shared__ float red_lds[PF_WAVES];
 
     const int tid = threadIdx.x;
@@ -214,7 +251,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         half8_t hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = q_live ? ldexpf(v[U4 ? U4_ORDER[e] : e], qk) : 0.0f;
+            const float x = q_live ? ldexpf(v[PERM ? U4_ORDER[e] : e], qk) : 0.0f;
             hi[e] = (_Float16)x;
             lo[e] = (_Float16)(x - (float)hi[e]);
         }
@@ -258,7 +295,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 key = off / ROWB;
                 col = off % ROWB;
             }
-            const int64_t j = min(jt + key, a.S - 1);
+            const int64_t j = min(jt + key, kv_len - 1);   // rows below kv_len only
             __attribute__((address_space(3))) void* l =
                 (__attribute__((address_space(3))) void*)(dst + i * 4096 + (wave & 3) * 1024);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + j * ROWB + col),
@@ -267,17 +304,40 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     };
     float mk_s = 0.0f, mv_s = 0.0f;
     int mk_z = 0, mv_z = 0;
+    uint32_t bk_r = 0, bv_r = 0;                      // block scales as loaded (fp32 bits / E8M0)
     auto fetch_meta = [&](int tt) {
-        if (tid < BN) {
-            const int j = min(tt * BN + tid, a.S - 1);
+        if constexpr (BLK) {
+            if (tid < NG * BN) {                      // thread -> (group tid / BN, key tid % BN)
+                const int j = min(tt * BN + tid % BN, kv_len - 1);
+                const int64_t gi = (plane + j) * NG + tid / BN;
+                if constexpr (F4) {
+                    bk_r = reinterpret_cast<const uint8_t*>(a.ks)[gi];
+                    bv_r = reinterpret_cast<const uint8_t*>(a.vs)[gi];
+                } else {
+                    bk_r = reinterpret_cast<const uint32_t*>(a.ks)[gi];
+                    bv_r = reinterpret_cast<const uint32_t*>(a.vs)[gi];
+                }
+            }
+        } else if (tid < BN) {
+            const int j = min(tt * BN + tid, kv_len - 1);
             mk_s = a.ks[plane + j];
             mv_s = a.vs[plane + j];
             mk_z = a.kz[plane + j];
             mv_z = a.vz[plane + j];
         }
     };
+    auto blk_scale = [](uint32_t raw) {              // E8M0 b = 2^(b - 127), b = 0 the subnormal 2^-127
+        if constexpr (F4) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
+        else return __uint_as_float(raw);
+    };
     auto store_meta = [&](int buf) {
-        if (tid < BN) {
+        if constexpr (BLK) {
+            if (tid < NG * BN) {
+                const int gk = (tid / BN) * BN + tid % BN;
+                bks_lds[buf][gk] = blk_scale(bk_r);
+                bvs_lds[buf][gk] = blk_scale(bv_r);
+            }
+        } else if (tid < BN) {
             mks_lds[buf][tid] = mk_s;
             mvs_lds[buf][tid] = mv_s;
             mkz_lds[buf][tid] = mk_z;
@@ -287,21 +347,23 @@ void sdpa_prefill_mfma(PrefillArgs a) {
 
     // Dequantize tile tt (raw codes in raw, metadata in mbuf) into the fp16
     // tiles kt / vt and its key scales into ct / st_.
-    auto stage = [&](int tt, const uint8_t* raw, int mbuf, _Float16* kt, _Float16* vt, float* ct, float* sv) {
+    auto stage = [&](int tt, const uint8_t* raw, int mbuf, _Float16* kt, _Float16* vt, float* ct, float* sv,
+                     float* bkt, float* bvt) {
         if (!vhalf) {
             // thread -> (key, eighth of the row: D/8 elements)
             constexpr int NPR = D / 16;                    // fp16 pairs of an eighth
             const int key = KPM ? (t256 & 31) : (t256 >> 3);
             const int part = KPM ? (t256 >> 5) : (t256 & 7);
             const uint8_t* rk = raw + (KPM ? (part * BN + key) * RB : key * ROWB + part * RB);
-            const uint32_t off = zp_pair(mkz_lds[mbuf][key], U4);
+            const uint32_t off = BLK ? 0u : zp_pair(mkz_lds[mbuf][key], U4);
             uint32_t w[RB / 4];
 #pragma unroll
             for (int i = 0; i < RB / 4; ++i) w[i] = reinterpret_cast<const uint32_t*>(rk)[i];
             uint32_t hv[NPR];
 #pragma unroll
             for (int i = 0; i < RB / 4; ++i) {
-                if constexpr (U4) dq_dword_u4p(w[i], off, hv + 4 * i);
+                if constexpr (BLK) blk_dword<F4>(w[i], hv + (F4 ? 4 : 2) * i);
+                else if constexpr (U4) dq_dword_u4p(w[i], off, hv + 4 * i);
                 else dq_dword_i8(w[i], off, hv + 2 * i);
             }
             constexpr int CPP = D / 64;                    // 16-byte chunks of an eighth
@@ -311,7 +373,15 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 *reinterpret_cast<uint4*>(kt + key * D + ch * 8) =
                     make_uint4(hv[4 * c], hv[4 * c + 1], hv[4 * c + 2], hv[4 * c + 3]);
             }
-            if (tid < BN) {
+            if constexpr (BLK) {
+                // block scales of keys past kv_len become 0 (their P is 0 too)
+                if (tid < NG * BN) {
+                    const bool in = tt * BN + tid % BN < kv_len;
+                    bkt[tid] = in ? bks_lds[mbuf][tid] : 0.0f;
+                    bvt[tid] = in ? bvs_lds[mbuf][tid] : 0.0f;
+                }
+                if (tid < BN) ct[tid] = tt * BN + tid < kv_len ? rs : 0.0f;
+            } else if (tid < BN) {
                 const bool in = tt * BN + tid < kv_len;
                 ct[tid] = in ? mks_lds[mbuf][tid] * rs : 0.0f;
                 sv[tid] = in ? mvs_lds[mbuf][tid] : 0.0f;
@@ -326,9 +396,17 @@ void sdpa_prefill_mfma(PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int k = kg * 4 + e;
-                    const uint32_t offv = zp_pair(mvz_lds[mbuf][k], U4);
+                    const uint32_t offv = BLK ? 0u : zp_pair(mvz_lds[mbuf][k], U4);
                     const uint8_t* vs = rv + k * ROWB + (U4 ? dg * 4 : dg * 8);
-                    if constexpr (U4) {
+                    if constexpr (BLK) {
+                        if constexpr (F4) {
+                            blk_dword<true>(*reinterpret_cast<const uint32_t*>(vs), pr[e]);
+                        } else {
+                            const uint2 w2 = *reinterpret_cast<const uint2*>(vs);
+                            blk_dword<false>(w2.x, pr[e]);
+                            blk_dword<false>(w2.y, pr[e] + 2);
+                        }
+                    } else if constexpr (U4) {
                         dq_dword_u4p(*reinterpret_cast<const uint32_t*>(vs), offv, pr[e]);
                     } else {
                         const uint2 w2 = *reinterpret_cast<const uint2*>(vs);
@@ -339,13 +417,13 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 const int col0 = pf_col(kg * 4);          // 4 consecutive columns
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
-                    const int pq = U4 ? ((dd & 1) * 2 + (dd >> 2)) : (dd >> 1);
-                    const int ph = U4 ? ((dd >> 1) & 1) : (dd & 1);
+                    const int pq = PERM ? ((dd & 1) * 2 + (dd >> 2)) : (dd >> 1);
+                    const int ph = PERM ? ((dd >> 1) & 1) : (dd & 1);
                     const uint32_t sel = ph ? 0x07060302u : 0x05040100u;
                     const uint32_t w0 = __builtin_amdgcn_perm(pr[1][pq], pr[0][pq], sel);
                     const uint32_t w1 = __builtin_amdgcn_perm(pr[3][pq], pr[2][pq], sel);
-                    const int row = dd * DG + dg;          // R(d) for d = dg * 8 + dd
-                    const int ch = (col0 >> 3) ^ pf_vsw(row);
+                    const int row = BLK ? dg * 8 + dd : dd * DG + dg;   // R(d) for d = dg * 8 + dd
+                    const int ch = (col0 >> 3) ^ (BLK ? pf_vswb(row) : pf_vsw(row));
                     *reinterpret_cast<uint2*>(vt + row * BN + ch * 8 + (col0 & 7)) = make_uint2(w0, w1);
                 }
             }
@@ -364,7 +442,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        stage(0, raw_a, 0, k_a, v_a, c_a, s_a);
+        stage(0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
         __syncthreads();
     }
 
@@ -372,29 +450,60 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     // into (kn, vn, cn, sn); streams tile t+2 into raw_n2 (the buffer tile t
     // came through).
     auto tile = [&](const int t, const _Float16* kc, const _Float16* vc, const float* cc, const float* sc,
-                    _Float16* kn, _Float16* vn, float* cn, float* sn, const uint8_t* raw_n1, uint8_t* raw_n2) {
+                    const float* bkc, const float* bvc, _Float16* kn, _Float16* vn, float* cn, float* sn,
+                    float* bkn, float* bvn, const uint8_t* raw_n1, uint8_t* raw_n2) {
         const int j0 = t * BN;
         if (t + 2 < n_tiles) {
             fetch_meta(t + 2);
             fetch_raw(t + 2, raw_n2);
         }
         // ---------------- S^T = K Q^T for the two 16-key blocks ----------------
-        float4_t st[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            st[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            const int key = kb * 16 + l16;
+        float4_t st[2] = {float4_t{0.0f, 0.0f, 0.0f, 0.0f}, float4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+        if constexpr (BLK) {
+            // one k-step = one 32-element scale block: each block's partial
+            // product is scaled per key (the lane's 4 keys) and summed in fp32;
+            // block by block, so only two partials are live at a time
 #pragma unroll
             for (int ds = 0; ds < NDS; ++ds) {
-                const int ch = (ds * 4 + lg) ^ pf_ksw(key);
-                const half8_t av = *reinterpret_cast<const half8_t*>(kc + key * D + ch * 8);
+                float4_t part[2];
 #pragma unroll
-                for (int ql = 0; ql < QL; ++ql)
-                    st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qh[ds][ql], st[kb], 0, 0, 0);
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int key = kb * 16 + l16;
+                    const int ch = (ds * 4 + lg) ^ pf_ksw(key);
+                    const half8_t av = *reinterpret_cast<const half8_t*>(kc + key * D + ch * 8);
+                    part[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int ql = 0; ql < QL; ++ql)
+                        part[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qh[ds][ql], part[kb], 0, 0, 0);
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const float4 k4 = *reinterpret_cast<const float4*>(bkc + ds * BN + kb * 16 + 4 * lg);
+                    st[kb][0] = fmaf(part[kb][0], k4.x, st[kb][0]);
+                    st[kb][1] = fmaf(part[kb][1], k4.y, st[kb][1]);
+                    st[kb][2] = fmaf(part[kb][2], k4.z, st[kb][2]);
+                    st[kb][3] = fmaf(part[kb][3], k4.w, st[kb][3]);
+                }
+                // keep the scaling here: sunk to the softmax it would hold
+                // every block's partial across the stage of the next tile
+                asm volatile("" : "+v"(st[0]), "+v"(st[1]));
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int key = kb * 16 + l16;
+#pragma unroll
+                for (int ds = 0; ds < NDS; ++ds) {
+                    const int ch = (ds * 4 + lg) ^ pf_ksw(key);
+                    const half8_t av = *reinterpret_cast<const half8_t*>(kc + key * D + ch * 8);
+#pragma unroll
+                    for (int ql = 0; ql < QL; ++ql)
+                        st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qh[ds][ql], st[kb], 0, 0, 0);
+                }
             }
         }
         // ---------------- tile t+1 dequantized while those MFMAs run -----------
-        if (t + 1 < n_tiles) stage(t + 1, raw_n1, (t + 1) & 1, kn, vn, cn, sn);
+        if (t + 1 < n_tiles) stage(t + 1, raw_n1, (t + 1) & 1, kn, vn, cn, sn, bkn, bvn);
 
         // ---------------- softmax over this lane's 8 keys -----------------------
         // lane holds keys j0 + kb*16 + 4*lg + i of query column qc
@@ -435,17 +544,21 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             for (int db = 0; db < NDB; ++db) o_acc[db] *= al;
         }
         const float msafe = m_run == NEG_INF ? 0.0f : m_run;
-        half8_t pb[PL];
-        {
-            const float4 s0 = *reinterpret_cast<const float4*>(sc + 4 * lg);
-            const float4 s1 = *reinterpret_cast<const float4*>(sc + 16 + 4 * lg);
+        float p8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p8[e] = __builtin_amdgcn_exp2f(sv8[e] - msafe);
+            l_run += p8[e];
+        }
+        // P * scale_v for the lane's 8 keys (scales sv[4lg..+3], sv[16+4lg..+3])
+        // as hi (+ lo) fp16 limbs: the B operand of the PV product
+        auto pack_p = [&](const float* svp, half8_t* pb) {
+            const float4 s0 = *reinterpret_cast<const float4*>(svp + 4 * lg);
+            const float4 s1 = *reinterpret_cast<const float4*>(svp + 16 + 4 * lg);
             const float svv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(sv8[e] - msafe);
-                const float p1 = __builtin_amdgcn_exp2f(sv8[e + 1] - msafe);
-                l_run += p0 + p1;
-                const float pv0 = p0 * svv[e], pv1 = p1 * svv[e + 1];
+                const float pv0 = p8[e] * svv[e], pv1 = p8[e + 1] * svv[e + 1];
                 const half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv0, pv1));
                 pb[0][e] = h2[0];
                 pb[0][e + 1] = h2[1];
@@ -456,25 +569,47 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                     pb[PL - 1][e + 1] = l2[1];
                 }
             }
-        }
+        };
 
-        // ---------------- O^T += V^T P^T (rows in the R(d) order) ---------------
+        // ---------------- O^T += V^T P^T ------------------------------------------
+        if constexpr (BLK) {
+            // rows in d order; output blocks 2g and 2g + 1 lie in scale block g
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const int row = db * 16 + l16;
-            const int ch = lg ^ pf_vsw(row);
-            const half8_t av = *reinterpret_cast<const half8_t*>(vc + row * BN + ch * 8);
+            for (int gb = 0; gb < NG; ++gb) {
+                half8_t pb[PL];
+                pack_p(bvc + gb * BN, pb);
 #pragma unroll
-            for (int pl = 0; pl < PL; ++pl)
-                o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[pl], o_acc[db], 0, 0, 0);
+                for (int db = 2 * gb; db < 2 * gb + 2; ++db) {
+                    const int row = db * 16 + l16;
+                    const int ch = lg ^ pf_vswb(row);
+                    const half8_t av = *reinterpret_cast<const half8_t*>(vc + row * BN + ch * 8);
+#pragma unroll
+                    for (int pl = 0; pl < PL; ++pl)
+                        o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[pl], o_acc[db], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);    // one group's P limbs live at a time
+            }
+        } else {
+            // rows in the R(d) order
+            half8_t pb[PL];
+            pack_p(sc, pb);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const int row = db * 16 + l16;
+                const int ch = lg ^ pf_vsw(row);
+                const half8_t av = *reinterpret_cast<const half8_t*>(vc + row * BN + ch * 8);
+#pragma unroll
+                for (int pl = 0; pl < PL; ++pl)
+                    o_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[pl], o_acc[db], 0, 0, 0);
+            }
         }
         if (t + 2 < n_tiles) store_meta(t & 1);       // tile t+2's metadata replaces tile t's
         __builtin_amdgcn_s_waitcnt(0);                // tile t+2's code rows have landed
         __syncthreads();
     };
     for (int t = 0; t < n_tiles; t += 2) {
-        tile(t, k_a, v_a, c_a, s_a, k_b, v_b, c_b, s_b, raw_b, raw_a);
-        if (t + 1 < n_tiles) tile(t + 1, k_b, v_b, c_b, s_b, k_a, v_a, c_a, s_a, raw_a, raw_b);
+        tile(t, k_a, v_a, c_a, s_a, bk_a, bv_a, k_b, v_b, c_b, s_b, bk_b, bv_b, raw_b, raw_a);
+        if (t + 1 < n_tiles) tile(t + 1, k_b, v_b, c_b, s_b, bk_b, bv_b, k_a, v_a, c_a, s_a, bk_a, bv_a, raw_a, raw_b);
     }
 
     // ---- epilogue: l over the 4 lane groups, normalize, store --------------------
@@ -492,7 +627,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int R = db * 16 + 4 * lg + i;
-            const int d = (R % DG) * 8 + R / DG;   // row R holds d with R(d) = R
+            const int d = BLK ? R : (R % DG) * 8 + R / DG;   // row R holds d with R(d) = R
             const float v = o_acc[db][i] * inv;
             if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[obase + d] = f32_to_bf16_rne(v);
             else reinterpret_cast<float*>(a.out)[obase + d] = v;
@@ -500,23 +635,34 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     }
 }
 
-template <int D, bool U4, int QL, int PL>
+template <int D, int QM, int QL, int PL>
 static hipError_t launch_pf(const PrefillArgs& a, hipStream_t s) {
     const int G = a.Hq / a.Hkv;
     const int QT = 16 * PF_WAVES / G;
     PrefillArgs aa = a;
     aa.n_qtiles = (a.Lq + QT - 1) / QT;
     const unsigned blocks = (unsigned)(a.B * a.Hkv * aa.n_qtiles);
-    hipLaunchKernelGGL((sdpa_prefill_mfma<D, U4, QL, PL>), dim3(blocks), dim3(64 * PF_WAVES), 0, s, aa);
+    hipLaunchKernelGGL((sdpa_prefill_mfma<D, QM, QL, PL>), dim3(blocks), dim3(64 * PF_WAVES), 0, s, aa);
     return hipGetLastError();
 }
 
-template <int D, bool U4>
+template <int D, int QM>
 static hipError_t dispatch_pf(const PrefillArgs& a, bool q_bf16, hipStream_t s) {
     // bf16 queries: one fp16 limb for Q (exact); fp32 queries: hi + lo limbs.
     // P * scale_v always goes in as hi + lo fp16 limbs (about 22 bits).
-    if (q_bf16) return launch_pf<D, U4, 1, 2>(a, s);
-    return launch_pf<D, U4, 2, 2>(a, s);
+    if (q_bf16) return launch_pf<D, QM, 1, 2>(a, s);
+    return launch_pf<D, QM, 2, 2>(a, s);
+}
+
+template <int D>
+static hipError_t dispatch_pm(const PrefillArgs& a, int qmode, bool q_bf16, hipStream_t s) {
+    switch (qmode) {
+    case QM_INT8_TH: return dispatch_pf<D, QM_INT8_TH>(a, q_bf16, s);
+    case QM_UINT4_TH: return dispatch_pf<D, QM_UINT4_TH>(a, q_bf16, s);
+    case QM_FP8E4M3_B32: return dispatch_pf<D, QM_FP8E4M3_B32>(a, q_bf16, s);
+    case QM_MXFP4_B32: return dispatch_pf<D, QM_MXFP4_B32>(a, q_bf16, s);
+    default: return hipErrorNotSupported;
+    }
 }
 
 hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s) {
@@ -525,11 +671,10 @@ hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s) {
                   L.sm_scale * 1.4426950408889634f, L.out, L.err};
     const int G = L.Hq / L.Hkv;
     if (G < 1 || G > 8 || (G & (G - 1))) return hipErrorNotSupported;
-    const bool u4 = L.qmode == QM_UINT4_TH;
     switch (L.D) {
-    case 64: return u4 ? dispatch_pf<64, true>(a, L.q_bf16, s) : dispatch_pf<64, false>(a, L.q_bf16, s);
-    case 128: return u4 ? dispatch_pf<128, true>(a, L.q_bf16, s) : dispatch_pf<128, false>(a, L.q_bf16, s);
-    case 256: return u4 ? dispatch_pf<256, true>(a, L.q_bf16, s) : dispatch_pf<256, false>(a, L.q_bf16, s);
+    case 64: return dispatch_pm<64>(a, L.qmode, L.q_bf16, s);
+    case 128: return dispatch_pm<128>(a, L.qmode, L.q_bf16, s);
+    case 256: return dispatch_pm<256>(a, L.qmode, L.q_bf16, s);
     default: return hipErrorNotSupported;
     }
 }

@@ -98,13 +98,14 @@ def test_host_validation_errors(kvq):
     assert L.kvq_positions_full(None, 4, 0, None, None, None, s) == 2
     assert L.kvq_positions_full(None, 4, 16, None, None, None, s) == 1
     assert L.kvq_build_mask(None, 0, None, 1, 0, 4, None, s) == 2
-    # block-mode caches: decode takes them (here it stops at the missing
-    # workspace); prefill rejects them as unsupported, never degraded
+    # block-mode caches pass validation (decode stops at the missing workspace)
     cb, keep3 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
     q = ctypes.c_void_p(c.codes)
     assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(cb), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
                              None, 0, None, s) == 5
-    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 8, ctypes.byref(cb), ctypes.byref(cb), None, None, 1, 0, 0.1, q, 1,
+    # block-mode prefill with an unsupported head_dim is still rejected
+    cb96, keep6 = _fake_cache(kvq, qmode=kvq.MXFP4_B32, D=96, zps=False)
+    assert L.kvq_sdpa_prefill(q, 1, 1, 4, 8, ctypes.byref(cb96), ctypes.byref(cb96), None, None, 1, 0, 0.1, q, 1,
                               None, s) == 4
     # K and V caches in different modes
     assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
