@@ -330,6 +330,64 @@ def leg_long_prefill():
     return res
 
 
+def leg_block_attention():
+    """Attention over block-quantized caches (FP8-E4M3 + fp32 scale, MX-FP4 +
+    E8M0 scale, per 32 elements): decode on the Llama-shaped layer (4 cache
+    replicas rotated, so bytes come from HBM) and the 2048-row chunked
+    prefill of the long-prefill shape at kv_len 65536."""
+    res = {}
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1005)
+    w = wl.LLAMA8B
+    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
+        reps = []
+        for _ in range(4):
+            K = kvq.Cache.empty(mode, w.B, w.Hkv, w.S, w.D)
+            V = kvq.Cache.empty(mode, w.B, w.Hkv, w.S, w.D)
+            sl = torch.arange(w.kv_len, dtype=torch.int32, device=DEV)
+            for c in (K, V):
+                x = torch.randn((w.B, w.Hkv, w.kv_len, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+                kvq.quant_scatter(x, sl, c)
+            reps.append((K, V))
+        q = torch.randn((w.B, w.Hq, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
+        kvl = i32(w.kv_len)
+        it = iter(range(10 ** 9))
+
+        def dec():
+            K, V = reps[next(it) % 4]
+            kvq.sdpa_decode(q, K, V, kv_len=kvl, out=out, workspace=ws)
+        ms = time_ms(dec, iters=10, inner=8)
+        rb = w.D if mode == kvq.FP8E4M3_B32 else w.D // 2
+        sb = (w.D // 32) * (4 if mode == kvq.FP8E4M3_B32 else 1)
+        nbytes = 2 * w.B * w.Hkv * w.kv_len * (rb + sb) + 2 * w.B * w.Hq * w.D * 2
+        res[f"decode_llama8b_{name}"] = {"us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
+                                         "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+        del reps
+    w = wl.LONGPREFILL
+    end = w.chunk_ends[0]
+    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
+        K = kvq.Cache.empty(mode, w.B, w.Hkv, end, w.D)
+        V = kvq.Cache.empty(mode, w.B, w.Hkv, end, w.D)
+        blk = 8192
+        for j0 in range(0, end, blk):
+            sl = torch.arange(j0, j0 + blk, dtype=torch.int32, device=DEV)
+            for c in (K, V):
+                x = torch.randn((w.B, w.Hkv, blk, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+                kvq.quant_scatter(x, sl, c)
+        q = torch.randn((w.B, w.Hq, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        kvl = i32(end)
+        ms = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=3, inner=1)
+        pairs = w.Lq * (end - w.Lq) + w.Lq * (w.Lq + 1) // 2
+        tfs = 4.0 * w.D * w.Hq * pairs / ms / 1e9
+        res[f"prefill_d256_kv{end}_{name}"] = {"ms": round(ms, 3), "tflops": round(tfs, 1),
+                                               "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4)}
+        del K, V
+    return res
+
+
 # --------------------------------------------------------------------------
 
 def main():
@@ -448,6 +506,8 @@ def main():
         log("[bench] sink/ring done")
         sec["long_prefill_uint4_d256"] = leg_long_prefill()
         log("[bench] long prefill done")
+        sec["block_cache_attention"] = leg_block_attention()
+        log("[bench] block-cache attention done")
         result["secondary"] = sec
     print(json.dumps(result))
 
