@@ -91,3 +91,39 @@ def test_block_decode_llama_shape(qmode):
     q = wl.to_bf16_values(np.random.default_rng(32).standard_normal((w.B, w.Hq, 1, w.D)).astype(np.float32))
     ref = oracle.sdpa(q, K[1], V[1], w.kv_len)
     check_attention(run_decode(q, K, V, w.kv_len), ref, "llama shape")
+
+
+@pytest.mark.parametrize("qmode", BLOCK_MODES)
+def test_block_decode_every_code(qmode):
+    """With kv_len = 1 the softmax weight is exactly 1, so the fp32 output is
+    the dequantized V row itself: every FP8 code (the two NaN codes, which no
+    encoder emits, replaced by 0x00) and every FP4 code at scale 1 must come
+    out exactly as the oracle's decoders give them."""
+    B, Hkv, G, S, D = 2, 1, 1, 4, 128
+    say(f"block decode every code qmode={qmode}")
+    K = kvq.Cache.empty(qmode, B, Hkv, S, D)
+    V = kvq.Cache.empty(qmode, B, Hkv, S, D)
+    if qmode == kvq.FP8E4M3_B32:
+        codes = np.arange(256, dtype=np.uint8).reshape(B, D)
+        codes[codes == 0x7F] = 0
+        codes[codes == 0xFF] = 0
+        ref = np.array([[oracle.e4m3fn_decode(int(c)) for c in row] for row in codes])
+        one = np.ones((B, Hkv, S, D // 32), np.float32)
+        for c in (K, V):
+            c.scales.copy_(torch.from_numpy(one))
+    else:
+        nib = (np.arange(B * D) % 16).astype(np.uint8)
+        nib = np.random.default_rng(5).permutation(nib).reshape(B, D)
+        codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+        ref = np.array([[oracle.e2m1_decode(int(c)) for c in row] for row in nib])
+        for c in (K, V):
+            c.scales.fill_(127)                       # E8M0 2^0
+    for c in (K, V):
+        c.codes.zero_()
+        c.codes[:, 0, 0, :] = torch.from_numpy(codes).to(DEV)
+    q = torch.zeros((B, Hkv * G, 1, D), dtype=torch.bfloat16, device=DEV)
+    out = kvq.sdpa_decode(q, K, V, kv_len=torch.tensor([1], dtype=torch.int32, device=DEV), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out[:, 0, 0, :].cpu().numpy()
+    # value equality (a -0 code sums to +0 in the accumulator)
+    assert np.array_equal(got, ref.astype(np.float32)), np.argwhere(got != ref.astype(np.float32))[:8]
