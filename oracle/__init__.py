@@ -22,6 +22,10 @@ _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
 INT8_TH, UINT4_TH, FP8E4M3_B32, MXFP4_B32 = 0, 1, 2, 3
+MXFP8_B32, FP8E5M2_B32, INT8_B32 = 4, 5, 6
+BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32)
+E8M0_MODES = (MXFP4_B32, MXFP8_B32)
+MX_SCALE_OCP = 1            # quantize option: MX scale by the OCP floor rule
 FLAG_SLOT_RANGE, FLAG_KVLEN, FLAG_POS_CAPACITY = 1, 2, 4
 
 CFLAGS = ["-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
@@ -67,20 +71,31 @@ def _declare(L):
     L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
     L.orc_e8m0_ceil.restype = ctypes.c_uint8
     L.orc_e8m0_ceil.argtypes = [ctypes.c_float]
-    for name in ("orc_e4m3fn_encode_array", "orc_e2m1_encode_array", "orc_e8m0_ceil_array"):
+    for name in ("orc_e4m3fn_encode_array", "orc_e2m1_encode_array", "orc_e8m0_ceil_array",
+                 "orc_e5m2_encode_array"):
         f = getattr(L, name)
         f.restype = None
         f.argtypes = [_P, _P, _LL]
+    L.orc_e5m2_decode.restype = ctypes.c_float
+    L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+    L.orc_e8m0_floor_array.restype = None
+    L.orc_e8m0_floor_array.argtypes = [_P, _I, _P, _LL]
     L.orc_affine_params.restype = None
     L.orc_affine_params.argtypes = [_P, _I, _I, _I, _P, _P]
     L.orc_quantize_rows.restype = None
     L.orc_quantize_rows.argtypes = [_I, _P, _I, _I, _P, _P, _P]
+    L.orc_quantize_rows_f.restype = None
+    L.orc_quantize_rows_f.argtypes = [_I, _I, _P, _I, _I, _P, _P, _P]
     L.orc_dequantize_rows.restype = None
     L.orc_dequantize_rows.argtypes = [_I, _P, _P, _P, _I, _I, _P]
     for name in ("orc_quant_scatter", "orc_quant_scatter_par"):
         f = getattr(L, name)
         f.restype = _I
         f.argtypes = [_I, _P, _I, _I, _I, _I, _P, _LL, _I, _P, _P, _P]
+    for name in ("orc_quant_scatter_f", "orc_quant_scatter_par_f"):
+        f = getattr(L, name)
+        f.restype = _I
+        f.argtypes = [_I, _I, _P, _I, _I, _I, _I, _P, _LL, _I, _P, _P, _P]
     L.orc_positions_sink.restype = _I
     L.orc_positions_sink.argtypes = [_I, _I, _I, _I, _P, _P]
     L.orc_positions_full.restype = _I
@@ -132,6 +147,24 @@ def e8m0_ceil(s):
     return out
 
 
+def e5m2_encode(y):
+    y = _c(np.asarray(y, dtype=np.float32), np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e5m2_encode_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def e8m0_floor(amax, emax: int):
+    a = _c(np.asarray(amax, dtype=np.float32), np.float32)
+    out = np.empty(a.shape, np.uint8)
+    lib().orc_e8m0_floor_array(_ptr(a), int(emax), _ptr(out), a.size)
+    return out
+
+
+def e5m2_decode(code: int) -> float:
+    return lib().orc_e5m2_decode(int(code))
+
+
 def e4m3fn_decode(code: int) -> float:
     return lib().orc_e4m3fn_decode(int(code))
 
@@ -157,20 +190,23 @@ def row_bytes(qmode: int, D: int) -> int:
 
 
 def scales_per_row(qmode: int, D: int) -> int:
-    return D // 32 if qmode in (FP8E4M3_B32, MXFP4_B32) else 1
+    return D // 32 if qmode in BLOCK_MODES else 1
+
+
+def scale_dtype(qmode: int):
+    return np.uint8 if qmode in E8M0_MODES else np.float32
 
 
 class HostCache:
     """Host copy of one quantized cache: codes [B,H,S,row_bytes] uint8,
-    scales [B,H,S,spr] (float32, or uint8 E8M0 for MX-FP4), zps [B,H,S] int8
+    scales [B,H,S,spr] (float32, or uint8 E8M0 for the MX modes), zps [B,H,S] int8
     (affine modes).  ``fill`` writes the sentinel pattern used to detect
     stray writes and reads: codes 0xA5, scales NaN / 0xFF, zp 0x5A."""
 
     def __init__(self, qmode, B, H, S, D, fill=True):
         self.qmode, self.B, self.H, self.S, self.D = qmode, B, H, S, D
         self.codes = np.empty((B, H, S, row_bytes(qmode, D)), np.uint8)
-        sdt = np.uint8 if qmode == MXFP4_B32 else np.float32
-        self.scales = np.empty((B, H, S, scales_per_row(qmode, D)), sdt)
+        self.scales = np.empty((B, H, S, scales_per_row(qmode, D)), scale_dtype(qmode))
         self.zps = np.empty((B, H, S), np.int8) if qmode in (INT8_TH, UINT4_TH) else None
         if fill:
             self.sentinel_fill()
@@ -193,22 +229,22 @@ class HostCache:
         return c
 
 
-def quantize_rows(qmode, x):
-    """Quantize rows x[..., D] (float32) -> (codes, scales, zps)."""
+def quantize_rows(qmode, x, flags=0):
+    """Quantize rows x[..., D] (float32) -> (codes, scales, zps).  flags:
+    MX_SCALE_OCP for the MX modes."""
     x = _c(np.asarray(x, dtype=np.float32), np.float32)
     D = x.shape[-1]
     n = x.size // D
     codes = np.empty(x.shape[:-1] + (row_bytes(qmode, D),), np.uint8)
-    sdt = np.uint8 if qmode == MXFP4_B32 else np.float32
-    scales = np.empty(x.shape[:-1] + (scales_per_row(qmode, D),), sdt)
+    scales = np.empty(x.shape[:-1] + (scales_per_row(qmode, D),), scale_dtype(qmode))
     zps = np.empty(x.shape[:-1], np.int8)
-    lib().orc_quantize_rows(qmode, _ptr(x), n, D, _ptr(codes), _ptr(scales), _ptr(zps))
+    lib().orc_quantize_rows_f(qmode, int(flags), _ptr(x), n, D, _ptr(codes), _ptr(scales), _ptr(zps))
     return codes, scales, (zps if qmode in (INT8_TH, UINT4_TH) else None)
 
 
 def dequantize_rows(qmode, codes, scales, zps, D):
     codes = _c(codes, np.uint8)
-    scales = _c(scales, np.uint8 if qmode == MXFP4_B32 else np.float32)
+    scales = _c(scales, scale_dtype(qmode))
     n = codes.size // row_bytes(qmode, D)
     out = np.empty(codes.shape[:-1] + (D,), np.float64)
     z = None if zps is None else _c(zps, np.int8)
@@ -216,9 +252,10 @@ def dequantize_rows(qmode, codes, scales, zps, D):
     return out
 
 
-def quant_scatter(cache: HostCache, x, slot_mapping, slot_stride_b=None, parallel=False):
+def quant_scatter(cache: HostCache, x, slot_mapping, slot_stride_b=None, parallel=False, qflags=0):
     """Quantize x[B,H,T,D] (float32 values) and scatter into ``cache`` in place.
-    slot_mapping is int32 [B,T] (or [T] with slot_stride_b=0).  Returns flags."""
+    slot_mapping is int32 [B,T] (or [T] with slot_stride_b=0); qflags:
+    MX_SCALE_OCP for the MX modes.  Returns the error flags."""
     x = _c(np.asarray(x, dtype=np.float32), np.float32)
     B, H, T, D = x.shape
     if (B, H, D) != (cache.B, cache.H, cache.D):
@@ -226,8 +263,8 @@ def quant_scatter(cache: HostCache, x, slot_mapping, slot_stride_b=None, paralle
     sm = _c(np.asarray(slot_mapping, dtype=np.int32), np.int32)
     if slot_stride_b is None:
         slot_stride_b = 0 if sm.ndim == 1 else sm.shape[-1]
-    f = lib().orc_quant_scatter_par if parallel else lib().orc_quant_scatter
-    return f(cache.qmode, _ptr(x), B, H, T, D, _ptr(sm), slot_stride_b, cache.S,
+    f = lib().orc_quant_scatter_par_f if parallel else lib().orc_quant_scatter_f
+    return f(cache.qmode, int(qflags), _ptr(x), B, H, T, D, _ptr(sm), slot_stride_b, cache.S,
              _ptr(cache.codes), _ptr(cache.scales), _ptr(cache.zps))
 
 

@@ -46,6 +46,13 @@
  *   R11 mask: slot visible iff cp>=0, cp<=qp and (cp<sink or qp-cp<window).
  *   R13 a query row with no visible key outputs 0.
  *   R14 GQA: query head h reads KV head h / (Hq/Hkv).
+ *   R19 Q_MAX = 57344 (E5M2, largest finite), 127 (INT8: symmetric codes in
+ *       [-127, 127], two's complement in the uint8 cache).
+ *   R20 MX-FP8 (quant_mode 0) with round_scale = true: the E8M0 scale is the
+ *       smallest power of two >= amax / 448 (the same rounding as R9).
+ *   R22 round_scale = false, and the OCP variant of MX-FP4: the scale is
+ *       2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 2 (E2M1), clamped to
+ *       the E8M0 range; elements beyond Q_MAX then saturate (R8).
  *
  * Parity pins: every function here is checked by the CPU tests against
  * closed forms, exhaustive grid search, library routines and hand-derived
@@ -62,6 +69,13 @@
 #define ORC_UINT4_TH 1
 #define ORC_FP8E4M3_B32 2
 #define ORC_MXFP4_B32 3
+#define ORC_MXFP8_B32 4     /* E4M3FN codes, E8M0 scale per 32 ([IQC] quant_mode 0) */
+#define ORC_FP8E5M2_B32 5   /* E5M2 codes, fp32 scale per 32 ([IQC] Normal mode, E5M2 cache) */
+#define ORC_INT8_B32 6      /* int8 codes in a uint8 cache, fp32 scale per 32 ([IQC] Normal, INT8) */
+
+/* Quantize option: the MX scale by the OCP floor rule (R22) instead of the
+ * smallest power of two >= amax / Q_MAX (R9). */
+#define ORC_MX_SCALE_OCP 1
 
 #define ORC_FLAG_SLOT_RANGE 1   /* slot outside [-1, n_slots) */
 #define ORC_FLAG_KVLEN 2        /* kv_len outside [Lq, n_slots] */
@@ -168,6 +182,54 @@ uint8_t orc_e8m0_ceil(float s) {
 
 float orc_e8m0_value(uint8_t b) { return ldexpf(1.0f, (int)b - 127); }
 
+/* E8M0 by the OCP floor rule (R22): biased exponent floor(log2 amax) - emax
+ * + 127, clamped to [0, 254]; amax == 0 gives 0.  floor(log2 amax) is read
+ * exactly from the fp32 bits (normal or subnormal). */
+uint8_t orc_e8m0_floor(float amax, int emax) {
+    if (!(amax > 0.0f)) return 0;
+    uint32_t bits;
+    memcpy(&bits, &amax, 4);
+    int ef = (int)((bits >> 23) & 0xFF);
+    int fl = ef == 0 ? (31 - __builtin_clz(bits & 0x7FFFFF)) - 149 : ef - 127;
+    int b = fl - emax + 127;
+    if (b < 0) b = 0;
+    if (b > 254) b = 254;
+    return (uint8_t)b;
+}
+
+/* FP8 E5M2: bias 15, 2 mantissa bits, subnormal step 2^-16, largest finite
+ * 57344; exponent 31 holds inf / NaN, which the encoder never produces
+ * (|y| >= 57344 saturates to 0x7B, R8).  Ties to the even mantissa, sign
+ * kept (R10).  [IQC] parameter table (FLOAT8_E5M2 cache). */
+static const float E5M2_MAX = 57344.0f;
+uint8_t orc_e5m2_encode(float y) {
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    float a = fabsf(y);
+    uint8_t mag;
+    if (!(a < E5M2_MAX)) {
+        mag = 0x7B;
+    } else if (a < 0x1p-14f) {             /* multiples of 2^-16 */
+        mag = (uint8_t)rintf(a * 65536.0f);  /* 4 is the smallest normal */
+    } else {
+        int e = fp32_floor_log2(a);        /* -14 .. 15 */
+        float frac = ldexpf(a, -e);
+        float m = rintf((frac - 1.0f) * 4.0f);
+        if (m == 4.0f) { m = 0.0f; e += 1; }
+        mag = (uint8_t)(((e + 15) << 2) | (int)m);
+        if (mag > 0x7B) mag = 0x7B;
+    }
+    return sign | mag;
+}
+
+float orc_e5m2_decode(uint8_t code) {
+    int s = code >> 7, e = (code >> 2) & 0x1F, m = code & 3;
+    float v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexpf((float)m, -16);
+    else v = ldexpf(1.0f + (float)m / 4.0f, e - 15);
+    return s ? -v : v;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Affine per token-head quantization (O2; [PR24473] Summary; [PR20351]      */
 /* nibble packing)                                                           */
@@ -207,8 +269,10 @@ int orc_affine_code(float x, float scale, int zp, int qmin, int qmax) {
 static int row_bytes(int qmode, int D) {
     return (qmode == ORC_UINT4_TH || qmode == ORC_MXFP4_B32) ? D / 2 : D;
 }
+static int is_block(int qmode) { return qmode >= ORC_FP8E4M3_B32; }
+static int e8m0_scales(int qmode) { return qmode == ORC_MXFP4_B32 || qmode == ORC_MXFP8_B32; }
 static int scales_per_row(int qmode, int D) {
-    return (qmode == ORC_FP8E4M3_B32 || qmode == ORC_MXFP4_B32) ? D / 32 : 1;
+    return is_block(qmode) ? D / 32 : 1;
 }
 
 int orc_row_bytes(int qmode, int D) { return row_bytes(qmode, D); }
@@ -216,7 +280,7 @@ int orc_scales_per_row(int qmode, int D) { return scales_per_row(qmode, D); }
 
 /* Quantize one vector x[D] into one cache row: codes (row_bytes bytes),
  * scales (float[] for INT8/UINT4/FP8, uint8 E8M0[] for MX-FP4), zp. */
-static void quantize_row(int qmode, const float* x, int D,
+static void quantize_row(int qmode, int flags, const float* x, int D,
                          uint8_t* codes, void* scales, int8_t* zp_out) {
     if (qmode == ORC_INT8_TH || qmode == ORC_UINT4_TH) {
         int qmin = qmode == ORC_INT8_TH ? -128 : 0;
@@ -245,21 +309,43 @@ static void quantize_row(int qmode, const float* x, int D,
             float a = fabsf(xg[i]);
             if (a > amax) amax = a;
         }
-        if (qmode == ORC_FP8E4M3_B32) {
-            float scale = amax / E4M3_MAX;
+        if (qmode == ORC_FP8E4M3_B32 || qmode == ORC_FP8E5M2_B32 || qmode == ORC_INT8_B32) {
+            /* fp32 scale = amax / Q_MAX; an all-zero block stores scale 0 and
+             * codes 0 (R7) */
+            float qmax = qmode == ORC_FP8E4M3_B32 ? E4M3_MAX : qmode == ORC_FP8E5M2_B32 ? E5M2_MAX : 127.0f;
+            float scale = amax / qmax;
             ((float*)scales)[g] = scale;
-            for (int i = 0; i < 32; ++i)
-                codes[32 * g + i] = scale == 0.0f ? 0x00            /* R7 */
-                                  : orc_e4m3fn_encode(xg[i] / scale);
+            for (int i = 0; i < 32; ++i) {
+                uint8_t c = 0x00;
+                if (scale != 0.0f) {
+                    float y = xg[i] / scale;
+                    if (qmode == ORC_FP8E4M3_B32) c = orc_e4m3fn_encode(y);
+                    else if (qmode == ORC_FP8E5M2_B32) c = orc_e5m2_encode(y);
+                    else {
+                        float r = rintf(y);
+                        if (r > 127.0f) r = 127.0f;
+                        if (r < -127.0f) r = -127.0f;
+                        c = (uint8_t)(int8_t)(int)r;
+                    }
+                }
+                codes[32 * g + i] = c;
+            }
         } else {
-            float s = amax / E2M1_MAX;
-            uint8_t e8 = orc_e8m0_ceil(s);
+            /* MX: E8M0 power-of-two scale X, codes of x / X (exact division) */
+            int fp4 = qmode == ORC_MXFP4_B32;
+            float qmax = fp4 ? E2M1_MAX : E4M3_MAX;
+            uint8_t e8 = (flags & ORC_MX_SCALE_OCP) ? orc_e8m0_floor(amax, fp4 ? 2 : 8)
+                                                    : orc_e8m0_ceil(amax / qmax);
             float X = orc_e8m0_value(e8);
             ((uint8_t*)scales)[g] = e8;
-            for (int i = 0; i < 16; ++i) {
-                uint8_t c0 = orc_e2m1_encode(xg[2 * i] / X);
-                uint8_t c1 = orc_e2m1_encode(xg[2 * i + 1] / X);
-                codes[16 * g + i] = (uint8_t)(c0 | (c1 << 4));
+            if (fp4) {
+                for (int i = 0; i < 16; ++i) {
+                    uint8_t c0 = orc_e2m1_encode(xg[2 * i] / X);
+                    uint8_t c1 = orc_e2m1_encode(xg[2 * i + 1] / X);
+                    codes[16 * g + i] = (uint8_t)(c0 | (c1 << 4));
+                }
+            } else {
+                for (int i = 0; i < 32; ++i) codes[32 * g + i] = orc_e4m3fn_encode(xg[i] / X);
             }
         }
     }
@@ -277,6 +363,13 @@ static double dequant_elem(int qmode, const uint8_t* codes, const void* scales,
     }
     case ORC_FP8E4M3_B32:
         return (double)orc_e4m3fn_decode(codes[d]) * (double)((const float*)scales)[d / 32];
+    case ORC_MXFP8_B32:
+        return (double)orc_e4m3fn_decode(codes[d]) *
+               (double)orc_e8m0_value(((const uint8_t*)scales)[d / 32]);
+    case ORC_FP8E5M2_B32:
+        return (double)orc_e5m2_decode(codes[d]) * (double)((const float*)scales)[d / 32];
+    case ORC_INT8_B32:
+        return (double)(int8_t)codes[d] * (double)((const float*)scales)[d / 32];
     default: {
         int c = (codes[d / 2] >> (4 * (d & 1))) & 0xF;
         return (double)orc_e2m1_decode((uint8_t)c) *
@@ -292,20 +385,24 @@ static size_t cache_row(int H, int S, int b, int h, int s) {
 }
 
 static void* scale_ptr(int qmode, void* scales, size_t row, int spr) {
-    if (qmode == ORC_MXFP4_B32) return (uint8_t*)scales + row * spr;
+    if (e8m0_scales(qmode)) return (uint8_t*)scales + row * spr;
     return (float*)scales + row * spr;
 }
 
 /* Quantize a row of one cache in place; exposed for the pin tests. */
-void orc_quantize_rows(int qmode, const float* x, int n_rows, int D,
-                       uint8_t* codes, void* scales, int8_t* zps) {
+void orc_quantize_rows_f(int qmode, int flags, const float* x, int n_rows, int D,
+                         uint8_t* codes, void* scales, int8_t* zps) {
     int rb = row_bytes(qmode, D), spr = scales_per_row(qmode, D);
     for (int r = 0; r < n_rows; ++r) {
         int8_t zp = 0;
-        quantize_row(qmode, x + (size_t)r * D, D, codes + (size_t)r * rb,
+        quantize_row(qmode, flags, x + (size_t)r * D, D, codes + (size_t)r * rb,
                      scale_ptr(qmode, scales, (size_t)r, spr), &zp);
         if (zps) zps[r] = zp;
     }
+}
+void orc_quantize_rows(int qmode, const float* x, int n_rows, int D,
+                       uint8_t* codes, void* scales, int8_t* zps) {
+    orc_quantize_rows_f(qmode, 0, x, n_rows, D, codes, scales, zps);
 }
 
 void orc_dequantize_rows(int qmode, const uint8_t* codes, const void* scales,
@@ -328,9 +425,9 @@ void orc_dequantize_rows(int qmode, const uint8_t* codes, const void* scales,
  * slot_mapping[b * slot_stride_b + t]; -1 skips the token, any other value
  * outside [0, n_slots) skips it and raises ORC_FLAG_SLOT_RANGE.  Every head
  * of token (b, t) is written to row (b, h, slot).  Returns the flags. */
-int orc_quant_scatter(int qmode, const float* x, int B, int H, int T, int D,
-                      const int32_t* slot_mapping, long long slot_stride_b,
-                      int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
+int orc_quant_scatter_f(int qmode, int qflags, const float* x, int B, int H, int T, int D,
+                        const int32_t* slot_mapping, long long slot_stride_b,
+                        int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
     int flags = 0;
     int rb = row_bytes(qmode, D), spr = scales_per_row(qmode, D);
     for (int b = 0; b < B; ++b)
@@ -341,12 +438,17 @@ int orc_quant_scatter(int qmode, const float* x, int B, int H, int T, int D,
             for (int h = 0; h < H; ++h) {
                 size_t row = cache_row(H, n_slots, b, h, s);
                 int8_t zp = 0;
-                quantize_row(qmode, x + (((size_t)b * H + h) * T + t) * D, D,
+                quantize_row(qmode, qflags, x + (((size_t)b * H + h) * T + t) * D, D,
                              codes + row * rb, scale_ptr(qmode, scales, row, spr), &zp);
                 if (qmode == ORC_INT8_TH || qmode == ORC_UINT4_TH) zps[row] = zp;
             }
         }
     return flags;
+}
+int orc_quant_scatter(int qmode, const float* x, int B, int H, int T, int D,
+                      const int32_t* slot_mapping, long long slot_stride_b,
+                      int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
+    return orc_quant_scatter_f(qmode, 0, x, B, H, T, D, slot_mapping, slot_stride_b, n_slots, codes, scales, zps);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -524,9 +626,9 @@ void orc_e8m0_ceil_array(const float* s, uint8_t* out, long long n) {
 /* Quantize-scatter in parallel over batches for large caches: the same
  * arithmetic as orc_quant_scatter, rows split over threads.  Used to build
  * long histories (the arithmetic is per row, so the order does not matter). */
-int orc_quant_scatter_par(int qmode, const float* x, int B, int H, int T, int D,
-                          const int32_t* slot_mapping, long long slot_stride_b,
-                          int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
+int orc_quant_scatter_par_f(int qmode, int qflags, const float* x, int B, int H, int T, int D,
+                            const int32_t* slot_mapping, long long slot_stride_b,
+                            int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
     int flags = 0;
     int rb = row_bytes(qmode, D), spr = scales_per_row(qmode, D);
     long long n = (long long)B * H * T;
@@ -540,9 +642,22 @@ int orc_quant_scatter_par(int qmode, const float* x, int B, int H, int T, int D,
         if (s < -1 || s >= n_slots) { flags |= ORC_FLAG_SLOT_RANGE; continue; }
         size_t row = cache_row(H, n_slots, b, h, s);
         int8_t zp = 0;
-        quantize_row(qmode, x + (size_t)i * D, D, codes + row * rb,
+        quantize_row(qmode, qflags, x + (size_t)i * D, D, codes + row * rb,
                      scale_ptr(qmode, scales, row, spr), &zp);
         if (qmode == ORC_INT8_TH || qmode == ORC_UINT4_TH) zps[row] = zp;
     }
     return flags;
+}
+
+int orc_quant_scatter_par(int qmode, const float* x, int B, int H, int T, int D,
+                          const int32_t* slot_mapping, long long slot_stride_b,
+                          int n_slots, uint8_t* codes, void* scales, int8_t* zps) {
+    return orc_quant_scatter_par_f(qmode, 0, x, B, H, T, D, slot_mapping, slot_stride_b, n_slots, codes, scales, zps);
+}
+
+void orc_e5m2_encode_array(const float* y, uint8_t* out, long long n) {
+    for (long long i = 0; i < n; ++i) out[i] = orc_e5m2_encode(y[i]);
+}
+void orc_e8m0_floor_array(const float* a, int emax, uint8_t* out, long long n) {
+    for (long long i = 0; i < n; ++i) out[i] = orc_e8m0_floor(a[i], emax);
 }

@@ -133,3 +133,73 @@ def test_e8m0_smallest_power_of_two_at_or_above(orc):
     assert orc.e8m0_ceil([0.0])[0] == 0
     assert list(orc.e8m0_ceil([1.0, 1.5, 2.0, 0.75, 2.0 ** -127, 2.0 ** -126 * 1.5])) == \
         [127, 128, 128, 127, 0, 2]
+
+
+def _e5m2_grid():
+    """Finite non-negative E5M2 values, index = 7-bit magnitude code (bias 15,
+    2 mantissa bits; exponent 31 is inf / NaN)."""
+    vals = []
+    for code in range(0x7C):
+        e, m = code >> 2, code & 3
+        vals.append(m * 2.0 ** -16 if e == 0 else (1 + m / 4) * 2.0 ** (e - 15))
+    return np.array(vals, np.float64)
+
+
+def test_e5m2_grid_is_the_format():
+    g = _e5m2_grid()
+    assert g[0x7B] == 57344.0 and g[1] == 2.0 ** -16 and g[4] == 2.0 ** -14
+    assert np.all(np.diff(g) > 0)
+
+
+def test_e5m2_decode_is_the_top_byte_of_fp16(orc):
+    """E5M2 is fp16 with the low mantissa byte dropped: code c decodes to the
+    fp16 value with bits c << 8 (inf and NaN codes included)."""
+    for c in range(256):
+        h = np.array([c << 8], np.uint16).view(np.float16)[0]
+        v = orc.e5m2_decode(c)
+        assert (np.isnan(h) and np.isnan(v)) or (float(h) == v and np.signbit(h) == np.signbit(v)), c
+
+
+def test_e5m2_exhaustive_bf16(orc):
+    y = _all_finite_bf16_as_f32()
+    got = orc.e5m2_encode(y)
+    want = _nearest_even(y, _e5m2_grid(), 0x80)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first y={y[bad[:5]]} got={got[bad[:5]]} want={want[bad[:5]]}"
+
+
+def test_e5m2_midpoints_and_torch_cast(orc):
+    g = _e5m2_grid()
+    mids = ((g[1:] + g[:-1]) / 2).astype(np.float32)
+    r = np.random.default_rng(17)
+    rand = (r.standard_normal(20000) * r.choice([1e-4, 0.1, 1, 300, 20000], 20000)).astype(np.float32)
+    y = np.concatenate([mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)), rand,
+                        np.array([57344, 57345, 61439, 61440, 1e30, -1e30, 0.0, -0.0], np.float32)])
+    assert np.array_equal(orc.e5m2_encode(y), _nearest_even(y, g, 0x80))
+    # torch's float8_e5m2 cast (a library routine), away from saturation
+    inside = y[np.abs(y) < 57344]
+    want = torch.from_numpy(inside).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(orc.e5m2_encode(inside), want)
+    assert orc.e5m2_encode([-0.0])[0] == 0x80 and orc.e5m2_encode([1e9])[0] == 0x7B
+    for c in range(0x7C):
+        assert orc.e5m2_encode([orc.e5m2_decode(c)])[0] == c
+
+
+@pytest.mark.parametrize("emax", [2, 8])
+def test_e8m0_floor_rule(orc, emax):
+    """OCP floor rule: X = 2^(b - 127) with X * 2^emax <= amax < X * 2^(emax+1)
+    inside the E8M0 range; amax = 0 gives 0; the ends clamp to [0, 254]."""
+    pos = _all_finite_bf16_as_f32()
+    pos = pos[pos > 0]
+    r = np.random.default_rng(13)
+    rand = np.abs(r.standard_normal(100000)).astype(np.float32) * \
+        np.float32(2.0) ** r.integers(-140, 120, 100000).astype(np.float32)
+    a = np.concatenate([pos, rand[rand > 0]])
+    b = orc.e8m0_floor(a, emax).astype(np.int64)
+    X = np.ldexp(1.0, b - 127)
+    inside = (b > 0) & (b < 254)
+    ratio = a[inside].astype(np.float64) / X[inside]
+    assert np.all(ratio >= 2.0 ** emax) and np.all(ratio < 2.0 ** (emax + 1))
+    assert orc.e8m0_floor([0.0], emax)[0] == 0
+    assert orc.e8m0_floor([3e38], emax)[0] == 127 + 127 - emax
+    assert orc.e8m0_floor([1e-44], emax)[0] == 0

@@ -193,3 +193,100 @@ def test_scatter_broadcast_slots_over_batch(orc):
     orc.quant_scatter(c1, x, np.array([5, 1, 6], np.int32))
     orc.quant_scatter(c2, x, np.array([[5, 1, 6], [5, 1, 6]], np.int32))
     assert np.array_equal(c1.codes, c2.codes) and np.array_equal(c1.zps, c2.zps)
+
+
+@pytest.mark.parametrize("ex", GOLD["e5m2_block"], ids=lambda e: e["name"])
+def test_e5m2_block_worked_examples(orc, ex):
+    codes, scales, _ = orc.quantize_rows(orc.FP8E5M2_B32, _block_x(ex["x_head"])[None])
+    assert scales[0, 0] == np.float32(ex["scale"])
+    assert list(codes[0, :len(ex["codes_head"])]) == ex["codes_head"]
+    assert np.all(codes[0, len(ex["codes_head"]):32] == 0)
+
+
+@pytest.mark.parametrize("ex", GOLD["int8_block"], ids=lambda e: e["name"])
+def test_int8_block_worked_examples(orc, ex):
+    codes, scales, _ = orc.quantize_rows(orc.INT8_B32, _block_x(ex["x_head"])[None])
+    assert scales[0, 0] == np.float32(ex["scale"])
+    assert list(codes[0, :len(ex["codes_head"])]) == ex["codes_head"]
+    assert np.all(codes[0, len(ex["codes_head"]):32] == 0)
+
+
+@pytest.mark.parametrize("ex", GOLD["mxfp8_block"], ids=lambda e: e["name"])
+def test_mxfp8_block_worked_examples(orc, ex):
+    flags = orc.MX_SCALE_OCP if ex["ocp"] else 0
+    codes, scales, _ = orc.quantize_rows(orc.MXFP8_B32, _block_x(ex["x_head"])[None], flags=flags)
+    assert scales[0, 0] == ex["e8m0"]
+    assert list(codes[0, :len(ex["codes_head"])]) == ex["codes_head"]
+    assert np.all(codes[0, len(ex["codes_head"]):32] == 0)
+
+
+@pytest.mark.parametrize("ex", GOLD["mxfp4_ocp_block"], ids=lambda e: e["name"])
+def test_mxfp4_ocp_block_worked_examples(orc, ex):
+    codes, scales, _ = orc.quantize_rows(orc.MXFP4_B32, _block_x(ex["x_head"])[None], flags=orc.MX_SCALE_OCP)
+    assert scales[0, 0] == ex["e8m0"]
+    assert list(codes[0, :len(ex["packed_head"])]) == ex["packed_head"]
+
+
+def test_int8_block_properties(orc):
+    """Symmetric int8 per 32: scale = max|x_g| / 127 in fp32 (the page's
+    formula), codes in [-127, 127], the block maximum maps to +-127, and the
+    per-element dequantization error is at most scale / 2 (up to the fp32
+    rounding of the quotient)."""
+    rng = np.random.default_rng(19)
+    x = _vectors(rng, 400, 128)
+    codes, scales, zps = orc.quantize_rows(orc.INT8_B32, x)
+    assert zps is None
+    amax = np.abs(x.reshape(400, 4, 32)).max(axis=2)
+    assert np.array_equal(scales, amax / np.float32(127))
+    c = codes.view(np.int8).reshape(400, 4, 32).astype(np.int64)
+    assert c.min() >= -127 and c.max() <= 127
+    am = np.abs(x.reshape(400, 4, 32)).argmax(axis=2)
+    top = np.take_along_axis(np.abs(c), am[..., None], axis=2)[..., 0]
+    assert np.all(top[scales > 0] == 127)
+    xhat = orc.dequantize_rows(orc.INT8_B32, codes, scales, None, 128)
+    err = np.abs(x.astype(np.float64) - xhat).reshape(400, 4, 32)
+    # scale / 2, plus the fp32 rounding of x / scale before the rounding to an
+    # integer: half an ulp of a quotient below 128 is 2^-18
+    assert np.all(err <= scales[..., None].astype(np.float64) * (0.5 + 2.0 ** -18))
+
+
+@pytest.mark.parametrize("mode_name", ["e5m2", "mxfp8", "mxfp8_ocp", "mxfp4_ocp"])
+def test_new_block_mode_properties(orc, mode_name):
+    """Scale rules and the half-grid-step error bound of the FP8 / FP4 codes
+    (no saturation for the rounded-up scales; the OCP floor rule keeps
+    amax / X in [2^emax, 2^(emax+1)) and saturates beyond Q_MAX)."""
+    rng = np.random.default_rng(23)
+    x = _vectors(rng, 400, 128)
+    mode = {"e5m2": orc.FP8E5M2_B32, "mxfp8": orc.MXFP8_B32, "mxfp8_ocp": orc.MXFP8_B32,
+            "mxfp4_ocp": orc.MXFP4_B32}[mode_name]
+    flags = orc.MX_SCALE_OCP if mode_name.endswith("ocp") else 0
+    codes, scales, _ = orc.quantize_rows(mode, x, flags=flags)
+    xhat = orc.dequantize_rows(mode, codes, scales, None, 128).reshape(400, 4, 32)
+    g = x.reshape(400, 4, 32).astype(np.float64)
+    amax = np.abs(x.reshape(400, 4, 32)).max(axis=2).astype(np.float64)
+    if mode == orc.FP8E5M2_B32:
+        assert np.array_equal(scales, (amax / 57344).astype(np.float32)) or \
+            np.array_equal(scales, np.abs(x.reshape(400, 4, 32)).max(axis=2) / np.float32(57344))
+        S = scales.astype(np.float64)
+        y = np.abs(g) / np.where(S == 0, 1, S)[..., None]
+        e = np.floor(np.log2(np.maximum(y, 2.0 ** -14)))
+        half = np.ldexp(1.0, (e - 3).astype(int)) * S[..., None]        # half of 2^(e-2)
+        assert np.all(np.abs(g - xhat) <= half * (1 + 1e-6) + 1e-45)
+        return
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    emax, qmax, mbits = (8, 448.0, 3) if mode == orc.MXFP8_B32 else (2, 6.0, 1)
+    ok = amax > 0
+    if flags:
+        r = amax[ok] / X[ok]
+        assert np.all(r >= 2.0 ** emax) and np.all(r < 2.0 ** (emax + 1))
+    else:
+        assert np.all(X[ok] >= amax[ok] / qmax) and np.all(X[ok] / 2 < amax[ok] / qmax)
+    y = np.abs(g) / X[..., None]
+    sat = y > qmax
+    assert flags or not sat.any()
+    # saturated elements decode to +-Q_MAX * X with the element's sign
+    assert np.all(xhat[sat] == np.sign(g[sat]) * qmax * np.broadcast_to(X[..., None], g.shape)[sat])
+    e = np.floor(np.log2(np.maximum(y, 2.0 ** (1 - (7 if mode == orc.MXFP8_B32 else 1)) * 1.0)))
+    half = np.ldexp(1.0, (e - mbits - 1).astype(int)) * X[..., None]
+    err = np.abs(g - xhat)
+    assert np.all(err[~sat] <= half[~sat] * (1 + 1e-6) + 1e-45)
