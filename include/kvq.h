@@ -26,14 +26,13 @@
  *   cache codes      [B, H, S, row_bytes] uint8           ([PR20351] positions
  *                                   on dim 2, nibble packing on the last dim)
  *   cache scales     INT8_TH/UINT4_TH: float [B, H, S]
- *                    FP8E4M3_B32:      float [B, H, S, D/32]
- *                    MXFP4_B32:        uint8 E8M0 [B, H, S, D/32]
+ *                    FP8E4M3_B32, FP8E5M2_B32, INT8_B32: float [B, H, S, D/32]
+ *                    MXFP4_B32, MXFP8_B32: uint8 E8M0 [B, H, S, D/32]
  *   cache zps        INT8_TH/UINT4_TH: int8 [B, H, S]; NULL for block modes
  *   q / out          [B, Hq, Lq, D] contiguous             ([ABADDON]
  *                                   forward_attention)
- *   row_bytes        D for INT8_TH and FP8E4M3_B32, D/2 for UINT4_TH and
- *                    MXFP4_B32 (two codes per byte, element 2i in the low
- *                    nibble).
+ *   row_bytes        D/2 for UINT4_TH and MXFP4_B32 (two codes per byte,
+ *                    element 2i in the low nibble), D for the other modes.
  *
  * Device error flags: entry points that take `int32_t* err_flags` (device,
  * nullable) OR these bits into it when the data (not the arguments) is out of
@@ -64,7 +63,10 @@ typedef enum kvq_qmode {
     KVQ_INT8_TH = 0,      /* per token-head affine int8, fp32 scale, int8 zp [PR24473] */
     KVQ_UINT4_TH = 1,     /* per token-head affine 4-bit, two codes per byte [PR20351] */
     KVQ_FP8E4M3_B32 = 2,  /* per-32 block FP8-E4M3FN + fp32 scale, amax/448 [IQC] */
-    KVQ_MXFP4_B32 = 3     /* per-32 block FP4-E2M1 + E8M0 scale [IQC] */
+    KVQ_MXFP4_B32 = 3,    /* per-32 block FP4-E2M1 + E8M0 scale [IQC] */
+    KVQ_MXFP8_B32 = 4,    /* per-32 block FP8-E4M3FN + E8M0 scale (MX-FP8 mode) [IQC] */
+    KVQ_FP8E5M2_B32 = 5,  /* per-32 block FP8-E5M2 + fp32 scale, amax/57344 [IQC] */
+    KVQ_INT8_B32 = 6      /* per-32 block symmetric int8 in a uint8 plane + fp32 scale, amax/127 [IQC] */
 } kvq_qmode;
 
 typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -75,6 +77,12 @@ typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
 #define KVQ_NO_CAUSAL_SKIP 1u    /* prefill: scan all KV tiles below kv_len
                                     (the per-tile causal bound switched off) */
+
+#define KVQ_MX_SCALE_OCP 1u      /* quantize, MX modes: E8M0 scale 2^(floor(log2 amax)
+                                    - emax) (emax 2 for E2M1, 8 for E4M3; elements
+                                    past Q_MAX saturate) instead of the smallest
+                                    power of two >= amax / Q_MAX.  The reading of
+                                    [IQC]'s round_scale = false. */
 
 /* One quantized cache (K or V).  Caller-owned device planes, see layouts. */
 typedef struct kvq_cache {
@@ -119,6 +127,16 @@ kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, in
                              int64_t stride_b, int64_t stride_h, int64_t stride_t,
                              const int32_t* slot_mapping, int64_t slot_stride_b,
                              const kvq_cache* cache, int32_t* err_flags, void* stream);
+
+/* kvq_quant_scatter with quantization options: flags = 0 is kvq_quant_scatter;
+ * KVQ_MX_SCALE_OCP selects the floor rule for the E8M0 scale of MXFP4_B32 and
+ * MXFP8_B32 caches.  KVQ_ERR_UNSUPPORTED for unknown bits or for an option the
+ * cache's mode does not have. */
+kvq_status kvq_quant_scatter_flags(const void* x, int x_dtype, int B, int H, int T, int D,
+                                   int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                   const int32_t* slot_mapping, int64_t slot_stride_b,
+                                   const kvq_cache* cache, unsigned flags, int32_t* err_flags,
+                                   void* stream);
 
 /* The K and V update of one step in a single launch ([PR24473] writes new
  * keys and values into their two caches through the same slot indices):

@@ -23,7 +23,13 @@ LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 # kvq_qmode
 INT8_TH, UINT4_TH, FP8E4M3_B32, MXFP4_B32 = 0, 1, 2, 3
-QMODES = {"int8": INT8_TH, "uint4": UINT4_TH, "fp8": FP8E4M3_B32, "mxfp4": MXFP4_B32}
+MXFP8_B32, FP8E5M2_B32, INT8_B32 = 4, 5, 6
+QMODES = {"int8": INT8_TH, "uint4": UINT4_TH, "fp8": FP8E4M3_B32, "mxfp4": MXFP4_B32, "mxfp8": MXFP8_B32,
+          "fp8e5m2": FP8E5M2_B32, "int8_block": INT8_B32}
+BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32)
+E8M0_MODES = (MXFP4_B32, MXFP8_B32)
+# quantize options
+MX_SCALE_OCP = 1
 # kvq_dtype
 F32, BF16 = 0, 1
 # device error flags
@@ -31,7 +37,8 @@ FLAG_SLOT_RANGE, FLAG_KVLEN, FLAG_POS_CAPACITY = 1, 2, 4
 NO_CAUSAL_SKIP = 1
 
 EXPORTS = (
-    "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_quant_scatter_kv", "kvq_positions_with_sink",
+    "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_quant_scatter_flags", "kvq_quant_scatter_kv",
+    "kvq_positions_with_sink",
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_prefill",
 )
@@ -67,6 +74,9 @@ def lib():
         L.kvq_cache_bytes.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
         L.kvq_quant_scatter.restype = _I
         L.kvq_quant_scatter.argtypes = [_P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, _P, _P]
+        L.kvq_quant_scatter_flags.restype = _I
+        L.kvq_quant_scatter_flags.argtypes = [_P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, ctypes.c_uint,
+                                              _P, _P]
         L.kvq_quant_scatter_kv.restype = _I
         L.kvq_quant_scatter_kv.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, _CP, _P, _P]
         L.kvq_positions_with_sink.restype = _I
@@ -150,9 +160,9 @@ class Cache:
     def empty(qmode, B, H, S, D, device="cuda"):
         cb, sb, zb = cache_bytes(qmode, B, H, S, D)
         rb = cb // (B * H * S)
-        spr = (D // 32) if qmode in (FP8E4M3_B32, MXFP4_B32) else 1
+        spr = (D // 32) if qmode in BLOCK_MODES else 1
         codes = torch.empty((B, H, S, rb), dtype=torch.uint8, device=device)
-        sdt = torch.uint8 if qmode == MXFP4_B32 else torch.float32
+        sdt = torch.uint8 if qmode in E8M0_MODES else torch.float32
         scales = torch.empty((B, H, S, spr), dtype=sdt, device=device)
         zps = torch.empty((B, H, S), dtype=torch.int8, device=device) if zb else None
         return Cache(qmode, B, H, S, D, codes, scales, zps)
@@ -180,9 +190,10 @@ class Cache:
 # Entry points
 # --------------------------------------------------------------------------
 
-def quant_scatter(x: torch.Tensor, slot_mapping: torch.Tensor, cache: Cache, err_flags=None, stream=None):
-    """kvq_quant_scatter: x [B, H, T, D] (bf16/fp32, D contiguous); slot_mapping
-    int32 [B, T] or [T] (shared over the batch)."""
+def quant_scatter(x: torch.Tensor, slot_mapping: torch.Tensor, cache: Cache, err_flags=None, stream=None, flags=0):
+    """kvq_quant_scatter (kvq_quant_scatter_flags when flags != 0): x [B, H, T, D]
+    (bf16/fp32, D contiguous); slot_mapping int32 [B, T] or [T] (shared over
+    the batch); flags: MX_SCALE_OCP for the MX modes."""
     _need_cuda(x, slot_mapping, err_flags)
     if x.dim() != 4 or x.stride(3) != 1:
         raise ValueError("x must be [B, H, T, D] with D contiguous")
@@ -191,6 +202,11 @@ def quant_scatter(x: torch.Tensor, slot_mapping: torch.Tensor, cache: Cache, err
     B, H, T, D = x.shape
     ssb = 0 if slot_mapping.dim() == 1 else slot_mapping.stride(0)
     c = cache.struct()
+    if flags:
+        _check("kvq_quant_scatter_flags", lib().kvq_quant_scatter_flags(
+            _ptr(x), _dtype_code(x), B, H, T, D, x.stride(0), x.stride(1), x.stride(2),
+            _ptr(slot_mapping), ssb, ctypes.byref(c), int(flags), _ptr(err_flags), _stream(stream)))
+        return
     _check("kvq_quant_scatter", lib().kvq_quant_scatter(
         _ptr(x), _dtype_code(x), B, H, T, D, x.stride(0), x.stride(1), x.stride(2),
         _ptr(slot_mapping), ssb, ctypes.byref(c), _ptr(err_flags), _stream(stream)))

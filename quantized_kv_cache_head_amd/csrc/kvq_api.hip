@@ -16,11 +16,13 @@ namespace {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int row_bytes(int qmode, int D) { return (qmode == KVQ_UINT4_TH || qmode == KVQ_MXFP4_B32) ? D / 2 : D; }
-int scales_per_row(int qmode, int D) { return (qmode == KVQ_FP8E4M3_B32 || qmode == KVQ_MXFP4_B32) ? D / 32 : 1; }
 bool is_affine(int qmode) { return qmode == KVQ_INT8_TH || qmode == KVQ_UINT4_TH; }
+bool is_mx(int qmode) { return qmode == KVQ_MXFP4_B32 || qmode == KVQ_MXFP8_B32; }
+int scales_per_row(int qmode, int D) { return is_affine(qmode) ? 1 : D / 32; }
+int scale_bytes(int qmode) { return is_mx(qmode) ? 1 : 4; }
 
 kvq_status check_dims(int qmode, int D) {
-    if (qmode < KVQ_INT8_TH || qmode > KVQ_MXFP4_B32) return KVQ_ERR_DTYPE;
+    if (qmode < KVQ_INT8_TH || qmode > KVQ_INT8_B32) return KVQ_ERR_DTYPE;
     if (D <= 0 || D > 8192) return KVQ_ERR_SHAPE;
     if (is_affine(qmode) ? (D % 8 != 0) : (D % 32 != 0)) return KVQ_ERR_SHAPE;
     return KVQ_OK;
@@ -62,17 +64,20 @@ KVQ_API kvq_status kvq_cache_bytes(int qmode, int B, int H, int n_slots, int D, 
     if (B <= 0 || H <= 0 || n_slots <= 0) return KVQ_ERR_SHAPE;
     const size_t rows = (size_t)B * H * n_slots;
     if (codes_bytes) *codes_bytes = rows * row_bytes(qmode, D);
-    if (scales_bytes) *scales_bytes = rows * scales_per_row(qmode, D) * (qmode == KVQ_MXFP4_B32 ? 1 : 4);
+    if (scales_bytes) *scales_bytes = rows * scales_per_row(qmode, D) * scale_bytes(qmode);
     if (zps_bytes) *zps_bytes = is_affine(qmode) ? rows : 0;
     return KVQ_OK;
 }
 
-KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, int D, int64_t stride_b,
-                                     int64_t stride_h, int64_t stride_t, const int32_t* slot_mapping,
-                                     int64_t slot_stride_b, const kvq_cache* cache, int32_t* err_flags,
-                                     void* stream) {
+KVQ_API kvq_status kvq_quant_scatter_flags(const void* x, int x_dtype, int B, int H, int T, int D,
+                                           int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                           const int32_t* slot_mapping, int64_t slot_stride_b,
+                                           const kvq_cache* cache, unsigned flags, int32_t* err_flags,
+                                           void* stream) {
     kvq_status st = check_cache(cache);
     if (st != KVQ_OK) return st;
+    if ((flags & ~KVQ_MX_SCALE_OCP) || ((flags & KVQ_MX_SCALE_OCP) && !is_mx(cache->qmode)))
+        return KVQ_ERR_UNSUPPORTED;
     if (x_dtype != KVQ_F32 && x_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
     if (T < 0 || B != cache->batch || H != cache->heads || D != cache->head_dim) return KVQ_ERR_SHAPE;
     if (T == 0) return KVQ_OK;
@@ -84,7 +89,15 @@ KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, i
     return from_hip(kvq::launch_quant_scatter(cache->qmode, x_dtype == KVQ_BF16, x, B, H, T, D, stride_b, stride_h,
                                               stride_t, slot_mapping, slot_stride_b, cache->n_slots,
                                               reinterpret_cast<uint8_t*>(cache->codes), cache->scales, cache->zps,
-                                              err_flags, reinterpret_cast<hipStream_t>(stream)));
+                                              (int)flags, err_flags, reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, int D, int64_t stride_b,
+                                     int64_t stride_h, int64_t stride_t, const int32_t* slot_mapping,
+                                     int64_t slot_stride_b, const kvq_cache* cache, int32_t* err_flags,
+                                     void* stream) {
+    return kvq_quant_scatter_flags(x, x_dtype, B, H, T, D, stride_b, stride_h, stride_t, slot_mapping,
+                                   slot_stride_b, cache, 0u, err_flags, stream);
 }
 
 KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
@@ -157,6 +170,7 @@ kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_
     if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
         return KVQ_ERR_DTYPE;
     if (k->qmode != v->qmode) return KVQ_ERR_DTYPE;
+    if (k->qmode > KVQ_MXFP4_B32) return KVQ_ERR_UNSUPPORTED;   // attention over these modes is not built
     if (k->batch != v->batch || k->heads != v->heads || k->n_slots != v->n_slots || k->head_dim != v->head_dim)
         return KVQ_ERR_SHAPE;
     if (B != k->batch || Hq <= 0 || Hq % k->heads != 0) return KVQ_ERR_SHAPE;

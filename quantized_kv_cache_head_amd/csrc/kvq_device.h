@@ -95,6 +95,36 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float s) {
     return (uint32_t)b;
 }
 
+// FP8 E5M2 (bias 15, 2 mantissa bits), round to nearest even, |y| >= 57344
+// saturates to 0x7B (never inf), sign kept.
+__device__ __forceinline__ uint32_t enc_e5m2(float y) {
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a >= 0x47600000u) {                 // >= 57344
+        mag = 0x7Bu;
+    } else if (a < 0x38800000u) {           // < 2^-14: multiples of 2^-16
+        mag = (uint32_t)rintf(__uint_as_float(a) * 65536.0f);
+    } else {                                // keep 2 mantissa bits, RNE
+        const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
+        mag = (r >> 21) - (112u << 2);      // rebias exponent 127 -> 15
+    }
+    return sign | mag;
+}
+
+// Biased E8M0 exponent floor(log2 amax) - emax + 127 (OCP MX shared-scale
+// rule), clamped to [0, 254]; 0 for amax == 0.
+__device__ __forceinline__ uint32_t e8m0_floor(float amax, int emax) {
+    if (!(amax > 0.0f)) return 0u;
+    const uint32_t u = __float_as_uint(amax);
+    const int ef = (int)(u >> 23);
+    const int fl = ef == 0 ? (31 - (int)__clz(u & 0x7FFFFFu)) - 149 : ef - 127;
+    int b = fl - emax + 127;
+    b = b < 0 ? 0 : (b > 254 ? 254 : b);
+    return (uint32_t)b;
+}
+
 __device__ __forceinline__ float e8m0_value(uint32_t b) {
     return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }

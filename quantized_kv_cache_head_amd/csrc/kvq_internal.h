@@ -11,12 +11,14 @@
 
 namespace kvq {
 
-enum { QM_INT8_TH = 0, QM_UINT4_TH = 1, QM_FP8E4M3_B32 = 2, QM_MXFP4_B32 = 3 };
+enum { QM_INT8_TH = 0, QM_UINT4_TH = 1, QM_FP8E4M3_B32 = 2, QM_MXFP4_B32 = 3, QM_MXFP8_B32 = 4, QM_FP8E5M2_B32 = 5,
+       QM_INT8_B32 = 6 };
+enum { QF_MX_SCALE_OCP = 1 };   // quantize option (kvq.h KVQ_MX_SCALE_OCP)
 
 hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,
                                 int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
                                 int64_t ssb, int n_slots, uint8_t* codes, void* scales,
-                                int8_t* zps, int32_t* err, hipStream_t s);
+                                int8_t* zps, int flags, int32_t* err, hipStream_t s);
 
 hipError_t launch_quant_scatter_kv(int qmode, bool bf16, const void* xk, const void* xv, int B, int H, int T, int D,
                                    int64_t sb, int64_t sh, int64_t st, const int32_t* slots, int64_t ssb,

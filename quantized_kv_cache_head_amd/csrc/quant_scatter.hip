@@ -4,16 +4,19 @@
 // (Summary: int8 entries per token and head, affine asymmetric, float32 scale,
 // int8 zero point, written through slot indices) and PR 20351 (4-bit codes
 // packed two per byte along head_dim; static scatter along the position dim).
-// Block modes (FP8-E4M3 + fp32 scale, MX-FP4 + E8M0 scale, 32 elements per
-// block): IndexerQuantCache page, function description (scale = max|x_g| /
-// Q_MAX, q = round(x / scale)), parameter table and constraints (slot -1
-// skipped, valid slots in [0, num_slots)).
+// Block modes (32 elements per block): IndexerQuantCache page, function
+// description (scale = max|x_g| / Q_MAX, q = round(x / scale); the MX-FP8 and
+// MX-FP4 modes with an E8M0 scale, the Normal mode with an fp32 scale),
+// parameter table (FP8-E4M3FN, FP8-E5M2 and UINT8 caches; round_scale) and
+// constraints (slot -1 skipped, valid slots in [0, num_slots)).
 //
 // Affine rule (the pages name the scheme without a formula; this is the
 // reading the library implements): lo = min(0, min x), hi = max(0, max x),
 // scale = max((hi - lo) / (qmax - qmin), 2^-23), zp = clamp(qmin -
-// rne(lo / scale)), code = clamp(rne(x / scale) + zp).  MX-FP4 scale: the
-// smallest power of two >= amax / 6.
+// rne(lo / scale)), code = clamp(rne(x / scale) + zp).  Q_MAX: 448 (E4M3),
+// 57344 (E5M2), 127 (int8, symmetric codes in [-127, 127]), 6 (E2M1).  MX
+// scale: the smallest power of two >= amax / Q_MAX, or with the OCP option
+// 2^(floor(log2 amax) - emax) and saturation past Q_MAX.
 //
 // Work mapping: a row (one token of one head) is split over L lanes of a
 // wavefront, 8 elements per lane (one 16-byte bf16 load), so a wave covers
@@ -39,6 +42,7 @@ struct ScatterArgs {
     void* scales;
     int8_t* zps;
     int32_t* err;
+    int flags;             // QF_MX_SCALE_OCP for the MX modes
 };
 
 // Decode row index -> (b, h, t) and look up its slot.
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
     }
 }
 
-template <bool BF16, bool MX>
+template <bool BF16, int QM>
 __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, ScatterArgs a1) {
     const ScatterArgs a = blockIdx.y ? a1 : a0;
     const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -168,26 +172,45 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
     if (!valid) return;
 
     const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
-    if constexpr (!MX) {
-        const float scale = amax / 448.0f;
+    if constexpr (QM == QM_FP8E4M3_B32 || QM == QM_FP8E5M2_B32 || QM == QM_INT8_B32) {
+        // fp32 scale amax / Q_MAX; an all-zero block stores scale 0, codes 0
+        constexpr float QMAX = QM == QM_FP8E4M3_B32 ? 448.0f : QM == QM_FP8E5M2_B32 ? 57344.0f : 127.0f;
+        const float scale = amax / QMAX;
         uint32_t w0 = 0, w1 = 0;
         if (scale != 0.0f) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w0 |= enc_e4m3fn(v[i] / scale) << (8 * i);
-                w1 |= enc_e4m3fn(v[4 + i] / scale) << (8 * i);
+            for (int i = 0; i < 8; ++i) {
+                const float y = v[i] / scale;
+                uint32_t c;
+                if constexpr (QM == QM_FP8E4M3_B32) c = enc_e4m3fn(y);
+                else if constexpr (QM == QM_FP8E5M2_B32) c = enc_e5m2(y);
+                else c = (uint32_t)(int)fminf(fmaxf(rintf(y), -127.0f), 127.0f) & 0xFFu;
+                if (i < 4) w0 |= c << (8 * i);
+                else w1 |= c << (8 * (i - 4));
             }
         }
         *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
         if (qi == 0) reinterpret_cast<float*>(a.scales)[crow * gpr + g] = scale;
     } else {
-        const float s = amax / 6.0f;
-        const uint32_t e8 = e8m0_ceil(s);
+        // MX: E8M0 power-of-two scale X; x / X is exact
+        constexpr bool F4 = QM == QM_MXFP4_B32;
+        const uint32_t e8 = (a.flags & QF_MX_SCALE_OCP) ? e8m0_floor(amax, F4 ? 2 : 8)
+                                                         : e8m0_ceil(amax / (F4 ? 6.0f : 448.0f));
         const float X = e8m0_value(e8);
-        uint32_t w = 0;
+        if constexpr (F4) {
+            uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] / X) << (4 * i);
-        *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+            for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] / X) << (4 * i);
+            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+        } else {
+            uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w0 |= enc_e4m3fn(v[i] / X) << (8 * i);
+                w1 |= enc_e4m3fn(v[4 + i] / X) << (8 * i);
+            }
+            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+        }
         if (qi == 0) reinterpret_cast<uint8_t*>(a.scales)[crow * gpr + g] = (uint8_t)e8;
     }
 }
@@ -223,21 +246,26 @@ static hipError_t launch_scatter_n(int qmode, bool bf16, const ScatterArgs& a, c
     if (qmode == QM_UINT4_TH) return bf16 ? dispatch_affine<true, true>(a, a1, n, s) : dispatch_affine<false, true>(a, a1, n, s);
     const int64_t lanes = (int64_t)a.B * a.H * a.T * (a.D / 8);
     const dim3 grid((unsigned)((lanes + 255) / 256), (unsigned)n);
-    if (qmode == QM_FP8E4M3_B32) {
-        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, false>), grid, dim3(256), 0, s, a, a1);
-        else hipLaunchKernelGGL((quant_scatter_block<false, false>), grid, dim3(256), 0, s, a, a1);
-    } else {
-        if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, true>), grid, dim3(256), 0, s, a, a1);
-        else hipLaunchKernelGGL((quant_scatter_block<false, true>), grid, dim3(256), 0, s, a, a1);
+#define KVQ_BLK(QQ)                                                                                     \
+    if (bf16) hipLaunchKernelGGL((quant_scatter_block<true, QQ>), grid, dim3(256), 0, s, a, a1);         \
+    else hipLaunchKernelGGL((quant_scatter_block<false, QQ>), grid, dim3(256), 0, s, a, a1);
+    switch (qmode) {
+    case QM_FP8E4M3_B32: KVQ_BLK(QM_FP8E4M3_B32) break;
+    case QM_MXFP4_B32: KVQ_BLK(QM_MXFP4_B32) break;
+    case QM_MXFP8_B32: KVQ_BLK(QM_MXFP8_B32) break;
+    case QM_FP8E5M2_B32: KVQ_BLK(QM_FP8E5M2_B32) break;
+    case QM_INT8_B32: KVQ_BLK(QM_INT8_B32) break;
+    default: return hipErrorInvalidValue;
     }
+#undef KVQ_BLK
     return hipGetLastError();
 }
 
 hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,
                                 int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
                                 int64_t ssb, int n_slots, uint8_t* codes, void* scales,
-                                int8_t* zps, int32_t* err, hipStream_t s) {
-    const ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err};
+                                int8_t* zps, int flags, int32_t* err, hipStream_t s) {
+    const ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err, flags};
     return launch_scatter_n(qmode, bf16, a, a, 1, s);
 }
 
@@ -245,8 +273,8 @@ hipError_t launch_quant_scatter_kv(int qmode, bool bf16, const void* xk, const v
                                    int64_t sb, int64_t sh, int64_t st, const int32_t* slots, int64_t ssb,
                                    int n_slots, uint8_t* kcodes, void* kscales, int8_t* kzps, uint8_t* vcodes,
                                    void* vscales, int8_t* vzps, int32_t* err, hipStream_t s) {
-    const ScatterArgs ak{xk, B, H, T, D, sb, sh, st, slots, ssb, n_slots, kcodes, kscales, kzps, err};
-    const ScatterArgs av{xv, B, H, T, D, sb, sh, st, slots, ssb, n_slots, vcodes, vscales, vzps, err};
+    const ScatterArgs ak{xk, B, H, T, D, sb, sh, st, slots, ssb, n_slots, kcodes, kscales, kzps, err, 0};
+    const ScatterArgs av{xv, B, H, T, D, sb, sh, st, slots, ssb, n_slots, vcodes, vscales, vzps, err, 0};
     return launch_scatter_n(qmode, bf16, ak, av, 2, s);
 }
 

@@ -18,7 +18,9 @@ def say(*a):
 
 def orc_mode(qmode):
     return {kvq.INT8_TH: oracle.INT8_TH, kvq.UINT4_TH: oracle.UINT4_TH,
-            kvq.FP8E4M3_B32: oracle.FP8E4M3_B32, kvq.MXFP4_B32: oracle.MXFP4_B32}[qmode]
+            kvq.FP8E4M3_B32: oracle.FP8E4M3_B32, kvq.MXFP4_B32: oracle.MXFP4_B32,
+            kvq.MXFP8_B32: oracle.MXFP8_B32, kvq.FP8E5M2_B32: oracle.FP8E5M2_B32,
+            kvq.INT8_B32: oracle.INT8_B32}[qmode]
 
 
 def new_pair(qmode, B, H, S, D):

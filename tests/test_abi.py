@@ -52,6 +52,9 @@ def test_cache_bytes(kvq):
     assert kvq.cache_bytes(kvq.UINT4_TH, 1, 16, 131072, 256) == (16 * 131072 * 128, 16 * 131072 * 4, 16 * 131072)
     assert kvq.cache_bytes(kvq.FP8E4M3_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
     assert kvq.cache_bytes(kvq.MXFP4_B32, 1, 1, 65536, 128) == (65536 * 64, 65536 * 4, 0)
+    assert kvq.cache_bytes(kvq.MXFP8_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4, 0)
+    assert kvq.cache_bytes(kvq.FP8E5M2_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
+    assert kvq.cache_bytes(kvq.INT8_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
     with pytest.raises(kvq.KvqError):
         kvq.cache_bytes(kvq.FP8E4M3_B32, 1, 1, 16, 48)        # D % 32 != 0
     with pytest.raises(kvq.KvqError):
@@ -84,6 +87,12 @@ def test_host_validation_errors(kvq):
     # affine cache without zero points
     cz, keep2 = _fake_cache(kvq, zps=False)
     assert L.kvq_quant_scatter(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(cz), None, s) == 1
+    # quantize options: unknown bits, and the MX scale option on a non-MX cache
+    cf8, keep7 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
+    cmx, keep8 = _fake_cache(kvq, qmode=kvq.MXFP8_B32, zps=False)
+    assert L.kvq_quant_scatter_flags(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(cf8), 1, None, s) == 4
+    assert L.kvq_quant_scatter_flags(None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(cmx), 2, None, s) == 4
+    assert L.kvq_quant_scatter_flags(None, 1, 1, 2, 0, 64, 0, 0, 64, None, 0, ctypes.byref(cmx), 1, None, s) == 0
     # K+V update: the two caches must agree in mode and sizes
     cv_other, keep5 = _fake_cache(kvq, S=32)
     assert L.kvq_quant_scatter_kv(None, None, 1, 1, 2, 4, 64, 0, 0, 64, None, 0, ctypes.byref(c),

@@ -11,7 +11,8 @@ from _gpu import DEV, assert_cache_equal, dev_input, new_pair, say
 
 pytestmark = pytest.mark.gpu
 
-MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32]
+MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+BLOCK = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
 
 
 def _inputs(rng, B, H, T, D, bf16):
@@ -61,12 +62,14 @@ def test_scatter_other_head_dims(qmode, D):
     assert_cache_equal(dc, hc, f"D {D}")
 
 
-@pytest.mark.parametrize("qmode", [kvq.FP8E4M3_B32, kvq.MXFP4_B32])
-def test_scatter_block_mode_extremes(qmode):
+@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + [(kvq.MXFP4_B32, True), (kvq.MXFP8_B32, True)])
+def test_scatter_block_mode_extremes(qmode, ocp):
     """Blocks at the edges of the encoders: exact ties, saturation, subnormal
-    results, power-of-two amax, all-zero blocks, E8M0 clamp."""
+    results, power-of-two amax, all-zero blocks, E8M0 clamp (both MX scale
+    rules)."""
     g = oracle
-    vals = [0.0, -0.0, 448.0, -448.0, 1.0, 0.5, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 6.0, 5.0, 0.25, 0.75]
+    vals = [0.0, -0.0, 448.0, -448.0, 1.0, 0.5, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10, 6.0, 5.0, 0.25, 0.75,
+            57344.0, 1.125, 1.375, 2.0 ** -16, 2.0 ** -17, 127.0, 2.5, -3.5, 500.0, 3.5]
     rows = []
     for scale in (1.0, 2.0 ** -20, 2.0 ** 20, 1.5, 3e-38, 1e30):
         r = np.zeros(128, np.float32)
@@ -77,11 +80,12 @@ def test_scatter_block_mode_extremes(qmode):
     x = wl.to_bf16_values(np.stack(rows)[None, None])
     T = x.shape[2]
     slots = np.arange(T, dtype=np.int32)[None]
-    say(f"scatter extremes qmode={qmode}")
+    say(f"scatter extremes qmode={qmode} ocp={ocp}")
     dc, hc = new_pair(qmode, 1, 1, T, 128)
-    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
+    fl = kvq.MX_SCALE_OCP if ocp else 0
+    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc, flags=fl)
     torch.cuda.synchronize()
-    g.quant_scatter(hc, x, slots)
+    g.quant_scatter(hc, x, slots, qflags=oracle.MX_SCALE_OCP if ocp else 0)
     assert_cache_equal(dc, hc, "extremes")
 
 
@@ -133,3 +137,21 @@ def test_scatter_kv_single_launch(qmode):
     assert_cache_equal(dk, hk, "kv scatter K")
     assert_cache_equal(dv, hv, "kv scatter V")
     assert int(err.item()) & 1
+
+
+@pytest.mark.parametrize("qmode", [kvq.MXFP4_B32, kvq.MXFP8_B32])
+@pytest.mark.parametrize("D", [64, 256])
+def test_scatter_mx_ocp_scale_parity(qmode, D):
+    """The OCP floor rule for the E8M0 scale (quantize option), bit-exact
+    with the oracle on random and outlier-heavy vectors."""
+    rng = np.random.default_rng(700 + qmode + D)
+    B, H, T, S = 2, 3, 41, 128
+    x = _inputs(rng, B, H, T, D, True)
+    slots = np.stack([rng.choice(S, T, replace=False) for _ in range(B)]).astype(np.int32)
+    slots[1, 2] = -1
+    say(f"scatter OCP qmode={qmode} D={D}")
+    dc, hc = new_pair(qmode, B, H, S, D)
+    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc, flags=kvq.MX_SCALE_OCP)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots, qflags=oracle.MX_SCALE_OCP)
+    assert_cache_equal(dc, hc, f"OCP qmode {qmode} D {D}")

@@ -191,16 +191,19 @@ def test_long_prefill_4bit_sampled_rows():
         check_attention(got, ref, f"long prefill kv_len {end}")
 
 
-@pytest.mark.parametrize("qmode", [kvq.FP8E4M3_B32, kvq.MXFP4_B32])
-def test_block_scatter_full(qmode):
+@pytest.mark.parametrize("qmode,ocp", [(kvq.FP8E4M3_B32, False), (kvq.MXFP4_B32, False), (kvq.MXFP8_B32, False),
+                                       (kvq.FP8E5M2_B32, False), (kvq.INT8_B32, False), (kvq.MXFP4_B32, True),
+                                       (kvq.MXFP8_B32, True)])
+def test_block_scatter_full(qmode, ocp):
     """x [16384, 128] bf16 with 1% outliers x20 into a 65536-slot block cache,
     1638 slots skipped: every byte of the cache against the oracle."""
     w = wl.BLOCKSCATTER
-    say(f"block scatter full size, qmode {qmode}")
+    say(f"block scatter full size, qmode {qmode} ocp {ocp}")
     x, slots = wl.blockscatter_inputs(w)
     dc, hc = new_pair(qmode, 1, 1, w.n_slots, w.d)
-    kvq.quant_scatter(dev_input(x[None, None], True), torch.from_numpy(slots).to(DEV), dc)
-    oracle.quant_scatter(hc, x[None, None], slots, parallel=True)
+    kvq.quant_scatter(dev_input(x[None, None], True), torch.from_numpy(slots).to(DEV), dc,
+                      flags=kvq.MX_SCALE_OCP if ocp else 0)
+    oracle.quant_scatter(hc, x[None, None], slots, parallel=True, qflags=oracle.MX_SCALE_OCP if ocp else 0)
     torch.cuda.synchronize()
     assert_cache_equal(dc, hc, f"block scatter qmode {qmode}")
     # the skipped tokens' slots were never written (still the sentinel)
