@@ -170,7 +170,6 @@ kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_
     if ((q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) || (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16))
         return KVQ_ERR_DTYPE;
     if (k->qmode != v->qmode) return KVQ_ERR_DTYPE;
-    if (k->qmode > KVQ_MXFP4_B32) return KVQ_ERR_UNSUPPORTED;   // attention over these modes is not built
     if (k->batch != v->batch || k->heads != v->heads || k->n_slots != v->n_slots || k->head_dim != v->head_dim)
         return KVQ_ERR_SHAPE;
     if (B != k->batch || Hq <= 0 || Hq % k->heads != 0) return KVQ_ERR_SHAPE;

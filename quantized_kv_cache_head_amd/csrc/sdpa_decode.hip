@@ -31,10 +31,10 @@
 //  * Pass 2 (p . v): a V row is split over CV lanes of 16 bytes; fp32 FMA of
 //    p * scale_v on v_cvt_f32_ubyte of the codes; the first PDV steps of the
 //    V ring are issued before the middle pass so the V stream overlaps it.
-//  * Block caches (FP8-E4M3 with an fp32 scale, MX-FP4 with an E8M0 scale,
-//    per 32 elements: the IndexerQuantCache operator page's per-block
-//    format): codes become exact fp16 / fp32 values through the gfx950
-//    conversion instructions; a 16-byte chunk of a lane lies inside one
+//  * Block caches (per 32 elements: FP8-E4M3 or FP8-E5M2 or int8 with an fp32
+//    scale, MX-FP8 / MX-FP4 with an E8M0 scale; the IndexerQuantCache operator
+//    page's per-block formats): codes become exact fp16 / fp32 values (the
+//    gfx950 conversion instructions, or the exponent trick for int8); a 16-byte chunk of a lane lies inside one
 //    block, so the block scale travels in the load ring with the codes and
 //    multiplies the chunk's partial q . k (pass 1) or p (pass 2).  Rows carry
 //    no scale or zero point of their own.
@@ -142,53 +142,69 @@ __device__ __forceinline__ void codes_to_f32(const uint4 w, float out[U4 ? 32 : 
     }
 }
 
-// Block-quantized codes (FP8-E4M3FN, or FP4-E2M1 two per byte with element
-// 2i in the low nibble of byte i) to exact fp16 pairs / fp32 values in
-// element order, with the gfx950 conversion instructions at scale 1: every
-// E4M3 and E2M1 value is exactly representable in fp16.  The per-block scale
-// is applied afterwards, in fp32.
-template <bool F4>
-__device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[F4 ? 16 : 8]) {
+// Block-quantized codes to exact fp16 pairs / fp32 values in element order:
+// FP8-E4M3FN (MX-FP8 too) and FP8-E5M2 through the gfx950 conversion
+// instructions at scale 1 (every E4M3 and E5M2 value is an fp16 value),
+// FP4-E2M1 two per byte (element 2i in the low nibble of byte i) the same way,
+// int8 as (code + 128) placed under the fp16 exponent of 1024 minus 1152.  The
+// per-block scale is applied afterwards, in fp32.
+template <int QM>
+__device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[QM == QM_MXFP4_B32 ? 16 : 8]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if constexpr (!F4) {
-            out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, false));
-            out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, true));
-        } else {
+        if constexpr (QM == QM_MXFP4_B32) {
             out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 0));
             out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 1));
             out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 2));
             out[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 3));
+        } else if constexpr (QM == QM_FP8E5M2_B32) {
+            out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(ws[i], 1.0f, false));
+            out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(ws[i], 1.0f, true));
+        } else if constexpr (QM == QM_INT8_B32) {
+            const uint32_t u = ws[i] ^ 0x80808080u;
+            out[2 * i] = h2_sub(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u), 0x64806480u);
+            out[2 * i + 1] = h2_sub(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u), 0x64806480u);
+        } else {
+            out[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, false));
+            out[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ws[i], 1.0f, true));
         }
     }
 }
 
-template <bool F4>
-__device__ __forceinline__ void blk_to_f32(const uint4 w, float out[F4 ? 32 : 16]) {
+template <int QM>
+__device__ __forceinline__ void blk_to_f32(const uint4 w, float out[QM == QM_MXFP4_B32 ? 32 : 16]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if constexpr (!F4) {
-            const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], false);
-            const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], true);
-            out[4 * i] = lo[0]; out[4 * i + 1] = lo[1]; out[4 * i + 2] = hi[0]; out[4 * i + 3] = hi[1];
-        } else {
+        if constexpr (QM == QM_MXFP4_B32) {
             const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 0);
             const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 1);
             const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 2);
             const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 3);
             out[8 * i + 0] = v0[0]; out[8 * i + 1] = v0[1]; out[8 * i + 2] = v1[0]; out[8 * i + 3] = v1[1];
             out[8 * i + 4] = v2[0]; out[8 * i + 5] = v2[1]; out[8 * i + 6] = v3[0]; out[8 * i + 7] = v3[1];
+        } else if constexpr (QM == QM_INT8_B32) {
+            const uint32_t u = ws[i] ^ 0x80808080u;          // code + 128
+            out[4 * i] = (float)(u & 0xFFu) - 128.0f;
+            out[4 * i + 1] = (float)((u >> 8) & 0xFFu) - 128.0f;
+            out[4 * i + 2] = (float)((u >> 16) & 0xFFu) - 128.0f;
+            out[4 * i + 3] = (float)(u >> 24) - 128.0f;
+        } else {
+            const auto lo = QM == QM_FP8E5M2_B32 ? __builtin_amdgcn_cvt_pk_f32_bf8(ws[i], false)
+                                                 : __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], false);
+            const auto hi = QM == QM_FP8E5M2_B32 ? __builtin_amdgcn_cvt_pk_f32_bf8(ws[i], true)
+                                                 : __builtin_amdgcn_cvt_pk_f32_fp8(ws[i], true);
+            out[4 * i] = lo[0]; out[4 * i + 1] = lo[1]; out[4 * i + 2] = hi[0]; out[4 * i + 3] = hi[1];
         }
     }
 }
 
 // A block scale as loaded (fp32 bits, or an E8M0 byte) to its fp32 value;
 // E8M0 b is 2^(b - 127), b = 0 being the subnormal 2^-127.
-template <bool F4>
+template <bool E8M0>
 __device__ __forceinline__ float blk_scale(uint32_t raw) {
-    if constexpr (F4) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
+    if constexpr (E8M0) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
     else return __uint_as_float(raw);
 }
 
@@ -329,11 +345,11 @@ __device__ __forceinline__ uint4 load16(gptr<uint8_t> base, uint32_t off) {
 
 template <int D, int QM, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
-    constexpr bool BLK = QM == QM_FP8E4M3_B32 || QM == QM_MXFP4_B32;   // per-32 block scales, no zero point
+    constexpr bool BLK = QM >= QM_FP8E4M3_B32;      // per-32 block scales, no zero point
     constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
-    constexpr bool F4 = QM == QM_MXFP4_B32;
+    constexpr bool SC8 = QM == QM_MXFP4_B32 || QM == QM_MXFP8_B32;     // E8M0 block scales
     constexpr int SPR = D / 32;                      // block scales per row
-    constexpr int SCB = F4 ? 1 : 4;                  // bytes per block scale
+    constexpr int SCB = SC8 ? 1 : 4;                 // bytes per block scale
     constexpr DecGeom GM = dec_geom(D, U4, G);
     constexpr int ROWB = GM.rowb;
     constexpr int EPB = U4 ? 2 : 1;                  // elements per code byte
@@ -480,7 +496,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
             kbuf[u][c] = load16(kbase, j * ROWB + (uint32_t)ck * KB + 16 * c);
             if constexpr (BLK) {
                 const uint32_t gi = j * SPR + (uint32_t)((ck * KB + 16 * c) * EPB) / 32;
-                ksr[u][c] = F4 ? (uint32_t)kscb[gi] : *(gptr<uint32_t>)(kscb + gi * SCB);
+                ksr[u][c] = SC8 ? (uint32_t)kscb[gi] : *(gptr<uint32_t>)(kscb + gi * SCB);
             }
         }
     };
@@ -550,8 +566,8 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         if constexpr (BLK) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                blk_to_h2<F4>(kbuf[u][c], kh + c * PPC);
-                kscale[c] = blk_scale<F4>(ksr[u][c]);
+                blk_to_h2<QM>(kbuf[u][c], kh + c * PPC);
+                kscale[c] = blk_scale<SC8>(ksr[u][c]);
             }
         } else {
             const uint32_t zo = s_kzo[min(i, i_last)];
@@ -613,7 +629,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         vbuf[u] = load16(vbase, j * ROWB + (uint32_t)cv * 16);
         if constexpr (BLK) {
             const uint32_t gi = j * SPR + (uint32_t)(cv * 16 * EPB) / 32;
-            vsr[u] = F4 ? (uint32_t)vscb[gi] : *(gptr<uint32_t>)(vscb + gi * SCB);
+            vsr[u] = SC8 ? (uint32_t)vscb[gi] : *(gptr<uint32_t>)(vscb + gi * SCB);
         }
     };
 #pragma unroll
@@ -727,8 +743,8 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         float vf[EV];
         float live_sc = 1.0f;
         if constexpr (BLK) {
-            blk_to_f32<F4>(vbuf[u], vf);
-            live_sc = blk_scale<F4>(vsr[u]);
+            blk_to_f32<QM>(vbuf[u], vf);
+            live_sc = blk_scale<SC8>(vsr[u]);
         } else {
             codes_to_f32<U4>(vbuf[u], vf);
         }
@@ -856,6 +872,9 @@ static const void* split_kernel_for(int D, int qm, int G, bool qbf16) {
     case QM_INT8_TH: { KVQ_SK(DD, QM_INT8_TH) }              \
     case QM_UINT4_TH: { KVQ_SK(DD, QM_UINT4_TH) }            \
     case QM_FP8E4M3_B32: { KVQ_SK(DD, QM_FP8E4M3_B32) }      \
+    case QM_MXFP8_B32: { KVQ_SK(DD, QM_MXFP8_B32) }          \
+    case QM_FP8E5M2_B32: { KVQ_SK(DD, QM_FP8E5M2_B32) }      \
+    case QM_INT8_B32: { KVQ_SK(DD, QM_INT8_B32) }            \
     default: { KVQ_SK(DD, QM_MXFP4_B32) }                    \
     }
     if (D == 64) { KVQ_SKD(64) }
@@ -872,9 +891,9 @@ static const void* split_kernel_for(int D, int qm, int G, bool qbf16) {
 static int resident_workgroups(int D, int qm, int G, bool qbf16) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    const int key = ((D == 64 ? 0 : D == 128 ? 1 : 2) * 4 + (qm & 3)) * 8 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3) * 2 +
+    const int key = ((D == 64 ? 0 : D == 128 ? 1 : 2) * 8 + (qm & 7)) * 8 + (G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3) * 2 +
                     (qbf16 ? 1 : 0);
-    static int cache[64][96];                         // 0 = not known yet; benign races
+    static int cache[64][192];                        // 0 = not known yet; benign races
     int v = cache[dev][key];
     if (v > 0) return v;
     hipFuncAttributes fa;
@@ -944,6 +963,9 @@ static hipError_t dispatch_m(const DecodeArgs& a, int qmode, bool qbf16, int G, 
     case QM_UINT4_TH: return dispatch_q<D, QM_UINT4_TH>(a, qbf16, G, nsplit, s);
     case QM_FP8E4M3_B32: return dispatch_q<D, QM_FP8E4M3_B32>(a, qbf16, G, nsplit, s);
     case QM_MXFP4_B32: return dispatch_q<D, QM_MXFP4_B32>(a, qbf16, G, nsplit, s);
+    case QM_MXFP8_B32: return dispatch_q<D, QM_MXFP8_B32>(a, qbf16, G, nsplit, s);
+    case QM_FP8E5M2_B32: return dispatch_q<D, QM_FP8E5M2_B32>(a, qbf16, G, nsplit, s);
+    case QM_INT8_B32: return dispatch_q<D, QM_INT8_B32>(a, qbf16, G, nsplit, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -31,9 +31,10 @@
 //    one barrier per tile.
 //  * Workgroups of one KV head are placed on the same XCD so its K/V stream
 //    is shared through that XCD's L2.
-//  * Block caches (FP8-E4M3 / MX-FP4 with a scale per 32 elements, the
-//    IndexerQuantCache operator page's format): the codes become exact fp16
-//    through the gfx950 conversions.  One QK k-step of 32 d is exactly one
+//  * Block caches (a scale per 32 elements: FP8-E4M3, FP8-E5M2 or int8 with
+//    an fp32 scale, MX-FP8 / MX-FP4 with an E8M0 scale; the IndexerQuantCache
+//    operator page's formats): the codes become exact fp16 through the gfx950
+//    conversions (int8: the exponent trick).  One QK k-step of 32 d is exactly one
 //    scale block, so each block's partial S^T is scaled per key in fp32 and
 //    summed; V^T rows stay in d order so a 16-row output block lies in one
 //    scale block, and P enters that block's PV product scaled by the keys'
@@ -130,28 +131,44 @@ __device__ __forceinline__ int pf_vsw(int row) { return (row >> 1) & 3; }
 // rows per thread, so the swizzle follows the row's group of 8.
 __device__ __forceinline__ int pf_vswb(int row) { return (row >> 3) & 3; }
 
-// FP8-E4M3 (4 per dword) or FP4-E2M1 (8 per dword, element 2i in the low
-// nibble of byte i) codes to exact fp16 pairs in element order (gfx950
-// conversions at scale 1).
-template <bool F4>
+// One dword of block codes to exact fp16 pairs in element order: FP8-E4M3
+// (MX-FP8 too) and FP8-E5M2, 4 per dword, and FP4-E2M1, 8 per dword (element
+// 2i in the low nibble of byte i), through the gfx950 conversions at scale 1;
+// int8, 4 per dword, as (code + 128) under the fp16 exponent of 1024 minus
+// 1152.
+template <int QM>
 __device__ __forceinline__ void blk_dword(uint32_t w, uint32_t* out) {
-    if constexpr (!F4) {
-        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
-        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
-    } else {
+    if constexpr (QM == QM_MXFP4_B32) {
         out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
         out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
         out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
         out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
+    } else if constexpr (QM == QM_FP8E5M2_B32) {
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true));
+    } else if constexpr (QM == QM_INT8_B32) {
+        dq_dword_i8(w, 0x64806480u, out);
+    } else {
+        out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+        out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
     }
 }
 
 template <int D, int QM, int QL, int PL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sdpa_prefill_mfma(PrefillArgs a) {
-    constexpr bool BLK = QM == QM_FP8E4M3_B32 || QM == QM_MXFP4_B32;   // per-32 block scales
+    constexpr bool BLK = QM >= QM_FP8E4M3_B32;      // per-32 block scales
     constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
     constexpr bool F4 = QM == QM_MXFP4_B32;
+    constexpr bool SC8 = QM == QM_MXFP4_B32 || QM == QM_MXFP8_B32;     // E8M0 block scales
+    // Block V scales are about amax / Q_MAX, so P * scale_v would drop into the
+    // fp16 subnormals for formats with a large Q_MAX (E5M2: 57344) and lose
+    // its digits against codes that large.  The staged V scales carry
+    // 2^VF = 2^(floor(log2 Q_MAX) - 4), removed exactly from the output.
+    constexpr int VF = QM == QM_FP8E5M2_B32 ? 11
+                     : (QM == QM_FP8E4M3_B32 || QM == QM_MXFP8_B32) ? 4
+                     : QM == QM_INT8_B32 ? 2 : 0;
+    constexpr float VSC = (float)(1 << VF);
     constexpr bool PERM = QM == QM_UINT4_TH;         // affine 4-bit: U4_ORDER element order
     constexpr int NG = D / 32;                       // scale blocks per row (= QK k-steps)
     constexpr int BN = PF_BN;
@@ -310,7 +327,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             if (tid < NG * BN) {                      // thread -> (group tid / BN, key tid % BN)
                 const int j = min(tt * BN + tid % BN, kv_len - 1);
                 const int64_t gi = (plane + j) * NG + tid / BN;
-                if constexpr (F4) {
+                if constexpr (SC8) {
                     bk_r = reinterpret_cast<const uint8_t*>(a.ks)[gi];
                     bv_r = reinterpret_cast<const uint8_t*>(a.vs)[gi];
                 } else {
@@ -327,7 +344,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
     };
     auto blk_scale = [](uint32_t raw) {              // E8M0 b = 2^(b - 127), b = 0 the subnormal 2^-127
-        if constexpr (F4) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
+        if constexpr (SC8) return __uint_as_float(raw ? raw << 23 : 0x00400000u);
         else return __uint_as_float(raw);
     };
     auto store_meta = [&](int buf) {
@@ -362,7 +379,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             uint32_t hv[NPR];
 #pragma unroll
             for (int i = 0; i < RB / 4; ++i) {
-                if constexpr (BLK) blk_dword<F4>(w[i], hv + (F4 ? 4 : 2) * i);
+                if constexpr (BLK) blk_dword<QM>(w[i], hv + (F4 ? 4 : 2) * i);
                 else if constexpr (U4) dq_dword_u4p(w[i], off, hv + 4 * i);
                 else dq_dword_i8(w[i], off, hv + 2 * i);
             }
@@ -378,7 +395,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 if (tid < NG * BN) {
                     const bool in = tt * BN + tid % BN < kv_len;
                     bkt[tid] = in ? bks_lds[mbuf][tid] : 0.0f;
-                    bvt[tid] = in ? bvs_lds[mbuf][tid] : 0.0f;
+                    bvt[tid] = in ? bvs_lds[mbuf][tid] * VSC : 0.0f;
                 }
                 if (tid < BN) ct[tid] = tt * BN + tid < kv_len ? rs : 0.0f;
             } else if (tid < BN) {
@@ -400,11 +417,11 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                     const uint8_t* vs = rv + k * ROWB + (U4 ? dg * 4 : dg * 8);
                     if constexpr (BLK) {
                         if constexpr (F4) {
-                            blk_dword<true>(*reinterpret_cast<const uint32_t*>(vs), pr[e]);
+                            blk_dword<QM>(*reinterpret_cast<const uint32_t*>(vs), pr[e]);
                         } else {
                             const uint2 w2 = *reinterpret_cast<const uint2*>(vs);
-                            blk_dword<false>(w2.x, pr[e]);
-                            blk_dword<false>(w2.y, pr[e] + 2);
+                            blk_dword<QM>(w2.x, pr[e]);
+                            blk_dword<QM>(w2.y, pr[e] + 2);
                         }
                     } else if constexpr (U4) {
                         dq_dword_u4p(*reinterpret_cast<const uint32_t*>(vs), offv, pr[e]);
@@ -620,7 +637,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         l_run = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
     }
     if (!q_live) return;
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+    const float inv = l_run > 0.0f ? (1.0f / l_run) * (1.0f / VSC) : 0.0f;
     const int64_t obase = (((int64_t)b * a.Hq + q_head) * a.Lq + q_row) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -661,6 +678,9 @@ static hipError_t dispatch_pm(const PrefillArgs& a, int qmode, bool q_bf16, hipS
     case QM_UINT4_TH: return dispatch_pf<D, QM_UINT4_TH>(a, q_bf16, s);
     case QM_FP8E4M3_B32: return dispatch_pf<D, QM_FP8E4M3_B32>(a, q_bf16, s);
     case QM_MXFP4_B32: return dispatch_pf<D, QM_MXFP4_B32>(a, q_bf16, s);
+    case QM_MXFP8_B32: return dispatch_pf<D, QM_MXFP8_B32>(a, q_bf16, s);
+    case QM_FP8E5M2_B32: return dispatch_pf<D, QM_FP8E5M2_B32>(a, q_bf16, s);
+    case QM_INT8_B32: return dispatch_pf<D, QM_INT8_B32>(a, q_bf16, s);
     default: return hipErrorNotSupported;
     }
 }

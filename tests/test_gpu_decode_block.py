@@ -15,7 +15,7 @@ from test_gpu_decode import fill_caches, run_decode
 
 pytestmark = pytest.mark.gpu
 
-BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32]
+BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
 
 
 @pytest.mark.parametrize("qmode", BLOCK_MODES)
@@ -96,29 +96,35 @@ def test_block_decode_llama_shape(qmode):
 @pytest.mark.parametrize("qmode", BLOCK_MODES)
 def test_block_decode_every_code(qmode):
     """With kv_len = 1 the softmax weight is exactly 1, so the fp32 output is
-    the dequantized V row itself: every FP8 code (the two NaN codes, which no
-    encoder emits, replaced by 0x00) and every FP4 code at scale 1 must come
-    out exactly as the oracle's decoders give them."""
+    the dequantized V row itself: every code of the format at scale 1 must
+    come out exactly as the oracle's decoders give it.  Codes no encoder
+    emits and that decode to inf / NaN (E4M3 0x7F / 0xFF, E5M2 exponent 31)
+    are replaced by 0x00."""
     B, Hkv, G, S, D = 2, 1, 1, 4, 128
     say(f"block decode every code qmode={qmode}")
     K = kvq.Cache.empty(qmode, B, Hkv, S, D)
     V = kvq.Cache.empty(qmode, B, Hkv, S, D)
-    if qmode == kvq.FP8E4M3_B32:
-        codes = np.arange(256, dtype=np.uint8).reshape(B, D)
-        codes[codes == 0x7F] = 0
-        codes[codes == 0xFF] = 0
-        ref = np.array([[oracle.e4m3fn_decode(int(c)) for c in row] for row in codes])
-        one = np.ones((B, Hkv, S, D // 32), np.float32)
-        for c in (K, V):
-            c.scales.copy_(torch.from_numpy(one))
-    else:
+    if qmode == kvq.MXFP4_B32:
         nib = (np.arange(B * D) % 16).astype(np.uint8)
         nib = np.random.default_rng(5).permutation(nib).reshape(B, D)
         codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
         ref = np.array([[oracle.e2m1_decode(int(c)) for c in row] for row in nib])
-        for c in (K, V):
-            c.scales.fill_(127)                       # E8M0 2^0
+    else:
+        codes = np.arange(256, dtype=np.uint8).reshape(B, D)
+        if qmode in (kvq.FP8E4M3_B32, kvq.MXFP8_B32):
+            codes[(codes & 0x7F) == 0x7F] = 0
+            dec = oracle.e4m3fn_decode
+        elif qmode == kvq.FP8E5M2_B32:
+            codes[(codes & 0x7C) == 0x7C] = 0
+            dec = oracle.e5m2_decode
+        else:
+            dec = lambda c: float(np.int8(np.uint8(c)))
+        ref = np.array([[dec(int(c)) for c in row] for row in codes])
     for c in (K, V):
+        if c.scales.dtype == torch.uint8:
+            c.scales.fill_(127)                       # E8M0 2^0
+        else:
+            c.scales.fill_(1.0)
         c.codes.zero_()
         c.codes[:, 0, 0, :] = torch.from_numpy(codes).to(DEV)
     q = torch.zeros((B, Hkv * G, 1, D), dtype=torch.bfloat16, device=DEV)
