@@ -235,12 +235,14 @@ def leg_block_scatter():
     slots = torch.from_numpy(slots_np).to(DEV)
     res = {}
     valid = int((slots_np >= 0).sum())
-    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
+    for name, mode, fl in (("fp8_e4m3", kvq.FP8E4M3_B32, 0), ("mxfp4", kvq.MXFP4_B32, 0),
+                           ("mxfp8", kvq.MXFP8_B32, 0), ("fp8_e5m2", kvq.FP8E5M2_B32, 0), ("int8", kvq.INT8_B32, 0),
+                           ("mxfp4_ocp_scale", kvq.MXFP4_B32, kvq.MX_SCALE_OCP)):
         caches = [kvq.Cache.empty(mode, 1, 1, w.n_slots, w.d).sentinel_fill() for _ in range(8)]
         it = iter(range(10 ** 9))
-        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8]), iters=10, inner=8)
-        rb = w.d if mode == kvq.FP8E4M3_B32 else w.d // 2
-        sb = (w.d // 32) * (4 if mode == kvq.FP8E4M3_B32 else 1)
+        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8], flags=fl), iters=10, inner=8)
+        rb = w.d // 2 if mode == kvq.MXFP4_B32 else w.d
+        sb = (w.d // 32) * (1 if mode in kvq.E8M0_MODES else 4)
         nbytes = w.bs * 4 + valid * (w.d * 2 + rb + sb)
         res[name] = {"us": round(ms * 1e3, 3), "mtok_s": round(w.bs / ms / 1e3, 1),
                      "gbs": round(nbytes / ms / 1e6, 1)}
@@ -331,15 +333,16 @@ def leg_long_prefill():
 
 
 def leg_block_attention():
-    """Attention over block-quantized caches (FP8-E4M3 + fp32 scale, MX-FP4 +
-    E8M0 scale, per 32 elements): decode on the Llama-shaped layer (4 cache
-    replicas rotated, so bytes come from HBM) and the 2048-row chunked
-    prefill of the long-prefill shape at kv_len 65536."""
+    """Attention over block-quantized caches (a scale per 32 elements): decode
+    on the Llama-shaped layer for each block format (4 cache replicas rotated,
+    so bytes come from HBM) and the 2048-row chunked prefill of the
+    long-prefill shape at kv_len 65536 for FP8-E4M3 and MX-FP4."""
     res = {}
     gen = torch.Generator(device=DEV)
     gen.manual_seed(1005)
     w = wl.LLAMA8B
-    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32)):
+    for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32), ("mxfp8", kvq.MXFP8_B32),
+                       ("fp8_e5m2", kvq.FP8E5M2_B32), ("int8", kvq.INT8_B32)):
         reps = []
         for _ in range(4):
             K = kvq.Cache.empty(mode, w.B, w.Hkv, w.S, w.D)
@@ -359,8 +362,8 @@ def leg_block_attention():
             K, V = reps[next(it) % 4]
             kvq.sdpa_decode(q, K, V, kv_len=kvl, out=out, workspace=ws)
         ms = time_ms(dec, iters=10, inner=8)
-        rb = w.D if mode == kvq.FP8E4M3_B32 else w.D // 2
-        sb = (w.D // 32) * (4 if mode == kvq.FP8E4M3_B32 else 1)
+        rb = w.D // 2 if mode == kvq.MXFP4_B32 else w.D
+        sb = (w.D // 32) * (1 if mode in kvq.E8M0_MODES else 4)
         nbytes = 2 * w.B * w.Hkv * w.kv_len * (rb + sb) + 2 * w.B * w.Hq * w.D * 2
         res[f"decode_llama8b_{name}"] = {"us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
                                          "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
