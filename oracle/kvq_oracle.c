@@ -46,11 +46,11 @@
  *   R11 mask: slot visible iff cp>=0, cp<=qp and (cp<sink or qp-cp<window).
  *   R13 a query row with no visible key outputs 0.
  *   R14 GQA: query head h reads KV head h / (Hq/Hkv).
- *   R19 Q_MAX = 57344 (E5M2, largest finite), 127 (INT8: symmetric codes in
+ *   R22 Q_MAX = 57344 (E5M2, largest finite), 127 (INT8: symmetric codes in
  *       [-127, 127], two's complement in the uint8 cache).
- *   R20 MX-FP8 (quant_mode 0) with round_scale = true: the E8M0 scale is the
+ *   R23 MX-FP8 (quant_mode 0) with round_scale = true: the E8M0 scale is the
  *       smallest power of two >= amax / 448 (the same rounding as R9).
- *   R22 round_scale = false, and the OCP variant of MX-FP4: the scale is
+ *   R24 round_scale = false, and the OCP variant of MX-FP4: the scale is
  *       2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 2 (E2M1), clamped to
  *       the E8M0 range; elements beyond Q_MAX then saturate (R8).
  *
@@ -73,7 +73,7 @@
 #define ORC_FP8E5M2_B32 5   /* E5M2 codes, fp32 scale per 32 ([IQC] Normal mode, E5M2 cache) */
 #define ORC_INT8_B32 6      /* int8 codes in a uint8 cache, fp32 scale per 32 ([IQC] Normal, INT8) */
 
-/* Quantize option: the MX scale by the OCP floor rule (R22) instead of the
+/* Quantize option: the MX scale by the OCP floor rule (R24) instead of the
  * smallest power of two >= amax / Q_MAX (R9). */
 #define ORC_MX_SCALE_OCP 1
 
@@ -182,7 +182,7 @@ uint8_t orc_e8m0_ceil(float s) {
 
 float orc_e8m0_value(uint8_t b) { return ldexpf(1.0f, (int)b - 127); }
 
-/* E8M0 by the OCP floor rule (R22): biased exponent floor(log2 amax) - emax
+/* E8M0 by the OCP floor rule (R24): biased exponent floor(log2 amax) - emax
  * + 127, clamped to [0, 254]; amax == 0 gives 0.  floor(log2 amax) is read
  * exactly from the fp32 bits (normal or subnormal). */
 uint8_t orc_e8m0_floor(float amax, int emax) {
