@@ -155,6 +155,9 @@ kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int
  * else sink_size + (p - sink_size) mod window.  slot_mapping_out: int32 [T].
  * cache_positions: int32 [sink_size + window], in/out, -1 = empty; receives
  * cache_positions[slot] = p (the latest position wins when a chunk wraps).
+ * A call with more tokens than the window writes them as if one after
+ * another: a token whose slot a later token of the same call takes again
+ * gets slot -1 (not written), so the scatter never sees a slot twice.
  * start_pos is a device int32 scalar; a negative value writes slot -1 for
  * every token and sets KVQ_FLAG_SLOT_RANGE.  sink_size >= 0, window >= 1. */
 kvq_status kvq_positions_with_sink(const int32_t* start_pos, int T, int sink_size, int window,
@@ -215,6 +218,18 @@ kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
                            void* workspace, size_t workspace_bytes,
                            int32_t* err_flags, void* stream);
 
+/* kvq_sdpa_decode with one filled length per batch row: kv_lens is a device
+ * int32 array [B] (batch row b attends slots [0, kv_lens[b])), each clamped to
+ * [1, n_slots] with KVQ_FLAG_KVLEN.  Otherwise as kvq_sdpa_decode; the same
+ * workspace size.  KVQ_ERR_NULL when kv_lens is NULL.  ([PR20351] kv_len
+ * bound, applied per sequence of the batch.) */
+kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int Hq,
+                                  const kvq_cache* k, const kvq_cache* v,
+                                  const int32_t* kv_lens, const float* mask, int64_t mask_stride_b,
+                                  float sm_scale, void* out, int out_dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t* err_flags, void* stream);
+
 /* Chunked-prefill attention over quantized K/V caches ([PR20351]): the Lq
  * query rows sit at positions [kv_len - Lq, kv_len); row r attends keys
  * j < kv_len, and when mask_is_causal only j <= kv_len - Lq + r.  The KV loop
@@ -231,6 +246,17 @@ kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq,
                             const int32_t* kv_len, const float* mask, int mask_is_causal,
                             unsigned flags, float sm_scale, void* out, int out_dtype,
                             int32_t* err_flags, void* stream);
+
+/* kvq_sdpa_prefill with one filled length per batch row: kv_lens is a device
+ * int32 array [B]; the Lq query rows of batch row b sit at positions
+ * [kv_lens[b] - Lq, kv_lens[b]), each value clamped to [Lq, n_slots] with
+ * KVQ_FLAG_KVLEN.  Otherwise as kvq_sdpa_prefill.  KVQ_ERR_NULL when kv_lens
+ * is NULL. */
+kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, int Lq,
+                                   const kvq_cache* k, const kvq_cache* v,
+                                   const int32_t* kv_lens, const float* mask, int mask_is_causal,
+                                   unsigned flags, float sm_scale, void* out, int out_dtype,
+                                   int32_t* err_flags, void* stream);
 
 #ifdef __cplusplus
 }

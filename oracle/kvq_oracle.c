@@ -50,6 +50,9 @@
  *       [-127, 127], two's complement in the uint8 cache).
  *   R23 MX-FP8 (quant_mode 0) with round_scale = true: the E8M0 scale is the
  *       smallest power of two >= amax / 448 (the same rounding as R9).
+ *   R25 A call with more tokens than the ring holds writes them one after
+ *       another: a token whose slot a later token of the call takes again is
+ *       not written (slot -1); cache_positions keeps the last position.
  *   R24 round_scale = false, and the OCP variant of MX-FP4: the scale is
  *       2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 2 (E2M1), clamped to
  *       the E8M0 range; elements beyond Q_MAX then saturate (R8).
@@ -468,6 +471,17 @@ int orc_positions_sink(int start_pos, int T, int sink, int window,
         slot_mapping[t] = slot;
         if (cache_positions) cache_positions[slot] = p;
     }
+    /* R25: tokens are written one after another, so a token whose slot a
+     * later token of the same call takes again leaves nothing behind; it gets
+     * slot -1 (found by a backward scan over the slots already claimed). */
+    int S = sink + window;
+    unsigned char* taken = (unsigned char*)calloc((size_t)S, 1);
+    for (int t = T - 1; t >= 0; --t) {
+        int slot = slot_mapping[t];
+        if (taken[slot]) slot_mapping[t] = -1;
+        else taken[slot] = 1;
+    }
+    free(taken);
     return 0;
 }
 

@@ -40,7 +40,8 @@ EXPORTS = (
     "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_quant_scatter_flags", "kvq_quant_scatter_kv",
     "kvq_positions_with_sink",
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
-    "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_prefill",
+    "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
+    "kvq_sdpa_prefill_varlen",
 )
 
 
@@ -93,6 +94,11 @@ def lib():
         L.kvq_sdpa_decode.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _SZ, _P, _P]
         L.kvq_sdpa_prefill.restype = _I
         L.kvq_sdpa_prefill.argtypes = [_P, _I, _I, _I, _I, _CP, _CP, _P, _P, _I, ctypes.c_uint, _F, _P, _I, _P, _P]
+        L.kvq_sdpa_decode_varlen.restype = _I
+        L.kvq_sdpa_decode_varlen.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _F, _P, _I, _P, _SZ, _P, _P]
+        L.kvq_sdpa_prefill_varlen.restype = _I
+        L.kvq_sdpa_prefill_varlen.argtypes = [_P, _I, _I, _I, _I, _CP, _CP, _P, _P, _I, ctypes.c_uint, _F, _P, _I,
+                                              _P, _P]
         _lib = L
     return _lib
 
@@ -308,6 +314,57 @@ def sdpa_prefill(q, k: Cache, v: Cache, kv_len=None, mask=None, causal=True, sm_
     kc, vc = k.struct(), v.struct()
     _check("kvq_sdpa_prefill", lib().kvq_sdpa_prefill(
         _ptr(q), _dtype_code(q), B, Hq, Lq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), _ptr(mask),
+        int(bool(causal)), NO_CAUSAL_SKIP if no_causal_skip else 0, float(sm_scale), _ptr(out),
+        _dtype_code(out), _ptr(err_flags), _stream(stream)))
+    return out
+
+
+def sdpa_decode_varlen(q, k: Cache, v: Cache, kv_lens, mask=None, sm_scale=None, out=None, out_dtype=None,
+                       workspace=None, err_flags=None, stream=None):
+    """kvq_sdpa_decode_varlen: as sdpa_decode with kv_lens int32 [B] on the device."""
+    _need_cuda(q, kv_lens, mask, out, workspace, err_flags)
+    B, Hq, Lq, D = q.shape
+    if Lq != 1 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 1, D]")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be contiguous int32 [B]")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, k.H, k.S, D, q.device)
+    msb = 0
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_contiguous():
+            raise ValueError("mask must be contiguous float32 [n_slots] or [B, n_slots]")
+        msb = 0 if mask.dim() == 1 or mask.shape[0] == 1 else mask.stride(0)
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_decode_varlen", lib().kvq_sdpa_decode_varlen(
+        _ptr(q), _dtype_code(q), B, Hq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_lens), _ptr(mask), msb,
+        float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(err_flags), _stream(stream)))
+    return out
+
+
+def sdpa_prefill_varlen(q, k: Cache, v: Cache, kv_lens, mask=None, causal=True, sm_scale=None, out=None,
+                        out_dtype=None, no_causal_skip=False, err_flags=None, stream=None):
+    """kvq_sdpa_prefill_varlen: as sdpa_prefill with kv_lens int32 [B] on the device."""
+    _need_cuda(q, kv_lens, mask, out, err_flags)
+    B, Hq, Lq, D = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be contiguous int32 [B]")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if mask is not None and (mask.dtype != torch.float32 or not mask.is_contiguous()):
+        raise ValueError("mask must be contiguous float32 [Lq, n_slots]")
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_prefill_varlen", lib().kvq_sdpa_prefill_varlen(
+        _ptr(q), _dtype_code(q), B, Hq, Lq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_lens), _ptr(mask),
         int(bool(causal)), NO_CAUSAL_SKIP if no_causal_skip else 0, float(sm_scale), _ptr(out),
         _dtype_code(out), _ptr(err_flags), _stream(stream)))
     return out

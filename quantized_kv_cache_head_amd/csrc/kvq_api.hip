@@ -200,12 +200,12 @@ KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slo
     return decode_ws_bytes(B, Hq, Hkv, decode_splits_any(B, Hq, Hkv, n_slots, D), D);
 }
 
-KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
-                                   const kvq_cache* v, const int32_t* kv_len, const float* mask,
-                                   int64_t mask_stride_b, int mask_is_causal, float sm_scale, void* out,
-                                   int out_dtype, void* workspace, size_t workspace_bytes, int32_t* err_flags,
-                                   void* stream) {
-    (void)mask_is_causal;   // at Lq = 1 the causal bound equals kv_len
+namespace {
+
+kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v,
+                            const int32_t* kv_len, int kv_len_sb, const float* mask, int64_t mask_stride_b,
+                            float sm_scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                            int32_t* err_flags, void* stream) {
     kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
@@ -229,6 +229,7 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
     L.vs = reinterpret_cast<const float*>(v->scales);
     L.vz = v->zps;
     L.kv_len = kv_len;
+    L.kv_len_sb = kv_len_sb;
     L.mask = mask;
     L.mask_sb = mask_stride_b;
     L.sm_scale = sm_scale;
@@ -241,10 +242,10 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
     return from_hip(kvq::launch_sdpa_decode(L, reinterpret_cast<hipStream_t>(stream)));
 }
 
-KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
-                                    const kvq_cache* v, const int32_t* kv_len, const float* mask,
-                                    int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
-                                    int32_t* err_flags, void* stream) {
+kvq_status sdpa_prefill_impl(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
+                             const kvq_cache* v, const int32_t* kv_len, int kv_len_sb, const float* mask,
+                             int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
+                             int32_t* err_flags, void* stream) {
     kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (Lq < 1 || Lq > k->n_slots) return KVQ_ERR_SHAPE;
@@ -266,6 +267,7 @@ KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, i
     L.vs = reinterpret_cast<const float*>(v->scales);
     L.vz = v->zps;
     L.kv_len = kv_len;
+    L.kv_len_sb = kv_len_sb;
     L.mask = mask;
     L.causal = mask_is_causal != 0;
     L.no_skip = (flags & KVQ_NO_CAUSAL_SKIP) != 0;
@@ -276,4 +278,43 @@ KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, i
     hipError_t e = kvq::launch_sdpa_prefill(L, reinterpret_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return KVQ_ERR_UNSUPPORTED;
     return from_hip(e);
+}
+
+}  // namespace
+
+KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
+                                   const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                   int64_t mask_stride_b, int mask_is_causal, float sm_scale, void* out,
+                                   int out_dtype, void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                   void* stream) {
+    (void)mask_is_causal;   // at Lq = 1 the causal bound equals kv_len
+    return sdpa_decode_impl(q, q_dtype, B, Hq, k, v, kv_len, 0, mask, mask_stride_b, sm_scale, out, out_dtype,
+                            workspace, workspace_bytes, err_flags, stream);
+}
+
+KVQ_API kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
+                                          const kvq_cache* v, const int32_t* kv_lens, const float* mask,
+                                          int64_t mask_stride_b, float sm_scale, void* out, int out_dtype,
+                                          void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                          void* stream) {
+    if (!kv_lens) return KVQ_ERR_NULL;
+    return sdpa_decode_impl(q, q_dtype, B, Hq, k, v, kv_lens, 1, mask, mask_stride_b, sm_scale, out, out_dtype,
+                            workspace, workspace_bytes, err_flags, stream);
+}
+
+KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
+                                    const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                    int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
+                                    int32_t* err_flags, void* stream) {
+    return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_len, 0, mask, mask_is_causal, flags, sm_scale, out,
+                             out_dtype, err_flags, stream);
+}
+
+KVQ_API kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
+                                           const kvq_cache* v, const int32_t* kv_lens, const float* mask,
+                                           int mask_is_causal, unsigned flags, float sm_scale, void* out,
+                                           int out_dtype, int32_t* err_flags, void* stream) {
+    if (!kv_lens) return KVQ_ERR_NULL;
+    return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_lens, 1, mask, mask_is_causal, flags, sm_scale, out,
+                             out_dtype, err_flags, stream);
 }

@@ -43,6 +43,7 @@ struct DecodeLaunch {
     const float* vs;
     const int8_t* vz;
     const int32_t* kv_len;
+    int kv_len_sb;          // 0: one kv_len for the batch; 1: kv_len[b]
     const float* mask;
     int64_t mask_sb;
     float sm_scale;
@@ -69,6 +70,7 @@ struct PrefillLaunch {
     const float* vs;
     const int8_t* vz;
     const int32_t* kv_len;
+    int kv_len_sb;          // 0: one kv_len for the batch; 1: kv_len[b]
     const float* mask;
     bool causal;
     bool no_skip;

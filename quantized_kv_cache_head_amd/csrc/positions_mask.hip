@@ -34,9 +34,12 @@ __global__ __launch_bounds__(256) void positions_sink_kernel(const int32_t* star
     int slot;
     if (p < sink) slot = (int)p;
     else slot = sink + (int)((p - sink) % window);
-    slot_out[t] = slot;
+    // a token whose slot a later token of the same call takes again is not
+    // written (slot -1): the cache then holds what writing the tokens one
+    // after another leaves, and one call never scatters to a slot twice
     const int64_t last = (int64_t)start + T - 1;
     const bool last_writer = p < sink || p + window > last;
+    slot_out[t] = last_writer ? slot : -1;
     if (cache_positions && last_writer) cache_positions[slot] = (int32_t)p;
 }
 

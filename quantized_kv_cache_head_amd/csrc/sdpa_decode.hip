@@ -62,6 +62,7 @@ struct DecodeArgs {
     const float* vs;
     const int8_t* vz;
     const int32_t* kv_len;
+    int kv_len_sb;         // 0: one kv_len for the batch; 1: one per batch row
     const float* mask;
     int64_t mask_sb;
     float sm_scale_log2;   // sm_scale * log2(e)
@@ -402,9 +403,9 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     }
 
     // ---- kv_len and this workgroup's slice --------------------------------
-    int kv_len = a.kv_len ? *a.kv_len : a.S;
+    int kv_len = a.kv_len ? a.kv_len[(int64_t)b * a.kv_len_sb] : a.S;
     if (kv_len < 1 || kv_len > a.S) {
-        if (a.err && split == 0 && g == 0 && b == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
+        if (a.err && split == 0 && g == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
         kv_len = kv_len < 1 ? 1 : a.S;
     }
     int chunk = (kv_len + nsplit - 1) / nsplit;
@@ -971,7 +972,7 @@ static hipError_t dispatch_m(const DecodeArgs& a, int qmode, bool qbf16, int G, 
 }
 
 hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s) {
-    DecodeArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len,
+    DecodeArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len, L.kv_len_sb,
                  L.mask, L.mask_sb, L.sm_scale * 1.4426950408889634f, L.part_o, L.part_ml, L.err};
     const int G = L.Hq / L.Hkv;
     hipError_t e;

@@ -57,6 +57,7 @@ struct PrefillArgs {
     const float* vs;
     const int8_t* vz;
     const int32_t* kv_len;
+    int kv_len_sb;         // 0: one kv_len for the batch; 1: one per batch row
     const float* mask;
     int causal, no_skip, out_bf16;
     float sm_scale_log2;
@@ -219,9 +220,9 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     const int b = bg / a.Hkv;
     const int r0 = qtile * QT;
 
-    int kv_len = a.kv_len ? *a.kv_len : a.S;
+    int kv_len = a.kv_len ? a.kv_len[(int64_t)b * a.kv_len_sb] : a.S;
     if (kv_len < a.Lq || kv_len > a.S) {
-        if (a.err && blockIdx.x == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
+        if (a.err && qtile == 0 && g == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
         kv_len = kv_len < a.Lq ? a.Lq : a.S;
     }
     const int row_last = min(r0 + QT, a.Lq) - 1;
@@ -686,7 +687,7 @@ static hipError_t dispatch_pm(const PrefillArgs& a, int qmode, bool q_bf16, hipS
 }
 
 hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s) {
-    PrefillArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.Lq, 0, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len,
+    PrefillArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.Lq, 0, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len, L.kv_len_sb,
                   L.mask, L.causal ? 1 : 0, L.no_skip ? 1 : 0, L.out_bf16 ? 1 : 0,
                   L.sm_scale * 1.4426950408889634f, L.out, L.err};
     const int G = L.Hq / L.Hkv;

@@ -119,6 +119,11 @@ def test_host_validation_errors(kvq):
     # K and V caches in different modes
     assert L.kvq_sdpa_decode(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(cb), None, None, 0, 0, 0.1, q, 1,
                              None, 0, None, s) == 3
+    # per-batch lengths are required by the varlen entry points
+    assert L.kvq_sdpa_decode_varlen(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0.1, q, 1,
+                                    None, 0, None, s) == 1
+    assert L.kvq_sdpa_prefill_varlen(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
+                                     None, s) == 1
     # Hq not a multiple of the KV heads
     assert L.kvq_sdpa_decode(q, 1, 1, 3, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
                              None, 0, None, s) == 2

@@ -30,34 +30,50 @@ def _simulate(sink, window, last_pos):
     return np.array(out, np.int32)
 
 
+def _sequential(slots):
+    """One call writes its tokens one after another: a token whose slot a
+    later token of the same call takes again is not written (-1)."""
+    out = slots.copy()
+    for t in range(len(slots)):
+        if np.any(slots[t + 1:] == slots[t]):
+            out[t] = -1
+    return out
+
+
 @pytest.mark.parametrize("sink,window", [(4, 2044), (0, 1024), (2, 3), (1, 1), (0, 7)])
 def test_positions_match_eviction_simulation(orc, sink, window):
     last = 6000
     want = _simulate(sink, window, last)
     cp = np.full(sink + window, -1, np.int32)
     got = orc.positions_sink(0, last + 1, sink, window, cp)
-    assert np.array_equal(got, want)
-    # chunked calls give the same slots and final positions
+    assert np.array_equal(got, _sequential(want))
+    # chunked calls: the same slots per chunk (minus in-chunk overwrites) and
+    # the same final positions
     cp2 = np.full(sink + window, -1, np.int32)
-    parts = []
     p = 0
-    for T in (1, 5, 17, 300, 1):
-        parts.append(orc.positions_sink(p, T, sink, window, cp2))
+    sizes = [1, 5, 17, 300, 1]
+    while p + sum(sizes) <= last:
+        sizes.append(min(999, last + 1 - p - sum(sizes)))
+    sizes = [s for s in sizes if s > 0]
+    for T in sizes:
+        assert np.array_equal(orc.positions_sink(p, T, sink, window, cp2), _sequential(want[p:p + T]))
         p += T
-    while p <= last:
-        T = min(999, last + 1 - p)
-        parts.append(orc.positions_sink(p, T, sink, window, cp2))
-        p += T
-    assert np.array_equal(np.concatenate(parts), want)
+    assert p == last + 1
     assert np.array_equal(cp, cp2)
+    # every slot's position is the simulator's last occupant
+    for s in range(sink + window):
+        held = np.nonzero(want == s)[0]
+        assert cp[s] == (held.max() if held.size else -1)
 
 
 def test_positions_hand_values(orc):
-    s = orc.positions_sink(0, 6001, 4, 2044)
-    assert s[0] == 0 and s[3] == 3 and s[4] == 4 and s[2047] == 2047
-    assert s[2048] == 4 and s[2049] == 5 and s[6000] == 4 + (5996 % 2044) == 1912
-    r = orc.positions_sink(0, 6001, 0, 1024)
-    assert r[1023] == 1023 and r[1024] == 0 and r[6000] == 880
+    one = lambda p, sink, window: int(orc.positions_sink(p, 1, sink, window)[0])
+    assert [one(p, 4, 2044) for p in (0, 3, 4, 2047, 2048, 2049)] == [0, 3, 4, 2047, 4, 5]
+    assert one(6000, 4, 2044) == 4 + (5996 % 2044) == 1912
+    assert [one(p, 0, 1024) for p in (1023, 1024, 6000)] == [1023, 0, 880]
+    # one call longer than the window: the early tokens of a reused slot are dropped
+    s = orc.positions_sink(0, 10, 2, 3)
+    assert list(s) == [0, 1, -1, -1, -1, -1, -1, 4, 2, 3]     # slots of 7, 8, 9: 2 + (p - 2) % 3
 
 
 def test_positions_full_rejects_past_capacity(orc):
