@@ -403,12 +403,14 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
+    ap.add_argument("--leg", choices=["block_scatter", "sink_ring", "long_prefill", "block_attention"],
+                    help="run only this secondary workload and print its result (for profiling)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; multi-GPU runs are not part "
-                                   "of this build (see the sharding notes in the design document)",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the path is single-GPU, and "
+                                   "its sharding over several GPUs is described, not implemented",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -416,6 +418,11 @@ def main():
         sys.exit(3)
     kvq.lib()
     torch.cuda.set_device(0)
+    if args.leg:
+        legs = {"block_scatter": leg_block_scatter, "sink_ring": leg_sink_ring, "long_prefill": leg_long_prefill,
+                "block_attention": leg_block_attention}
+        print(json.dumps({"leg": args.leg, "result": legs[args.leg]()}))
+        return
 
     st = Llama8BStep(args.replicas)
     w = st.w
