@@ -124,8 +124,13 @@ constexpr int PF_WAVES = 8;
 // holds keys 4g..4g+3 of the first and of the second 16-key block (the S^T
 // accumulator layout), as k-indices 8g..8g+3 and 8g+4..8g+7.
 __device__ __forceinline__ int pf_col(int k) { return ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3); }
-// 16-byte chunk swizzles: K rows by key, V^T rows by row.
-__device__ __forceinline__ int pf_ksw(int key) { return key & 7; }
+// 16-byte chunk swizzles: K rows by key, V^T rows by row.  A 128-bit LDS
+// read serves 16 lanes per pass; for 16 consecutive keys of a 256- or 512-byte
+// K row the chunk index is XORed with 4 key bits so the 16 reads fall in
+// distinct banks (measured: 3 bits left them 2-way conflicted); 128-byte rows
+// (D 64) need 3.
+template <int D>
+__device__ __forceinline__ int pf_ksw(int key) { return D >= 128 ? (key & 15) : (key & 7); }
 __device__ __forceinline__ int pf_vsw(int row) { return (row >> 1) & 3; }
 // V^T rows of block caches are in natural d order (a 16-row MFMA block then
 // lies inside one 32-element scale block); the stage writes 8 consecutive
@@ -387,7 +392,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             constexpr int CPP = D / 64;                    // 16-byte chunks of an eighth
 #pragma unroll
             for (int c = 0; c < CPP; ++c) {
-                const int ch = (part * CPP + c) ^ pf_ksw(key);
+                const int ch = (part * CPP + c) ^ pf_ksw<D>(key);
                 *reinterpret_cast<uint4*>(kt + key * D + ch * 8) =
                     make_uint4(hv[4 * c], hv[4 * c + 1], hv[4 * c + 2], hv[4 * c + 3]);
             }
@@ -487,7 +492,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int key = kb * 16 + l16;
-                    const int ch = (ds * 4 + lg) ^ pf_ksw(key);
+                    const int ch = (ds * 4 + lg) ^ pf_ksw<D>(key);
                     const half8_t av = *reinterpret_cast<const half8_t*>(kc + key * D + ch * 8);
                     part[kb] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -512,7 +517,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 const int key = kb * 16 + l16;
 #pragma unroll
                 for (int ds = 0; ds < NDS; ++ds) {
-                    const int ch = (ds * 4 + lg) ^ pf_ksw(key);
+                    const int ch = (ds * 4 + lg) ^ pf_ksw<D>(key);
                     const half8_t av = *reinterpret_cast<const half8_t*>(kc + key * D + ch * 8);
 #pragma unroll
                     for (int ql = 0; ql < QL; ++ql)
