@@ -122,7 +122,8 @@ kvq_status kvq_cache_bytes(int qmode, int B, int H, int n_slots, int D,
  * Rounding: round half to even, IEEE fp32 division, no contraction; codes,
  *   scales and zero points are bit-exact with the documented formulas.
  * Limits: T >= 0 (T == 0 enqueues nothing), D % 8 == 0 and D <= 8192
- *   (affine modes), D % 32 == 0 and D <= 8192 (block modes). */
+ *   (affine modes), D % 32 == 0 and D <= 8192 (block modes); B*H*T*D < 2^34
+ *   elements per call (else KVQ_ERR_SHAPE; split the call along T). */
 kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, int D,
                              int64_t stride_b, int64_t stride_h, int64_t stride_t,
                              const int32_t* slot_mapping, int64_t slot_stride_b,

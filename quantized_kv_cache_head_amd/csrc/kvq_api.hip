@@ -42,6 +42,9 @@ kvq_status check_cache(const kvq_cache* c) {
 
 kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
 
+// The scatter kernels index lanes (8 elements each) in 32 bits.
+bool scatter_size_ok(int B, int H, int T, int D) { return (int64_t)B * H * T * (D / 8) < (int64_t(1) << 31); }
+
 }  // namespace
 
 KVQ_API const char* kvq_status_string(kvq_status s) {
@@ -86,6 +89,7 @@ KVQ_API kvq_status kvq_quant_scatter_flags(const void* x, int x_dtype, int B, in
     // 8 elements per lane are loaded with 16-byte loads
     const int64_t vec = x_dtype == KVQ_BF16 ? 8 : 4;
     if (!aligned(x, 16) || stride_b % vec || stride_h % vec || stride_t % vec) return KVQ_ERR_SHAPE;
+    if (!scatter_size_ok(B, H, T, D)) return KVQ_ERR_SHAPE;
     return from_hip(kvq::launch_quant_scatter(cache->qmode, x_dtype == KVQ_BF16, x, B, H, T, D, stride_b, stride_h,
                                               stride_t, slot_mapping, slot_stride_b, cache->n_slots,
                                               reinterpret_cast<uint8_t*>(cache->codes), cache->scales, cache->zps,
@@ -118,6 +122,7 @@ KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dt
     const int64_t vec = x_dtype == KVQ_BF16 ? 8 : 4;
     if (!aligned(xk, 16) || !aligned(xv, 16) || stride_b % vec || stride_h % vec || stride_t % vec)
         return KVQ_ERR_SHAPE;
+    if (!scatter_size_ok(B, H, T, D)) return KVQ_ERR_SHAPE;
     return from_hip(kvq::launch_quant_scatter_kv(
         k_cache->qmode, x_dtype == KVQ_BF16, xk, xv, B, H, T, D, stride_b, stride_h, stride_t, slot_mapping,
         slot_stride_b, k_cache->n_slots, reinterpret_cast<uint8_t*>(k_cache->codes), k_cache->scales, k_cache->zps,

@@ -25,11 +25,32 @@
 // the contiguous code row.  Block modes: 4 lanes per 32-element block.
 // All arithmetic is single IEEE fp32 operations (file built with
 // -ffp-contract=off; division is correctly rounded; rintf is RNE), so codes,
-// scales and zero points are bit-exact with the documented formulas.
+// scales and zero points are bit-exact with the documented formulas.  An MX
+// scale X = 2^k divides by multiplying with 2^-k, which is exactly
+// representable (a subnormal for k = 127), so x * 2^-k rounds the same real
+// number as x / X and gives the same bits.
+//
+// Latency: a lane issues its x load together with its slot load (a row whose
+// slot turns out to be -1 has read 16 bytes for nothing), and thread indices
+// become (b, h, t, lane) with 32-bit multiply-shift division by the host's
+// precomputed constants (the launch holds fewer than 2^31 lanes).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
+
+// n / d for n < 2^31 as (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 (Granlund and Montgomery, division by
+// invariant integers using multiplication); the sum stays below 2^32.
+struct FastDiv {
+    uint32_t m, s;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+    uint32_t s = 0;
+    while (s < 32 && (1ull << s) < d) ++s;
+    return FastDiv{(uint32_t)((((1ull << s) - d) << 32) / d + 1), s};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) { return (__umulhi(n, f.m) + n) >> f.s; }
 
 struct ScatterArgs {
     const void* x;
@@ -43,14 +64,16 @@ struct ScatterArgs {
     int8_t* zps;
     int32_t* err;
     int flags;             // QF_MX_SCALE_OCP for the MX modes
+    uint32_t rows;         // B * H * T
+    FastDiv div_t, div_h, div_lpr;   // by T, by H, by the lanes of a row (block modes: D / 8)
 };
 
-// Decode row index -> (b, h, t) and look up its slot.
-__device__ __forceinline__ void row_coords(const ScatterArgs& a, int64_t row, int& b, int& h, int& t) {
-    t = (int)(row % a.T);
-    const int64_t bh = row / a.T;
-    h = (int)(bh % a.H);
-    b = (int)(bh / a.H);
+// Row index -> (b, h, t).
+__device__ __forceinline__ void row_coords(const ScatterArgs& a, uint32_t row, int& b, int& h, int& t) {
+    const uint32_t bh = fdiv(row, a.div_t);
+    t = (int)(row - bh * (uint32_t)a.T);
+    b = (int)fdiv(bh, a.div_h);
+    h = (int)(bh - (uint32_t)b * (uint32_t)a.H);
 }
 
 // Kernels take two argument sets and serve the one blockIdx.y picks (K and V
@@ -63,37 +86,36 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
     constexpr int QMAX = U4 ? 15 : 127;
     const int lane = threadIdx.x & 63;
     const int li = lane % L;
-    const int64_t rows = (int64_t)a.B * a.H * a.T;
-    const int64_t row = ((int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * (64 / L) + lane / L;
+    const uint32_t row = (blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * (64 / L) + lane / L;
 
+    // The slot and the row's x are loaded together (zeros past the last row
+    // or past D; zeros never change the range, which always contains 0).
     int b = 0, h = 0, t = 0, slot = -1;
-    if (row < rows) {
+    float v[NP][8];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
+    if (row < a.rows) {
         row_coords(a, row, b, h, t);
         slot = a.slots[(int64_t)b * a.ssb + t];
+        const int64_t xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int d0 = (p * L + li) * 8;
+            if (d0 < a.D) load8<BF16>(a.x, xoff + d0, v[p]);
+        }
         if (slot < -1 || slot >= a.n_slots) {
             if (h == 0 && li == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
             slot = -1;
         }
     }
     const bool valid = slot >= 0;
-
-    // Load (zeros where the row is skipped or past D; zeros never change the
-    // range, which always contains 0).
-    float v[NP][8];
     float lo = 0.0f, hi = 0.0f;
-    const int64_t xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int d0 = (p * L + li) * 8;
-        if (valid && d0 < a.D) {
-            load8<BF16>(a.x, xoff + d0, v[p]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
-        }
+    for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < 8; ++i) { lo = fminf(lo, v[p][i]); hi = fmaxf(hi, v[p][i]); }
-    }
     lo = wave_min_sub<L>(lo);
     hi = wave_max_sub<L>(hi);
     if (!valid) return;
@@ -139,32 +161,29 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
 template <bool BF16, int QM>
 __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, ScatterArgs a1) {
     const ScatterArgs a = blockIdx.y ? a1 : a0;
-    const int64_t gl = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int qi = (int)(gl & 3);                  // lane within the 32-block
-    const int64_t blk = gl >> 2;
+    const uint32_t gl = blockIdx.x * blockDim.x + threadIdx.x;
     const int gpr = a.D / 32;                      // blocks per row
-    const int64_t rows = (int64_t)a.B * a.H * a.T;
-    const int64_t row = blk / gpr;
-    const int g = (int)(blk % gpr);
+    const uint32_t row = fdiv(gl, a.div_lpr);
+    const int lr = (int)(gl - row * (uint32_t)(a.D / 8));   // lane within the row
+    const int qi = lr & 3;                         // lane within the 32-block
+    const int g = lr >> 2;
+    const int d0 = g * 32 + qi * 8;
 
+    // the slot and the row's x are loaded together
     int b = 0, h = 0, t = 0, slot = -1;
-    if (row < rows) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    if (row < a.rows) {
         row_coords(a, row, b, h, t);
         slot = a.slots[(int64_t)b * a.ssb + t];
+        load8<BF16>(a.x, (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st + d0, v);
         if (slot < -1 || slot >= a.n_slots) {
             if (h == 0 && g == 0 && qi == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
             slot = -1;
         }
     }
     const bool valid = slot >= 0;
-    float v[8];
-    const int d0 = g * 32 + qi * 8;
-    if (valid) {
-        load8<BF16>(a.x, (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st + d0, v);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
@@ -196,18 +215,18 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
         constexpr bool F4 = QM == QM_MXFP4_B32;
         const uint32_t e8 = (a.flags & QF_MX_SCALE_OCP) ? e8m0_floor(amax, F4 ? 2 : 8)
                                                          : e8m0_ceil(amax / (F4 ? 6.0f : 448.0f));
-        const float X = e8m0_value(e8);
+        const float inv = __uint_as_float(e8 == 254u ? 0x00400000u : (254u - e8) << 23);   // 1 / X, exact
         if constexpr (F4) {
             uint32_t w = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] / X) << (4 * i);
+            for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] * inv) << (4 * i);
             *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
         } else {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                w0 |= enc_e4m3fn(v[i] / X) << (8 * i);
-                w1 |= enc_e4m3fn(v[4 + i] / X) << (8 * i);
+                w0 |= enc_e4m3fn(v[i] * inv) << (8 * i);
+                w1 |= enc_e4m3fn(v[4 + i] * inv) << (8 * i);
             }
             *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
         }
@@ -239,9 +258,21 @@ static hipError_t dispatch_affine(const ScatterArgs& a, const ScatterArgs& a1, i
     }
 }
 
+// The launch's 32-bit index arithmetic needs fewer than 2^31 lanes (D / 8 per
+// row; the affine kernels use at most that many).
+static bool fill_index(ScatterArgs& a) {
+    const int64_t rows = (int64_t)a.B * a.H * a.T;
+    if (rows * ((a.D + 7) / 8) >= (int64_t(1) << 31)) return false;
+    a.rows = (uint32_t)rows;
+    a.div_t = make_fastdiv((uint32_t)a.T);
+    a.div_h = make_fastdiv((uint32_t)a.H);
+    a.div_lpr = make_fastdiv((uint32_t)(a.D / 8));
+    return true;
+}
+
 // One or two caches (n = 1 or 2) of the same mode and sizes in one launch.
-static hipError_t launch_scatter_n(int qmode, bool bf16, const ScatterArgs& a, const ScatterArgs& a1, int n,
-                                   hipStream_t s) {
+static hipError_t launch_scatter_n(int qmode, bool bf16, ScatterArgs a, ScatterArgs a1, int n, hipStream_t s) {
+    if (!fill_index(a) || !fill_index(a1)) return hipErrorInvalidValue;
     if (qmode == QM_INT8_TH) return bf16 ? dispatch_affine<true, false>(a, a1, n, s) : dispatch_affine<false, false>(a, a1, n, s);
     if (qmode == QM_UINT4_TH) return bf16 ? dispatch_affine<true, true>(a, a1, n, s) : dispatch_affine<false, true>(a, a1, n, s);
     const int64_t lanes = (int64_t)a.B * a.H * a.T * (a.D / 8);
