@@ -129,6 +129,30 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
     return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
 
+// Four codes per call through the gfx950 conversion instructions (round to
+// nearest even).  |y| is first clamped to the format's largest value, which
+// also turns a NaN into that value with its sign kept; so clamped, the
+// instructions return the encoders' codes above for every fp32 input (all
+// 2^32 bit patterns compared on the device).  Codes of y[0..3] in bytes 0..3
+// (FP8), nibbles 0..3 (E2M1; a second call fills nibbles 4..7 via `sel`).
+__device__ __forceinline__ float clamp_mag(float y, float mx) {
+    return __builtin_copysignf(fminf(__builtin_fabsf(y), mx), y);
+}
+__device__ __forceinline__ uint32_t cvt4_e4m3fn(const float* y) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_mag(y[0], 448.0f), clamp_mag(y[1], 448.0f), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp_mag(y[2], 448.0f), clamp_mag(y[3], 448.0f), lo, true);
+}
+__device__ __forceinline__ uint32_t cvt4_e5m2(const float* y) {
+    const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_mag(y[0], 57344.0f), clamp_mag(y[1], 57344.0f), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(clamp_mag(y[2], 57344.0f), clamp_mag(y[3], 57344.0f), lo, true);
+}
+__device__ __forceinline__ uint32_t cvt8_e2m1(const float* y) {
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, clamp_mag(y[0], 6.0f), clamp_mag(y[1], 6.0f), 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(y[2], 6.0f), clamp_mag(y[3], 6.0f), 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(y[4], 6.0f), clamp_mag(y[5], 6.0f), 1.0f, 2);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(y[6], 6.0f), clamp_mag(y[7], 6.0f), 1.0f, 3);
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64)
 // ---------------------------------------------------------------------------

@@ -197,15 +197,22 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
         const float scale = amax / QMAX;
         uint32_t w0 = 0, w1 = 0;
         if (scale != 0.0f) {
+            float y[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float y = v[i] / scale;
-                uint32_t c;
-                if constexpr (QM == QM_FP8E4M3_B32) c = enc_e4m3fn(y);
-                else if constexpr (QM == QM_FP8E5M2_B32) c = enc_e5m2(y);
-                else c = (uint32_t)(int)fminf(fmaxf(rintf(y), -127.0f), 127.0f) & 0xFFu;
-                if (i < 4) w0 |= c << (8 * i);
-                else w1 |= c << (8 * (i - 4));
+            for (int i = 0; i < 8; ++i) y[i] = v[i] / scale;
+            if constexpr (QM == QM_FP8E4M3_B32) {
+                w0 = cvt4_e4m3fn(y);
+                w1 = cvt4_e4m3fn(y + 4);
+            } else if constexpr (QM == QM_FP8E5M2_B32) {
+                w0 = cvt4_e5m2(y);
+                w1 = cvt4_e5m2(y + 4);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t c = (uint32_t)(int)fminf(fmaxf(rintf(y[i]), -127.0f), 127.0f) & 0xFFu;
+                    if (i < 4) w0 |= c << (8 * i);
+                    else w1 |= c << (8 * (i - 4));
+                }
             }
         }
         *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
@@ -216,19 +223,13 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
         const uint32_t e8 = (a.flags & QF_MX_SCALE_OCP) ? e8m0_floor(amax, F4 ? 2 : 8)
                                                          : e8m0_ceil(amax / (F4 ? 6.0f : 448.0f));
         const float inv = __uint_as_float(e8 == 254u ? 0x00400000u : (254u - e8) << 23);   // 1 / X, exact
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = v[i] * inv;
         if constexpr (F4) {
-            uint32_t w = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) w |= enc_e2m1(v[i] * inv) << (4 * i);
-            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = cvt8_e2m1(y);
         } else {
-            uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w0 |= enc_e4m3fn(v[i] * inv) << (8 * i);
-                w1 |= enc_e4m3fn(v[4 + i] * inv) << (8 * i);
-            }
-            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(cvt4_e4m3fn(y), cvt4_e4m3fn(y + 4));
         }
         if (qi == 0) reinterpret_cast<uint8_t*>(a.scales)[crow * gpr + g] = (uint8_t)e8;
     }

@@ -155,3 +155,65 @@ def test_scatter_mx_ocp_scale_parity(qmode, D):
     torch.cuda.synchronize()
     oracle.quant_scatter(hc, x, slots, qflags=oracle.MX_SCALE_OCP)
     assert_cache_equal(dc, hc, f"OCP qmode {qmode} D {D}")
+
+
+def _unit_scale_rows(code_values, qmax, top):
+    """fp32 rows of 32-element blocks whose first element is `top` (giving the
+    block a scale of exactly 1) and whose other elements are every code value,
+    every midpoint between neighbouring values (an exact tie), and each
+    midpoint one fp32 ulp either side, in both signs; values above qmax up to
+    `top` when top > qmax (the saturating range)."""
+    v = np.unique(np.abs(np.asarray(code_values, np.float64)))
+    mids = (v[:-1] + v[1:]) / 2
+    f = [v, mids]
+    m32 = mids.astype(np.float32)
+    f += [np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(0))]
+    f.append(np.array([2.0 ** -149, 2.0 ** -126, 1e-30, v[1] / 4, v[1] / 2 * (1 + 2 ** -20)]))
+    if top > qmax:
+        f.append(np.linspace(qmax, top, 9))
+    vals = np.concatenate([np.asarray(a, np.float64) for a in f]).astype(np.float32)
+    vals = np.concatenate([vals, -vals])
+    nblk = -(-len(vals) // 31)
+    x = np.zeros((nblk, 32), np.float32)
+    x[:, 0] = top
+    flat = x[:, 1:].reshape(-1)
+    flat[:len(vals)] = vals
+    x[:, 1:] = flat.reshape(nblk, 31)
+    return x
+
+
+@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + [(kvq.MXFP4_B32, True), (kvq.MXFP8_B32, True)])
+def test_scatter_block_every_rounding_boundary(qmode, ocp):
+    """Every code, every tie between neighbouring codes and the values one ulp
+    either side of it, at a block scale of exactly 1 (fp32 input), so the
+    element encoders see these values unchanged: the codes must be the
+    oracle's, bit for bit.  With the OCP scale rule the block maximum may
+    exceed the format's largest value while the scale stays 1, which
+    exercises saturation."""
+    if qmode == kvq.MXFP4_B32:
+        codes, qmax = [oracle.e2m1_decode(c) for c in range(8)], 6.0
+    elif qmode == kvq.FP8E5M2_B32:
+        codes, qmax = [oracle.e5m2_decode(c) for c in range(0x7C)], 57344.0
+    elif qmode == kvq.INT8_B32:
+        codes, qmax = list(range(128)), 127.0
+    else:
+        codes, qmax = [oracle.e4m3fn_decode(c) for c in range(0x7F)], 448.0
+    # OCP floor rule: the scale is 1 for any block maximum in [2^emax, 2^(emax+1))
+    top = (7.5 if qmode == kvq.MXFP4_B32 else 511.0) if ocp else qmax
+    blocks = _unit_scale_rows(codes, qmax, top)
+    D = 128
+    T = -(-blocks.shape[0] // (D // 32))
+    x = np.zeros((T * (D // 32), 32), np.float32)
+    x[:blocks.shape[0]] = blocks
+    x = x.reshape(1, 1, T, D)
+    say(f"scatter rounding boundaries qmode={qmode} ocp={ocp} T={T}")
+    dc, hc = new_pair(qmode, 1, 1, T, D)
+    slots = np.arange(T, dtype=np.int32)[None]
+    kvq.quant_scatter(dev_input(x, False), torch.from_numpy(slots).to(DEV), dc, flags=kvq.MX_SCALE_OCP if ocp else 0)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots, qflags=oracle.MX_SCALE_OCP if ocp else 0)
+    sc = hc.scales.reshape(-1)[:blocks.shape[0]].astype(np.float64)
+    if hc.scales.dtype == np.uint8:
+        sc = 2.0 ** (sc - 127)
+    assert np.all(sc == 1.0), "every block must have scale 1"
+    assert_cache_equal(dc, hc, f"boundaries qmode {qmode}")
