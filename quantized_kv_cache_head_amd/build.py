@@ -64,5 +64,28 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+TESTS_CSRC = os.path.join(os.path.dirname(PKG), "tests", "csrc")
+
+
+def build_test_tools(verbose: bool = False) -> list:
+    """Compile the device-side test programs under tests/csrc (one executable
+    per .hip file, next to its source)."""
+    out = []
+    if not os.path.isdir(TESTS_CSRC):
+        return out
+    for f in sorted(os.listdir(TESTS_CSRC)):
+        if not f.endswith(".hip"):
+            continue
+        exe = os.path.join(TESTS_CSRC, f[:-4])
+        flags = [x for x in COMMON if x not in ("-fPIC", "-fvisibility=hidden")]
+        r = subprocess.run([hipcc(), *flags, "-o", exe, os.path.join(TESTS_CSRC, f)], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {f}:\n{r.stdout}\n{r.stderr}")
+        out.append(exe)
+        if verbose:
+            print(f"built {exe}")
+    return out
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])

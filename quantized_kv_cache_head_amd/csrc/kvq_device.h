@@ -43,42 +43,8 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem_off, float 
 }
 
 // ---------------------------------------------------------------------------
-// Element encoders (integer rounding on the fp32 bit pattern)
+// E8M0 scales and element encoders
 // ---------------------------------------------------------------------------
-
-// FP8 E4M3FN, round to nearest even, |y| >= 448 saturates to 0x7E, sign kept.
-__device__ __forceinline__ uint32_t enc_e4m3fn(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x43E00000u) {                 // >= 448
-        mag = 0x7Eu;
-    } else if (a < 0x3C800000u) {           // < 2^-6: multiples of 2^-9
-        mag = (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-    } else {                                // keep 3 mantissa bits, RNE
-        const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-        mag = (r >> 20) - (120u << 3);      // rebias exponent 127 -> 7
-    }
-    return sign | mag;
-}
-
-// FP4 E2M1 (magnitudes 0,.5,1,1.5,2,3,4,6), RNE, |y| >= 6 saturates, sign bit 3.
-__device__ __forceinline__ uint32_t enc_e2m1(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 28) & 0x8u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x40C00000u) {                 // >= 6
-        mag = 7u;
-    } else if (a < 0x3F800000u) {           // < 1: multiples of 0.5
-        mag = (uint32_t)rintf(__uint_as_float(a) * 2.0f);
-    } else {                                // keep 1 mantissa bit, RNE
-        const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-        mag = (r >> 22) - (126u << 1);      // rebias exponent 127 -> 1
-    }
-    return sign | mag;
-}
 
 // Biased E8M0 exponent of the smallest power of two >= s (s >= 0), clamped
 // to [0, 254].
@@ -93,24 +59,6 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float s) {
     int b = e + 127;
     b = b < 0 ? 0 : (b > 254 ? 254 : b);
     return (uint32_t)b;
-}
-
-// FP8 E5M2 (bias 15, 2 mantissa bits), round to nearest even, |y| >= 57344
-// saturates to 0x7B (never inf), sign kept.
-__device__ __forceinline__ uint32_t enc_e5m2(float y) {
-    const uint32_t u = __float_as_uint(y);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x47600000u) {                 // >= 57344
-        mag = 0x7Bu;
-    } else if (a < 0x38800000u) {           // < 2^-14: multiples of 2^-16
-        mag = (uint32_t)rintf(__uint_as_float(a) * 65536.0f);
-    } else {                                // keep 2 mantissa bits, RNE
-        const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
-        mag = (r >> 21) - (112u << 2);      // rebias exponent 127 -> 15
-    }
-    return sign | mag;
 }
 
 // Biased E8M0 exponent floor(log2 amax) - emax + 127 (OCP MX shared-scale
@@ -129,12 +77,14 @@ __device__ __forceinline__ float e8m0_value(uint32_t b) {
     return b == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
 
-// Four codes per call through the gfx950 conversion instructions (round to
-// nearest even).  |y| is first clamped to the format's largest value, which
-// also turns a NaN into that value with its sign kept; so clamped, the
-// instructions return the encoders' codes above for every fp32 input (all
-// 2^32 bit patterns compared on the device).  Codes of y[0..3] in bytes 0..3
-// (FP8), nibbles 0..3 (E2M1; a second call fills nibbles 4..7 via `sel`).
+// Element encoders: FP8 E4M3FN, FP8 E5M2 and FP4 E2M1 codes, round to nearest
+// even, |y| at or above the format's largest value (448, 57344, 6) saturating
+// to it, sign kept (a NaN saturates too).  The gfx950 conversion instructions
+// round to nearest even; |y| is clamped to the largest value first, which
+// gives the saturation and turns a NaN into that value with its sign kept.
+// tests/csrc/encoder_sweep.hip compares these with bit-level encoders over
+// all 2^32 fp32 inputs.  Codes of y[0..3] go to bytes 0..3 (FP8); E2M1 codes
+// of y[0..7] to nibbles 0..7.
 __device__ __forceinline__ float clamp_mag(float y, float mx) {
     return __builtin_copysignf(fminf(__builtin_fabsf(y), mx), y);
 }
