@@ -885,10 +885,15 @@ static const void* split_kernel_for(int D, int qm, int G, bool qbf16) {
 #undef KVQ_SK
 }
 
-// Workgroups of one split-kernel instantiation that fit on the current device
-// at once: per CU, the smaller of the VGPR limit (512 registers per lane of a
-// SIMD in granules of 8; a 4-wave workgroup puts one wave on each SIMD) and
-// the LDS limit, times the CU count.  0 when the runtime cannot tell.
+// Workgroups of one split-kernel instantiation to keep on the device at once:
+// per CU, the smaller of the VGPR limit (512 registers per lane of a SIMD in
+// granules of 8; a 4-wave workgroup puts one wave on each SIMD), the LDS limit
+// and 2, times the CU count.  0 when the runtime cannot tell.  Two per CU
+// (8 waves) ran as fast as three or faster on the int8 decode at batch 1 to 32
+// and 1k to 32k keys (up to 15-20% at batch 1-4): each workgroup's prologue,
+// merge and partials cost more than a third workgroup's latency hiding buys.
+// Counts that leave CUs unevenly loaded (between two and three per CU) were
+// slower than either.
 static int resident_workgroups(int D, int qm, int G, bool qbf16) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -907,7 +912,7 @@ static int resident_workgroups(int D, int qm, int G, bool qbf16) {
         lds_cu = 160 * 1024;
     const int granule = (fa.numRegs + 7) / 8 * 8;
     int per_cu = 512 / granule;
-    if (per_cu > 8) per_cu = 8;
+    if (per_cu > 2) per_cu = 2;
     if (fa.sharedSizeBytes > 0) {
         const int by_lds = lds_cu / (int)fa.sharedSizeBytes;
         if (by_lds < per_cu) per_cu = by_lds;
