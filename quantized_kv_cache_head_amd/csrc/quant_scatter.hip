@@ -25,7 +25,9 @@
 // the contiguous code row.  Block modes: 4 lanes per 32-element block.
 // All arithmetic is single IEEE fp32 operations (file built with
 // -ffp-contract=off; division is correctly rounded; rintf is RNE), so codes,
-// scales and zero points are bit-exact with the documented formulas.  An MX
+// scales and zero points are bit-exact with the documented formulas.  FP8 and
+// E2M1 codes come from the conversion instructions, which round the quotient
+// to nearest even after a magnitude clamp (kvq_device.h).  An MX
 // scale X = 2^k divides by multiplying with 2^-k, which is exactly
 // representable (a subnormal for k = 127), so x * 2^-k rounds the same real
 // number as x / X and gives the same bits.
