@@ -28,7 +28,11 @@
 //    column's max grows by more than 8).
 //  * Software pipeline over tiles: the raw codes of tile t+2 stream into LDS
 //    (global_load_lds) and tile t+1 is dequantized while tile t's MFMAs run;
-//    one barrier per tile.
+//    one barrier per tile.  The tile loop is compiled separately for the
+//    K-dequantizing and the V-dequantizing waves, so a wave's QK MFMAs and its
+//    dequantization share one basic block, and the scheduler is asked to
+//    issue them interleaved (one MFMA, then four VALU instructions): the
+//    VALU work runs while the matrix core is busy instead of after it.
 //  * Workgroups of one KV head are placed on the same XCD so its K/V stream
 //    is shared through that XCD's L2.
 //  * Block caches (a scale per 32 elements: FP8-E4M3, FP8-E5M2 or int8 with
@@ -39,6 +43,7 @@
 //    summed; V^T rows stay in d order so a 16-row output block lies in one
 //    scale block, and P enters that block's PV product scaled by the keys'
 //    V scales of that block.  Raw rows are read below kv_len only.
+#include <type_traits>
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -370,9 +375,10 @@ void sdpa_prefill_mfma(PrefillArgs a) {
 
     // Dequantize tile tt (raw codes in raw, metadata in mbuf) into the fp16
     // tiles kt / vt and its key scales into ct / st_.
-    auto stage = [&](int tt, const uint8_t* raw, int mbuf, _Float16* kt, _Float16* vt, float* ct, float* sv,
-                     float* bkt, float* bvt) {
-        if (!vhalf) {
+    auto stage = [&](auto vh, int tt, const uint8_t* raw, int mbuf, _Float16* kt, _Float16* vt, float* ct, float* sv,
+                     float* bkt, float* bvt) __attribute__((always_inline)) {
+        constexpr bool VH = decltype(vh)::value;
+        if constexpr (!VH) {
             // thread -> (key, eighth of the row: D/8 elements)
             constexpr int NPR = D / 16;                    // fp16 pairs of an eighth
             const int key = KPM ? (t256 & 31) : (t256 >> 3);
@@ -465,16 +471,17 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        stage(0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
+        if (vhalf) stage(std::true_type{}, 0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
+        else stage(std::false_type{}, 0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
         __syncthreads();
     }
 
     // Tile t: computes on (kc, vc, cc, sc); dequantizes tile t+1 from raw_n1
     // into (kn, vn, cn, sn); streams tile t+2 into raw_n2 (the buffer tile t
     // came through).
-    auto tile = [&](const int t, const _Float16* kc, const _Float16* vc, const float* cc, const float* sc,
+    auto tile = [&](auto vh, const int t, const _Float16* kc, const _Float16* vc, const float* cc, const float* sc,
                     const float* bkc, const float* bvc, _Float16* kn, _Float16* vn, float* cn, float* sn,
-                    float* bkn, float* bvn, const uint8_t* raw_n1, uint8_t* raw_n2) {
+                    float* bkn, float* bvn, const uint8_t* raw_n1, uint8_t* raw_n2) __attribute__((always_inline)) {
         const int j0 = t * BN;
         if (t + 2 < n_tiles) {
             fetch_meta(t + 2);
@@ -526,7 +533,15 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             }
         }
         // ---------------- tile t+1 dequantized while those MFMAs run -----------
-        if (t + 1 < n_tiles) stage(t + 1, raw_n1, (t + 1) & 1, kn, vn, cn, sn, bkn, bvn);
+        // (unconditional, so it stays in the MFMAs' basic block: past the last
+        // tile it converts whatever the raw buffer holds into a buffer nobody
+        // reads)
+        stage(vh, t + 1, raw_n1, (t + 1) & 1, kn, vn, cn, sn, bkn, bvn);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+        }
 
         // ---------------- softmax over this lane's 8 keys -----------------------
         // lane holds keys j0 + kb*16 + 4*lg + i of query column qc
@@ -630,10 +645,14 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         __builtin_amdgcn_s_waitcnt(0);                // tile t+2's code rows have landed
         __syncthreads();
     };
-    for (int t = 0; t < n_tiles; t += 2) {
-        tile(t, k_a, v_a, c_a, s_a, bk_a, bv_a, k_b, v_b, c_b, s_b, bk_b, bv_b, raw_b, raw_a);
-        if (t + 1 < n_tiles) tile(t + 1, k_b, v_b, c_b, s_b, bk_b, bv_b, k_a, v_a, c_a, s_a, bk_a, bv_a, raw_a, raw_b);
-    }
+    auto run = [&](auto vh) __attribute__((always_inline)) {
+        for (int t = 0; t < n_tiles; t += 2) {
+            tile(vh, t, k_a, v_a, c_a, s_a, bk_a, bv_a, k_b, v_b, c_b, s_b, bk_b, bv_b, raw_b, raw_a);
+            if (t + 1 < n_tiles) tile(vh, t + 1, k_b, v_b, c_b, s_b, bk_b, bv_b, k_a, v_a, c_a, s_a, bk_a, bv_a, raw_a, raw_b);
+        }
+    };
+    if (vhalf) run(std::true_type{});
+    else run(std::false_type{});
 
     // ---- epilogue: l over the 4 lane groups, normalize, store --------------------
     {
