@@ -289,7 +289,7 @@ __device__ __forceinline__ void reduce_scatter(float* v, int lane) {
 // A split holds at most rows_max rows (scores in LDS); rows_max is a multiple
 // of both workgroup steps.
 struct DecGeom {
-    int rowb, kb, ck, rk, cv, rv, stepk, stepv, stepm, rows_max;
+    int rowb, kb, ck, rk, cv, rv, stepk, stepv, rows_max;
 };
 __host__ __device__ constexpr DecGeom dec_geom(int D, bool u4, int G) {
     const int rowb = u4 ? D / 2 : D;
@@ -298,7 +298,7 @@ __host__ __device__ constexpr DecGeom dec_geom(int D, bool u4, int G) {
     const int cv = rowb / 16, rv = 64 / cv;
     const int stepk = rk * DEC_WAVES, stepv = rv * DEC_WAVES;
     const int rows_max = G <= 4 ? 1024 : 512;
-    return DecGeom{rowb, kb, ck, rk, cv, rv, stepk, stepv, stepk > stepv ? stepk : stepv, rows_max};
+    return DecGeom{rowb, kb, ck, rk, cv, rv, stepk, stepv, rows_max};
 }
 
 // Sum over aligned groups of N lanes (N = 2, 4, 8, 16) valid in the first
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr float VOFF = (U4 || BLK) ? 0.0f : 128.0f;   // fp32 value = code + VOFF
     constexpr int NV = G * EV;                       // accumulators per lane
     constexpr int NVR = NV / RV;                     // after the row-group reduce-scatter
-    constexpr int STEPK = GM.stepk, STEPV = GM.stepv, STEPM = GM.stepm;
+    constexpr int STEPK = GM.stepk, STEPV = GM.stepv;
     constexpr int PD = KVQ_DEC_PD;                   // K ring depth (steps in flight)
     constexpr int PDV = KVQ_DEC_PDV;                 // V ring depth: issued before the middle pass
     constexpr int ROWS_MAX = GM.rows_max;
