@@ -259,6 +259,30 @@ kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, in
                                    unsigned flags, float sm_scale, void* out, int out_dtype,
                                    int32_t* err_flags, void* stream);
 
+/* kvq_sdpa_prefill for chunks too short to fill the GPU with query tiles alone
+ * (the chunked prefill of [PR20351] with a small Lq, which gives
+ * B * heads * ceil(Lq * (Hq / heads) / 128) workgroups): each query tile's
+ * key range, below its per-tile causal bound, is split over several
+ * workgroups, and the splits' partial (max, sum, output) are merged per query
+ * row afterwards, as in decode.  Arguments, bounds, masks, errors and result
+ * as kvq_sdpa_prefill, within the same tolerance (the split changes the
+ * summation order, so the bits may differ from it), plus:
+ * workspace: device buffer, 16-byte aligned, of at least
+ *   kvq_sdpa_prefill_split_workspace_bytes(B, Hq, heads, Lq, n_slots, D)
+ *   bytes ([B*Hq*Lq, splits, D + 2] fp32 partials; no initialisation needed;
+ *   calls that overlap in time need separate workspaces).  KVQ_ERR_WORKSPACE
+ *   when it is missing, misaligned or too small.  A size of 0 means the query
+ *   tiles fill the part already: the call then runs as kvq_sdpa_prefill and
+ *   workspace may be NULL.  The split count depends on the sizes only (about
+ *   512 workgroups, at least 256 keys of n_slots per split, at most 64). */
+size_t kvq_sdpa_prefill_split_workspace_bytes(int B, int Hq, int heads, int Lq, int n_slots, int D);
+kvq_status kvq_sdpa_prefill_split(const void* q, int q_dtype, int B, int Hq, int Lq,
+                                  const kvq_cache* k, const kvq_cache* v,
+                                  const int32_t* kv_len, const float* mask, int mask_is_causal,
+                                  unsigned flags, float sm_scale, void* out, int out_dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t* err_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -247,14 +247,23 @@ kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq
     return from_hip(kvq::launch_sdpa_decode(L, reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Bytes of a key-split prefill's partials: [B * Hq * Lq, splits, D + 2] fp32.
+size_t prefill_ws_bytes(int splits, int B, int Hq, int Lq, int D) {
+    return splits > 1 ? (size_t)B * Hq * Lq * splits * ((size_t)D + 2) * sizeof(float) : 0;
+}
+
 kvq_status sdpa_prefill_impl(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
                              const kvq_cache* v, const int32_t* kv_len, int kv_len_sb, const float* mask,
                              int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
-                             int32_t* err_flags, void* stream) {
+                             bool split, void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                             void* stream) {
     kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (Lq < 1 || Lq > k->n_slots) return KVQ_ERR_SHAPE;
     if (flags & ~KVQ_NO_CAUSAL_SKIP) return KVQ_ERR_UNSUPPORTED;
+    const int splits = split ? kvq::prefill_kv_splits(B, Hq, k->heads, Lq, k->n_slots) : 1;
+    const size_t need = prefill_ws_bytes(splits, B, Hq, Lq, k->head_dim);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16))) return KVQ_ERR_WORKSPACE;
     kvq::PrefillLaunch L;
     L.q = q;
     L.q_bf16 = q_dtype == KVQ_BF16;
@@ -280,6 +289,11 @@ kvq_status sdpa_prefill_impl(const void* q, int q_dtype, int B, int Hq, int Lq, 
     L.out = out;
     L.out_bf16 = out_dtype == KVQ_BF16;
     L.err = err_flags;
+    L.kv_splits = splits;
+    if (splits > 1) {
+        L.part_o = reinterpret_cast<float*>(workspace);
+        L.part_ml = L.part_o + (size_t)B * Hq * Lq * splits * k->head_dim;
+    }
     hipError_t e = kvq::launch_sdpa_prefill(L, reinterpret_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported) return KVQ_ERR_UNSUPPORTED;
     return from_hip(e);
@@ -312,7 +326,7 @@ KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, i
                                     int mask_is_causal, unsigned flags, float sm_scale, void* out, int out_dtype,
                                     int32_t* err_flags, void* stream) {
     return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_len, 0, mask, mask_is_causal, flags, sm_scale, out,
-                             out_dtype, err_flags, stream);
+                             out_dtype, false, nullptr, 0, err_flags, stream);
 }
 
 KVQ_API kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
@@ -321,5 +335,19 @@ KVQ_API kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, in
                                            int out_dtype, int32_t* err_flags, void* stream) {
     if (!kv_lens) return KVQ_ERR_NULL;
     return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_lens, 1, mask, mask_is_causal, flags, sm_scale, out,
-                             out_dtype, err_flags, stream);
+                             out_dtype, false, nullptr, 0, err_flags, stream);
+}
+
+KVQ_API size_t kvq_sdpa_prefill_split_workspace_bytes(int B, int Hq, int Hkv, int Lq, int n_slots, int D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || Lq <= 0 || n_slots <= 0 || D <= 0) return 0;
+    return prefill_ws_bytes(kvq::prefill_kv_splits(B, Hq, Hkv, Lq, n_slots), B, Hq, Lq, D);
+}
+
+KVQ_API kvq_status kvq_sdpa_prefill_split(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,
+                                          const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                          int mask_is_causal, unsigned flags, float sm_scale, void* out,
+                                          int out_dtype, void* workspace, size_t workspace_bytes,
+                                          int32_t* err_flags, void* stream) {
+    return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_len, 0, mask, mask_is_causal, flags, sm_scale, out,
+                             out_dtype, true, workspace, workspace_bytes, err_flags, stream);
 }

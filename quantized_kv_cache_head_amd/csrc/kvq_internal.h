@@ -78,8 +78,18 @@ struct PrefillLaunch {
     void* out;
     bool out_bf16;
     int32_t* err;
+    int kv_splits = 1;      // > 1: key range split over workgroups, partials in part_o / part_ml
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
 };
 
 hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s);
+int prefill_kv_splits(int B, int Hq, int Hkv, int Lq, int S);
+
+// Merge per-split partials (o [rows, nsplit, D], (m, l) [rows, nsplit, 2],
+// log2 units) into out [rows, D]; rows are (b, head) for decode and
+// (b, head, query row) for a split prefill.
+hipError_t launch_split_combine(int D, const float* part_o, const float* part_ml, int nsplit, int64_t rows,
+                                void* out, bool out_bf16, hipStream_t s);
 
 }  // namespace kvq

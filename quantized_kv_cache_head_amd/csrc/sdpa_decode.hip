@@ -797,7 +797,8 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     }
 }
 
-// Merge the splits of one (b, query head): o = sum_s o_s 2^(m_s - m*) / l
+// Merge the splits of one row -- a (b, query head) of decode, a (b, query
+// head, query row) of a key-split prefill: o = sum_s o_s 2^(m_s - m*) / l
 // with l = sum_s l_s 2^(m_s - m*).  The splits go in chunks of CH whose o and
 // (m, l) loads are all issued before any arithmetic (one memory round trip
 // per chunk); a running maximum rescales the sums between chunks.  A row
@@ -988,12 +989,19 @@ hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s) {
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    const unsigned nbh = (unsigned)(L.B * L.Hq);
-    const int ob = L.out_bf16 ? 1 : 0;
-    switch (L.D) {
-    case 64: hipLaunchKernelGGL((sdpa_decode_combine<64>), dim3(nbh), dim3(64), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
-    case 128: hipLaunchKernelGGL((sdpa_decode_combine<128>), dim3(nbh), dim3(128), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
-    default: hipLaunchKernelGGL((sdpa_decode_combine<256>), dim3(nbh), dim3(256), 0, s, L.part_o, L.part_ml, L.nsplit, L.out, ob); break;
+    return launch_split_combine(L.D, L.part_o, L.part_ml, L.nsplit, (int64_t)L.B * L.Hq, L.out, L.out_bf16, s);
+}
+
+hipError_t launch_split_combine(int D, const float* part_o, const float* part_ml, int nsplit, int64_t rows,
+                                void* out, bool out_bf16, hipStream_t s) {
+    if (rows <= 0 || rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const unsigned nr = (unsigned)rows;
+    const int ob = out_bf16 ? 1 : 0;
+    switch (D) {
+    case 64: hipLaunchKernelGGL((sdpa_decode_combine<64>), dim3(nr), dim3(64), 0, s, part_o, part_ml, nsplit, out, ob); break;
+    case 128: hipLaunchKernelGGL((sdpa_decode_combine<128>), dim3(nr), dim3(128), 0, s, part_o, part_ml, nsplit, out, ob); break;
+    case 256: hipLaunchKernelGGL((sdpa_decode_combine<256>), dim3(nr), dim3(256), 0, s, part_o, part_ml, nsplit, out, ob); break;
+    default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

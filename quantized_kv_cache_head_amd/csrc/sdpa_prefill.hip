@@ -68,6 +68,9 @@ struct PrefillArgs {
     float sm_scale_log2;
     void* out;
     int32_t* err;
+    int kv_splits;         // workgroups per query tile along the key range (gridDim.y)
+    float* part_o;         // kv_splits > 1: [B * Hq * Lq, kv_splits, D] unnormalized outputs
+    float* part_ml;        //                [B * Hq * Lq, kv_splits, 2] (max, sum) in log2 units
 };
 
 constexpr float PF_TAU = 8.0f;   // lazy rescale threshold (log2 units)
@@ -296,7 +299,13 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
     const uint8_t* kcodes = a.kc + plane * ROWB;
     const uint8_t* vcodes = a.vc + plane * ROWB;
-    const int n_tiles = (loop_end + BN - 1) / BN;
+    // this workgroup's share of the key tiles below loop_end (all of them
+    // unless the key range is split over gridDim.y workgroups); t below
+    // counts tiles from t0
+    const int tiles_all = (loop_end + BN - 1) / BN;
+    const int per_split = (tiles_all + a.kv_splits - 1) / a.kv_splits;
+    const int t0 = (int)blockIdx.y * per_split;
+    const int n_tiles = max(min(per_split, tiles_all - t0), 0);
     const int diag_lo = qpos0 + r0;        // keys <= this are visible to every row of the tile
     const int lim = a.causal ? qpos0 + q_row : kv_len - 1;   // this column's last visible key
 
@@ -307,7 +316,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     constexpr int RSTEPS = (TILEB + 4095) / 4096;
     static_assert(TILEB % 4096 == 0 || TILEB < 4096, "raw tile steps");
     auto fetch_raw = [&](int tt, uint8_t* raw) {
-        const int jt = tt * BN;
+        const int jt = (t0 + tt) * BN;
         const uint8_t* src = vhalf ? vcodes : kcodes;
         uint8_t* dst = raw + (vhalf ? TILEB : 0);
 #pragma unroll
@@ -336,7 +345,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     auto fetch_meta = [&](int tt) {
         if constexpr (BLK) {
             if (tid < NG * BN) {                      // thread -> (group tid / BN, key tid % BN)
-                const int j = min(tt * BN + tid % BN, kv_len - 1);
+                const int j = min((t0 + tt) * BN + tid % BN, kv_len - 1);
                 const int64_t gi = (plane + j) * NG + tid / BN;
                 if constexpr (SC8) {
                     bk_r = reinterpret_cast<const uint8_t*>(a.ks)[gi];
@@ -347,7 +356,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 }
             }
         } else if (tid < BN) {
-            const int j = min(tt * BN + tid, kv_len - 1);
+            const int j = min((t0 + tt) * BN + tid, kv_len - 1);
             mk_s = a.ks[plane + j];
             mv_s = a.vs[plane + j];
             mk_z = a.kz[plane + j];
@@ -405,13 +414,13 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             if constexpr (BLK) {
                 // block scales of keys past kv_len become 0 (their P is 0 too)
                 if (tid < NG * BN) {
-                    const bool in = tt * BN + tid % BN < kv_len;
+                    const bool in = (t0 + tt) * BN + tid % BN < kv_len;
                     bkt[tid] = in ? bks_lds[mbuf][tid] : 0.0f;
                     bvt[tid] = in ? bvs_lds[mbuf][tid] * VSC : 0.0f;
                 }
-                if (tid < BN) ct[tid] = tt * BN + tid < kv_len ? rs : 0.0f;
+                if (tid < BN) ct[tid] = (t0 + tt) * BN + tid < kv_len ? rs : 0.0f;
             } else if (tid < BN) {
-                const bool in = tt * BN + tid < kv_len;
+                const bool in = (t0 + tt) * BN + tid < kv_len;
                 ct[tid] = in ? mks_lds[mbuf][tid] * rs : 0.0f;
                 sv[tid] = in ? mvs_lds[mbuf][tid] : 0.0f;
             }
@@ -482,7 +491,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     auto tile = [&](auto vh, const int t, const _Float16* kc, const _Float16* vc, const float* cc, const float* sc,
                     const float* bkc, const float* bvc, _Float16* kn, _Float16* vn, float* cn, float* sn,
                     float* bkn, float* bvn, const uint8_t* raw_n1, uint8_t* raw_n2) __attribute__((always_inline)) {
-        const int j0 = t * BN;
+        const int j0 = (t0 + t) * BN;
         if (t + 2 < n_tiles) {
             fetch_meta(t + 2);
             fetch_raw(t + 2, raw_n2);
@@ -662,6 +671,25 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         l_run = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
     }
     if (!q_live) return;
+    if (a.kv_splits > 1) {
+        // partial (m, l, o) of this key range for the split combine; o carries
+        // the V-scale factor 2^VF removed
+        const int64_t pr = (((int64_t)b * a.Hq + q_head) * a.Lq + q_row) * a.kv_splits + blockIdx.y;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int R = db * 16 + 4 * lg + i;
+                const int d = BLK ? R : (R % DG) * 8 + R / DG;
+                a.part_o[pr * D + d] = o_acc[db][i] * (1.0f / VSC);
+            }
+        }
+        if (lg == 0) {
+            a.part_ml[pr * 2] = m_run;
+            a.part_ml[pr * 2 + 1] = l_run;
+        }
+        return;
+    }
     const float inv = l_run > 0.0f ? (1.0f / l_run) * (1.0f / VSC) : 0.0f;
     const int64_t obase = (((int64_t)b * a.Hq + q_head) * a.Lq + q_row) * D;
 #pragma unroll
@@ -684,7 +712,8 @@ static hipError_t launch_pf(const PrefillArgs& a, hipStream_t s) {
     PrefillArgs aa = a;
     aa.n_qtiles = (a.Lq + QT - 1) / QT;
     const unsigned blocks = (unsigned)(a.B * a.Hkv * aa.n_qtiles);
-    hipLaunchKernelGGL((sdpa_prefill_mfma<D, QM, QL, PL>), dim3(blocks), dim3(64 * PF_WAVES), 0, s, aa);
+    hipLaunchKernelGGL((sdpa_prefill_mfma<D, QM, QL, PL>), dim3(blocks, (unsigned)a.kv_splits), dim3(64 * PF_WAVES), 0, s,
+                       aa);
     return hipGetLastError();
 }
 
@@ -711,17 +740,40 @@ static hipError_t dispatch_pm(const PrefillArgs& a, int qmode, bool q_bf16, hipS
 }
 
 hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s) {
+    const int ks = L.kv_splits > 1 ? L.kv_splits : 1;
     PrefillArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.Lq, 0, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len, L.kv_len_sb,
                   L.mask, L.causal ? 1 : 0, L.no_skip ? 1 : 0, L.out_bf16 ? 1 : 0,
-                  L.sm_scale * 1.4426950408889634f, L.out, L.err};
+                  L.sm_scale * 1.4426950408889634f, L.out, L.err, ks, L.part_o, L.part_ml};
     const int G = L.Hq / L.Hkv;
     if (G < 1 || G > 8 || (G & (G - 1))) return hipErrorNotSupported;
+    if (ks > 1 && (!L.part_o || !L.part_ml)) return hipErrorInvalidValue;
+    hipError_t e;
     switch (L.D) {
-    case 64: return dispatch_pm<64>(a, L.qmode, L.q_bf16, s);
-    case 128: return dispatch_pm<128>(a, L.qmode, L.q_bf16, s);
-    case 256: return dispatch_pm<256>(a, L.qmode, L.q_bf16, s);
+    case 64: e = dispatch_pm<64>(a, L.qmode, L.q_bf16, s); break;
+    case 128: e = dispatch_pm<128>(a, L.qmode, L.q_bf16, s); break;
+    case 256: e = dispatch_pm<256>(a, L.qmode, L.q_bf16, s); break;
     default: return hipErrorNotSupported;
     }
+    if (e != hipSuccess || ks == 1) return e;
+    return launch_split_combine(L.D, L.part_o, L.part_ml, ks, (int64_t)L.B * L.Hq * L.Lq, L.out, L.out_bf16, s);
+}
+
+// Key-range splits of a prefill launch: enough workgroups for about two per
+// CU of the 256 (a chunk whose query tiles alone give fewer), each split
+// covering at least 8 key tiles (256 keys) of the n_slots upper bound, at most
+// 64.  1 when the query tiles already fill the part.  The same on every device,
+// so the workspace size can be queried without one.
+int prefill_kv_splits(int B, int Hq, int Hkv, int Lq, int S) {
+    const int G = Hq / Hkv;
+    if (G < 1) return 1;
+    const int QT = 16 * PF_WAVES / G;
+    const int64_t blocks = (int64_t)B * Hkv * ((Lq + QT - 1) / QT);
+    if (blocks >= 512) return 1;
+    int ks = (int)((512 + blocks - 1) / blocks);
+    const int by_len = (S + 8 * PF_BN - 1) / (8 * PF_BN);
+    if (ks > by_len) ks = by_len;
+    if (ks > 64) ks = 64;
+    return ks < 1 ? 1 : ks;
 }
 
 }  // namespace kvq

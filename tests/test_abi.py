@@ -146,3 +146,27 @@ def test_workspace_size(kvq):
     n = kvq.sdpa_decode_workspace_bytes(8, 32, 8, 8192, 128)
     assert n > 0 and n % (8 * 32 * 130 * 4) == 0
     assert kvq.sdpa_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
+
+
+def test_prefill_split_workspace(kvq):
+    """Key-split prefill: the workspace size follows the sizes only (0 when the
+    query tiles fill the part), and a missing or short workspace is rejected
+    before anything is enqueued."""
+    n = kvq.sdpa_prefill_split_workspace_bytes(1, 32, 8, 64, 16384, 128)
+    assert n > 0 and n % (1 * 32 * 64 * 130 * 4) == 0
+    assert kvq.sdpa_prefill_split_workspace_bytes(1, 32, 16, 2048, 131072, 256) == 0
+    assert kvq.sdpa_prefill_split_workspace_bytes(1, 4, 2, 16, 256, 64) == 0      # too few keys to split
+    assert kvq.sdpa_prefill_split_workspace_bytes(0, 32, 8, 64, 16384, 128) == 0
+    assert kvq.sdpa_prefill_split_workspace_bytes(1, 30, 8, 64, 16384, 128) == 0  # Hq % heads != 0
+    L = kvq.lib()
+    c, keep = _fake_cache(kvq, S=4096)
+    q = ctypes.c_void_p(c.codes)
+    need = kvq.sdpa_prefill_split_workspace_bytes(1, 4, 2, 8, 4096, 64)
+    assert need > 0
+    assert L.kvq_sdpa_prefill_split(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
+                                    None, 0, None, None) == 5
+    assert L.kvq_sdpa_prefill_split(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
+                                    q, need - 4, None, None) == 5
+    # the ordinary argument checks come first
+    assert L.kvq_sdpa_prefill_split(q, 1, 1, 3, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
+                                    None, 0, None, None) == 2
