@@ -338,6 +338,23 @@ def leg_long_prefill():
                                 "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4),
                                 "chunk_scatter_us": round(sc_ms * 1e3, 2),
                                 "chunk_scatter_gbs": round(sc_bytes / sc_ms / 1e6, 1)}
+    # shorter chunks over the same cache, ending at 65536: few query tiles,
+    # so the key range is split over workgroups (kvq_sdpa_prefill_split)
+    end = w.chunk_ends[0]
+    kvl = i32(end)
+    for Lq in (64, 256):
+        q = torch.randn((w.B, w.Hq, Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(kvq.sdpa_prefill_split_workspace_bytes(w.B, w.Hq, w.Hkv, Lq, w.S, w.D), 1),
+                         dtype=torch.uint8, device=DEV)
+        ms_one = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=5, inner=2)
+        ms_split = time_ms(lambda: kvq.sdpa_prefill_split(q, K, V, kv_len=kvl, causal=True, out=out,
+                                                          workspace=ws), iters=5, inner=2)
+        flops = 4.0 * w.D * w.Hq * (Lq * (end - Lq) + Lq * (Lq + 1) // 2)
+        res[f"short_chunk_lq{Lq}_kv_len_{end}"] = {
+            "prefill_ms": round(ms_one, 4), "tflops": round(flops / ms_one / 1e9, 1),
+            "split_prefill_ms": round(ms_split, 4), "split_tflops": round(flops / ms_split / 1e9, 1),
+            "split_mfma_frac": round(flops / ms_split / 1e9 / MFMA_F16_PEAK_TFLOPS, 4)}
     return res
 
 
