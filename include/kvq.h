@@ -266,7 +266,8 @@ kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, in
  * workgroups, and the splits' partial (max, sum, output) are merged per query
  * row afterwards, as in decode.  Arguments, bounds, masks, errors and result
  * as kvq_sdpa_prefill, within the same tolerance (the split changes the
- * summation order, so the bits may differ from it), plus:
+ * summation order, so the bits may differ from it; KVQ_NO_CAUSAL_SKIP is
+ * bit-identical to the default here too), plus:
  * workspace: device buffer, 16-byte aligned, of at least
  *   kvq_sdpa_prefill_split_workspace_bytes(B, Hq, heads, Lq, n_slots, D)
  *   bytes ([B*Hq*Lq, splits, D + 2] fp32 partials; no initialisation needed;

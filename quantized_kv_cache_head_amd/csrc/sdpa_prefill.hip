@@ -299,13 +299,14 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     const int64_t plane = ((int64_t)b * a.Hkv + g) * a.S;
     const uint8_t* kcodes = a.kc + plane * ROWB;
     const uint8_t* vcodes = a.vc + plane * ROWB;
-    // this workgroup's share of the key tiles below loop_end (all of them
-    // unless the key range is split over gridDim.y workgroups); t below
-    // counts tiles from t0
-    const int tiles_all = (loop_end + BN - 1) / BN;
-    const int per_split = (tiles_all + a.kv_splits - 1) / a.kv_splits;
+    // this workgroup's share of the key tiles (all of them unless the key
+    // range is split over gridDim.y workgroups), cut at loop_end; t below
+    // counts tiles from t0.  Split boundaries follow kv_len, not loop_end, so
+    // skipping the tiles past the causal bound changes no boundary and stays
+    // bit-identical to scanning them (they are fully masked and add 0).
+    const int per_split = ((kv_len + BN - 1) / BN + a.kv_splits - 1) / a.kv_splits;
     const int t0 = (int)blockIdx.y * per_split;
-    const int n_tiles = max(min(per_split, tiles_all - t0), 0);
+    const int n_tiles = max(min(per_split, (loop_end + BN - 1) / BN - t0), 0);
     const int diag_lo = qpos0 + r0;        // keys <= this are visible to every row of the tile
     const int lim = a.causal ? qpos0 + q_row : kv_len - 1;   // this column's last visible key
 

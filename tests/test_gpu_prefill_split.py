@@ -91,3 +91,22 @@ def test_split_prefill_small_workspace_raises():
     ws = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
     with pytest.raises(RuntimeError):
         kvq.sdpa_prefill_split(q, K[0], V[0], workspace=ws)
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.MXFP8_B32])
+def test_split_prefill_causal_skip_identity_and_fp32(qmode):
+    """Split boundaries follow kv_len, so scanning every tile below kv_len
+    (KVQ_NO_CAUSAL_SKIP) gives the same bits as stopping at the per-tile causal
+    bound; fp32 queries (hi + lo limbs) through the split path against the
+    oracle."""
+    B, Hkv, G, S, D, Lq, kv_len = 1, 2, 4, 4096, 128, 200, 3000
+    say(f"split prefill skip identity qmode={qmode}")
+    K, V = fill_caches(qmode, B, Hkv, S, D, kv_len, seed=12 + qmode)
+    q = _q(np.random.default_rng(13), B, Hkv * G, Lq, D)
+    assert torch.equal(_run(q, K, V, kv_len), _run(q, K, V, kv_len, no_causal_skip=True))
+    q32 = np.random.default_rng(14).standard_normal((B, Hkv * G, Lq, D)).astype(np.float32)
+    out = kvq.sdpa_prefill_split(torch.from_numpy(q32).to(DEV), K[0], V[0],
+                                 kv_len=torch.tensor([kv_len], dtype=torch.int32, device=DEV),
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attention(out, oracle.sdpa(q32, K[1], V[1], kv_len, causal=True), "fp32 q")
