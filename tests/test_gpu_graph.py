@@ -69,3 +69,51 @@ def test_step_graph_replays_match_eager():
         assert torch.equal(K.codes, eager_codes), f"replay {rep}: cache differs"
         assert torch.isfinite(junk.float()).all()
     assert np.isfinite(eager.float().cpu().numpy()).all()
+
+
+def test_split_prefill_graph_replays_match_eager():
+    """The key-split prefill (prefill launch + combine launch, caller
+    workspace) captured in a HIP graph: every replay, with eager work and
+    synchronizations between replays, equals the eager call bit for bit, also
+    after kv_len changes between replays."""
+    B, Hkv, G, S, D, Lq = 1, 2, 2, 4096, 128, 32
+    Hq = Hkv * G
+    say(f"graph split prefill Hq={Hq} Hkv={Hkv} S={S} D={D} Lq={Lq}")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(78)
+    K = kvq.Cache.empty(kvq.UINT4_TH, B, Hkv, S, D)
+    V = kvq.Cache.empty(kvq.UINT4_TH, B, Hkv, S, D)
+    x = torch.randn((B, Hkv, S, D), generator=gen, device=DEV).to(torch.bfloat16)
+    kvq.quant_scatter(x, torch.arange(S, dtype=torch.int32, device=DEV), K)
+    kvq.quant_scatter(x.flip(2).contiguous(), torch.arange(S, dtype=torch.int32, device=DEV), V)
+    q = torch.randn((B, Hq, Lq, D), generator=gen, device=DEV).to(torch.bfloat16)
+    kv_len = torch.tensor([3000], dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, Lq, D), dtype=torch.float32, device=DEV)
+    ws = torch.empty(kvq.sdpa_prefill_split_workspace_bytes(B, Hq, Hkv, Lq, S, D), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > 0
+
+    def call():
+        kvq.sdpa_prefill_split(q, K, V, kv_len=kv_len, out=out, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for n in (3000, 3000, 1800, 4096):
+        kv_len.fill_(n)
+        call()
+        torch.cuda.synchronize()
+        eager = out.clone()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay differs at kv_len {n}"
