@@ -217,3 +217,21 @@ def test_scatter_block_every_rounding_boundary(qmode, ocp):
         sc = 2.0 ** (sc - 127)
     assert np.all(sc == 1.0), "every block must have scale 1"
     assert_cache_equal(dc, hc, f"boundaries qmode {qmode}")
+
+
+@pytest.mark.parametrize("qmode", BLOCK)
+@pytest.mark.parametrize("D", [96, 160, 224, 8192])
+def test_scatter_block_other_head_dims(qmode, D):
+    """Block modes at head dims whose lanes per row (D / 8) are not a power of
+    two (the lane -> row mapping divides by it), and at the largest D."""
+    rng = np.random.default_rng(900 + D + qmode)
+    B, H, T, S = 2, 3, 11, 40
+    x = _inputs(rng, B, H, T, D, True)
+    slots = np.stack([rng.choice(S, T, replace=False) for _ in range(B)]).astype(np.int32)
+    slots[1, 4] = -1
+    say(f"scatter block qmode={qmode} D={D}")
+    dc, hc = new_pair(qmode, B, H, S, D)
+    kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, f"block qmode {qmode} D {D}")
