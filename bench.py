@@ -249,7 +249,10 @@ def leg_block_scatter():
                            ("mxfp4_ocp_scale", kvq.MXFP4_B32, kvq.MX_SCALE_OCP)):
         caches = [kvq.Cache.empty(mode, 1, 1, w.n_slots, w.d).sentinel_fill() for _ in range(8)]
         it = iter(range(10 ** 9))
-        ms = time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8], flags=fl), iters=10, inner=8)
+        # the faster of two timings: the first one after a new graph is
+        # sometimes slow
+        ms = min(time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8], flags=fl), iters=20, inner=8)
+                 for _ in range(2))
         rb = w.d // 2 if mode == kvq.MXFP4_B32 else w.d
         sb = (w.d // 32) * (1 if mode in kvq.E8M0_MODES else 4)
         nbytes = w.bs * 4 + valid * (w.d * 2 + rb + sb)
