@@ -526,7 +526,9 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
                           "tokens_per_step": tokens, "bytes": scatter_bytes(w),
-                          "note": "positions + one K+V quant-scatter launch for the new token"},
+                          "note": ("positions + one K+V quant-scatter launch for the 8 new tokens of the step: "
+                                   "launch-bound at this size; the 16384-token block scatter is "
+                                   "secondary.block_scatter_16384x128")},
         "roofline": {"bound": "hbm", "kernel": "kvq_sdpa_decode (sdpa_decode_split + sdpa_decode_combine)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
