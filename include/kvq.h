@@ -275,7 +275,7 @@ kvq_status kvq_sdpa_prefill_varlen(const void* q, int q_dtype, int B, int Hq, in
  *   when it is missing, misaligned or too small.  A size of 0 means the query
  *   tiles fill the part already: the call then runs as kvq_sdpa_prefill and
  *   workspace may be NULL.  The split count depends on the sizes only (about
- *   512 workgroups, at least 256 keys of n_slots per split, at most 64). */
+ *   256 workgroups, at least 256 keys of n_slots per split, at most 64). */
 size_t kvq_sdpa_prefill_split_workspace_bytes(int B, int Hq, int heads, int Lq, int n_slots, int D);
 kvq_status kvq_sdpa_prefill_split(const void* q, int q_dtype, int B, int Hq, int Lq,
                                   const kvq_cache* k, const kvq_cache* v,

@@ -759,18 +759,20 @@ hipError_t launch_sdpa_prefill(const PrefillLaunch& L, hipStream_t s) {
     return launch_split_combine(L.D, L.part_o, L.part_ml, ks, (int64_t)L.B * L.Hq * L.Lq, L.out, L.out_bf16, s);
 }
 
-// Key-range splits of a prefill launch: enough workgroups for about two per
-// CU of the 256 (a chunk whose query tiles alone give fewer), each split
-// covering at least 8 key tiles (256 keys) of the n_slots upper bound, at most
-// 64.  1 when the query tiles already fill the part.  The same on every device,
-// so the workspace size can be queried without one.
+// Key-range splits of a prefill launch: enough workgroups for one per CU of
+// the 256 -- one round, as the kernels keep one 8-wave workgroup per CU;
+// measured faster than two or more rounds, whose extra splits add partials
+// to write and merge -- for a chunk whose query tiles alone give fewer, each
+// split covering at least 8 key tiles (256 keys) of the n_slots upper bound,
+// at most 64.  1 when the query tiles already fill the part.  The same on
+// every device, so the workspace size can be queried without one.
 int prefill_kv_splits(int B, int Hq, int Hkv, int Lq, int S) {
     const int G = Hq / Hkv;
     if (G < 1) return 1;
     const int QT = 16 * PF_WAVES / G;
     const int64_t blocks = (int64_t)B * Hkv * ((Lq + QT - 1) / QT);
-    if (blocks >= 512) return 1;
-    int ks = (int)((512 + blocks - 1) / blocks);
+    if (blocks >= 256) return 1;
+    int ks = (int)((256 + blocks - 1) / blocks);
     const int by_len = (S + 8 * PF_BN - 1) / (8 * PF_BN);
     if (ks > by_len) ks = by_len;
     if (ks > 64) ks = 64;
