@@ -284,6 +284,17 @@ kvq_status kvq_sdpa_prefill_split(const void* q, int q_dtype, int B, int Hq, int
                                   void* workspace, size_t workspace_bytes,
                                   int32_t* err_flags, void* stream);
 
+/* kvq_sdpa_prefill_split with one filled length per batch row, as
+ * kvq_sdpa_prefill_varlen ([PR20351] kv_len bound per sequence): kv_lens is a
+ * device int32 array [B], each value clamped to [Lq, n_slots] with
+ * KVQ_FLAG_KVLEN; the same workspace size.  KVQ_ERR_NULL when kv_lens is NULL. */
+kvq_status kvq_sdpa_prefill_split_varlen(const void* q, int q_dtype, int B, int Hq, int Lq,
+                                         const kvq_cache* k, const kvq_cache* v,
+                                         const int32_t* kv_lens, const float* mask, int mask_is_causal,
+                                         unsigned flags, float sm_scale, void* out, int out_dtype,
+                                         void* workspace, size_t workspace_bytes,
+                                         int32_t* err_flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

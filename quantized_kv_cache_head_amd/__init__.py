@@ -42,6 +42,7 @@ EXPORTS = (
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
     "kvq_sdpa_prefill_varlen", "kvq_sdpa_prefill_split_workspace_bytes", "kvq_sdpa_prefill_split",
+    "kvq_sdpa_prefill_split_varlen",
 )
 
 
@@ -104,6 +105,8 @@ def lib():
         L.kvq_sdpa_prefill_split.restype = _I
         L.kvq_sdpa_prefill_split.argtypes = [_P, _I, _I, _I, _I, _CP, _CP, _P, _P, _I, ctypes.c_uint, _F, _P, _I,
                                              _P, _SZ, _P, _P]
+        L.kvq_sdpa_prefill_split_varlen.restype = _I
+        L.kvq_sdpa_prefill_split_varlen.argtypes = L.kvq_sdpa_prefill_split.argtypes
         _lib = L
     return _lib
 
@@ -349,6 +352,33 @@ def sdpa_prefill_split(q, k: Cache, v: Cache, kv_len=None, mask=None, causal=Tru
     kc, vc = k.struct(), v.struct()
     _check("kvq_sdpa_prefill_split", lib().kvq_sdpa_prefill_split(
         _ptr(q), _dtype_code(q), B, Hq, Lq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), _ptr(mask),
+        int(bool(causal)), NO_CAUSAL_SKIP if no_causal_skip else 0, float(sm_scale), _ptr(out),
+        _dtype_code(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_flags),
+        _stream(stream)))
+    return out
+
+
+def sdpa_prefill_split_varlen(q, k: Cache, v: Cache, kv_lens, mask=None, causal=True, sm_scale=None, out=None,
+                              out_dtype=None, no_causal_skip=False, workspace=None, err_flags=None, stream=None):
+    """kvq_sdpa_prefill_split_varlen: sdpa_prefill_split with kv_lens int32 [B] on the device."""
+    _need_cuda(q, kv_lens, mask, out, workspace, err_flags)
+    B, Hq, Lq, D = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if kv_lens.dtype != torch.int32 or kv_lens.numel() != B or not kv_lens.is_contiguous():
+        raise ValueError("kv_lens must be contiguous int32 [B]")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, Lq, D), dtype=out_dtype or q.dtype, device=q.device)
+    if mask is not None and (mask.dtype != torch.float32 or not mask.is_contiguous()):
+        raise ValueError("mask must be contiguous float32 [Lq, n_slots]")
+    if workspace is None:
+        nb = sdpa_prefill_split_workspace_bytes(B, Hq, k.H, Lq, k.S, D)
+        workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_prefill_split_varlen", lib().kvq_sdpa_prefill_split_varlen(
+        _ptr(q), _dtype_code(q), B, Hq, Lq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_lens), _ptr(mask),
         int(bool(causal)), NO_CAUSAL_SKIP if no_causal_skip else 0, float(sm_scale), _ptr(out),
         _dtype_code(out), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_flags),
         _stream(stream)))

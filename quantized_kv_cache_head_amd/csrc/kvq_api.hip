@@ -351,3 +351,13 @@ KVQ_API kvq_status kvq_sdpa_prefill_split(const void* q, int q_dtype, int B, int
     return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_len, 0, mask, mask_is_causal, flags, sm_scale, out,
                              out_dtype, true, workspace, workspace_bytes, err_flags, stream);
 }
+
+KVQ_API kvq_status kvq_sdpa_prefill_split_varlen(const void* q, int q_dtype, int B, int Hq, int Lq,
+                                                 const kvq_cache* k, const kvq_cache* v, const int32_t* kv_lens,
+                                                 const float* mask, int mask_is_causal, unsigned flags,
+                                                 float sm_scale, void* out, int out_dtype, void* workspace,
+                                                 size_t workspace_bytes, int32_t* err_flags, void* stream) {
+    if (!kv_lens) return KVQ_ERR_NULL;
+    return sdpa_prefill_impl(q, q_dtype, B, Hq, Lq, k, v, kv_lens, 1, mask, mask_is_causal, flags, sm_scale, out,
+                             out_dtype, true, workspace, workspace_bytes, err_flags, stream);
+}

@@ -167,6 +167,8 @@ def test_prefill_split_workspace(kvq):
                                     None, 0, None, None) == 5
     assert L.kvq_sdpa_prefill_split(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
                                     q, need - 4, None, None) == 5
+    assert L.kvq_sdpa_prefill_split_varlen(q, 1, 1, 4, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1,
+                                           q, 1, q, need, None, None) == 1      # kv_lens required
     # the ordinary argument checks come first
     assert L.kvq_sdpa_prefill_split(q, 1, 1, 3, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
                                     None, 0, None, None) == 2

@@ -129,3 +129,21 @@ def test_ring_sink_chunks(qmode, sink, window, chunks):
         assert np.array_equal(mask.cpu().numpy(), mask_ref)
         ref = oracle.sdpa(q, hK, hV, kv_len, mask=mask_ref, causal=False)
         check_attention(out, ref, f"chunk p0 {p0} T {T}")
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.MXFP4_B32])
+def test_prefill_split_varlen(qmode):
+    """Short chunks of a batch with one filled length per row, through the
+    key-split prefill: each row against the oracle on that row alone."""
+    B, Hkv, G, S, D, Lq = 3, 2, 2, 4096, 128, 24
+    kv_lens = np.array([24, 1500, 4000], np.int32)
+    assert kvq.sdpa_prefill_split_workspace_bytes(B, Hkv * G, Hkv, Lq, S, D) > 0
+    say(f"prefill split varlen qmode={qmode}")
+    K, V = fill_caches(qmode, B, Hkv, S, D, S, seed=440 + qmode)
+    q = wl.to_bf16_values(np.random.default_rng(441).standard_normal((B, Hkv * G, Lq, D)).astype(np.float32))
+    out = kvq.sdpa_prefill_split_varlen(dev_input(q, True), K[0], V[0], torch.from_numpy(kv_lens).to(DEV),
+                                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = oracle.sdpa(q[b:b + 1], _row_cache(K[1], b), _row_cache(V[1], b), int(kv_lens[b]), causal=True)
+        check_attention(out[b:b + 1], ref, f"b {b} kv_len {kv_lens[b]}")
