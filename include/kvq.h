@@ -186,11 +186,12 @@ kvq_status kvq_positions_full(const int32_t* start_pos, int T, int capacity,
 kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos,
                           int Lq, int sink_size, int window, float* mask_out, void* stream);
 
-/* Workspace bytes kvq_sdpa_decode needs for these sizes (partial softmax
- * states of the split-K pass).  It is an upper bound valid on any device and
- * for every cache mode (the split count of a launch depends on how
- * many workgroups the device keeps resident); needs no device.  0 on invalid
- * sizes. */
+/* Workspace bytes kvq_sdpa_decode needs for these sizes: a counter region
+ * (one 4-byte ticket per (batch, kv head), rounded up to 256 bytes), then the
+ * partial softmax states of the split-K pass.  It is an upper bound valid on
+ * any device and for every cache mode (the split count of a launch depends on
+ * how many workgroups the device keeps resident); needs no device.  0 on
+ * invalid sizes. */
 size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D);
 
 /* Decode attention (Lq = 1) over quantized K/V caches ([ABADDON]
@@ -198,19 +199,25 @@ size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int 
  * ring/sink caches):
  *   out[b, h, 0, :] = softmax_j(sm_scale * q[b,h,0,:] . k_hat[b,g,j,:] + mask[b,j]) v_hat[b,g,j,:]
  * over j in [0, kv_len), g = h / (Hq / Hkv), k_hat / v_hat dequantized on the
- * fly: (code - zp) * scale for the affine modes, decode(code) * scale of the
- * element's 32-element block for FP8E4M3_B32 and MXFP4_B32 (the read side of
- * [IQC]'s per-block write).  A row with no visible key gives 0.
+ * fly: (code - zp) * scale for the affine modes (INT8_TH, UINT4_TH),
+ * decode(code) * scale of the element's 32-element block for the five block
+ * modes (FP8E4M3_B32, FP8E5M2_B32, MXFP8_B32, MXFP4_B32, INT8_B32: the read
+ * side of [IQC]'s per-block write).  A slot at or past kv_len, or one the
+ * mask sets to -inf, takes no part at all (its codes and scales may hold any
+ * bytes, NaN included).  A row with no visible key gives 0.
  * q: [B, Hq, 1, D] (q_dtype); out: [B, Hq, 1, D] (out_dtype).
- * k, v: caches of one mode (any of the four) with equal sizes; Hq % heads == 0.
+ * k, v: caches of one mode (any of the seven) with equal sizes; Hq % heads == 0.
  * kv_len: device int32 scalar or NULL (= n_slots); a value outside
  *   [1, n_slots] is clamped and sets KVQ_FLAG_KVLEN.
  * mask: NULL or fp32 [B, n_slots] with batch stride mask_stride_b (0 shares
  *   one row); values 0 or -inf.  mask_is_causal is accepted for symmetry with
  *   prefill: at Lq = 1 the causal bound is kv_len itself.
- * workspace: device buffer of kvq_sdpa_decode_workspace_bytes() bytes for the
- *   per-split partial results (contents need no initialisation).  Calls that
- *   overlap in time (different streams) need separate workspaces.
+ * workspace: device buffer of kvq_sdpa_decode_workspace_bytes() bytes,
+ *   16-byte aligned.  Its counter region must be zero when a call starts;
+ *   every call leaves it zero, so zero-fill a new workspace once (and again
+ *   after writing anything else into it).  The rest holds per-split partial
+ *   results and needs no initialisation.  Calls that overlap in time
+ *   (different streams) need separate workspaces.
  * Supported D: 64, 128, 256; Hq / heads in {1, 2, 4, 8}. */
 kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
                            const kvq_cache* k, const kvq_cache* v,

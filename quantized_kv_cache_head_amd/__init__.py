@@ -18,8 +18,7 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# KVQ_LIB may name another build of the same library (e.g. a tuning variant)
-LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 # kvq_qmode
 INT8_TH, UINT4_TH, FP8E4M3_B32, MXFP4_B32 = 0, 1, 2, 3

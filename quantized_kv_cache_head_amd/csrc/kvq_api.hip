@@ -186,9 +186,13 @@ kvq_status check_attention(const void* q, int q_dtype, int B, int Hq, const kvq_
     return KVQ_OK;
 }
 
-// Partial outputs [B, Hq, splits, D] and (m, l) [B, Hq, splits, 2], fp32.
-size_t decode_ws_bytes(int B, int Hq, int Hkv, int splits, int D) {
-    (void)Hkv;
+// Decode workspace: a counter region (one ticket per (b, kv head), which the
+// single-pass kernel needs at zero when a call starts and leaves at zero),
+// then the per-split partials, fp32: (m, l) and o for every (b, kv head,
+// split, query head of the group).
+size_t decode_ctr_bytes(int B, int Hkv) { return ((size_t)B * Hkv * sizeof(unsigned) + 255) / 256 * 256; }
+
+size_t decode_part_bytes(int B, int Hq, int splits, int D) {
     return (size_t)B * Hq * splits * ((size_t)D + 2) * sizeof(float);
 }
 
@@ -202,7 +206,13 @@ int decode_splits_any(int B, int Hq, int Hkv, int S, int D) {
 
 KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int D) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16 || Hq % Hkv) return 0;
-    return decode_ws_bytes(B, Hq, Hkv, decode_splits_any(B, Hq, Hkv, n_slots, D), D);
+    size_t part = decode_part_bytes(B, Hq, decode_splits_any(B, Hq, Hkv, n_slots, D), D);
+    const int G = Hq / Hkv;
+    if (kvq::stream_supported(KVQ_INT8_TH, D, G, n_slots)) {
+        const size_t ps = decode_part_bytes(B, Hq, kvq::stream_splits_max(B, Hkv, n_slots, D, G), D);
+        if (ps > part) part = ps;
+    }
+    return decode_ctr_bytes(B, Hkv) + part;
 }
 
 namespace {
@@ -215,8 +225,12 @@ kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq
     if (st != KVQ_OK) return st;
     if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
     const int D = k->head_dim;
-    const int nsplit = kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
-    const size_t need = decode_ws_bytes(B, Hq, k->heads, nsplit, D);
+    const int G = Hq / k->heads;
+    const bool single = kvq::stream_supported(k->qmode, D, G, k->n_slots) && aligned(k->zps, 4) && aligned(v->zps, 4);
+    const int nsplit = single ? kvq::stream_splits(B, k->heads, k->n_slots, D, G, q_dtype == KVQ_BF16)
+                              : kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
+    const size_t ctr = decode_ctr_bytes(B, k->heads);
+    const size_t need = ctr + decode_part_bytes(B, Hq, nsplit, D);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
     kvq::DecodeLaunch L;
     L.q = q;
@@ -241,9 +255,16 @@ kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq
     L.out = out;
     L.out_bf16 = out_dtype == KVQ_BF16;
     L.nsplit = nsplit;
-    L.part_o = reinterpret_cast<float*>(workspace);
-    L.part_ml = L.part_o + (size_t)B * Hq * nsplit * D;
     L.err = err_flags;
+    L.ctr = reinterpret_cast<unsigned*>(workspace);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
+    if (single) {
+        L.part_ml = part;
+        L.part_o = part + (size_t)B * Hq * nsplit * 2;
+        return from_hip(kvq::launch_sdpa_decode_stream(L, reinterpret_cast<hipStream_t>(stream)));
+    }
+    L.part_o = part;
+    L.part_ml = L.part_o + (size_t)B * Hq * nsplit * D;
     return from_hip(kvq::launch_sdpa_decode(L, reinterpret_cast<hipStream_t>(stream)));
 }
 

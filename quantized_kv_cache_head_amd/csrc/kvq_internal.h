@@ -53,11 +53,19 @@ struct DecodeLaunch {
     float* part_o;
     float* part_ml;
     int32_t* err;
+    unsigned* ctr = nullptr;   // single-pass kernel: per-plane tickets (zero between calls)
 };
 
 int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode);
 int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16);
 hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s);
+
+// Single-pass decode with the split merge in the same launch (int8
+// per-token-head caches): which requests it runs, its split count, launch.
+bool stream_supported(int qmode, int D, int G, int S);
+int stream_splits_max(int B, int Hkv, int S, int D, int G);
+int stream_splits(int B, int Hkv, int S, int D, int G, bool qbf16);
+hipError_t launch_sdpa_decode_stream(const DecodeLaunch& L, hipStream_t s);
 
 struct PrefillLaunch {
     const void* q;

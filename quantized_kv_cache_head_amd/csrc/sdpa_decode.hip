@@ -669,7 +669,8 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
                 if (i < n) {
 #pragma unroll
                     for (int hx = 0; hx < HPW; ++hx) {
-                        const float sc = fmaf(dv[u][hx], mt[u].x, mt[u].y);
+                        // a masked row is -inf whatever its (possibly unwritten) scale holds
+                        const float sc = mt[u].y == NEG_INF ? NEG_INF : fmaf(dv[u][hx], mt[u].x, mt[u].y);
                         s_row[i * G + h_first + hx] = sc;
                         mloc[hx] = fmaxf(mloc[hx], sc);
                     }
@@ -712,7 +713,7 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
 #pragma unroll
                     for (int hx = 0; hx < HPW; ++hx) {
                         const float p = __builtin_amdgcn_exp2f(sv[u][hx] - msafe[hx]);
-                        const float pv = p * mt[u].x;
+                        const float pv = p == 0.0f ? 0.0f : p * mt[u].x;   // a dropped row adds exactly 0
                         lsum[hx] += p;
                         csum[hx] = fmaf(pv, mt[u].y, csum[hx]);
                         s_row[i * G + h_first + hx] = pv;
@@ -759,7 +760,10 @@ __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
         const int ic = min(i, i_last);
         float pv[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) pv[hh] = s_row[ic * G + hh] * live;
+        for (int hh = 0; hh < G; ++hh) {
+            const float w = s_row[ic * G + hh];
+            pv[hh] = w == 0.0f ? 0.0f : w * live;      // a dropped row adds exactly 0, whatever its scale
+        }
 #pragma unroll
         for (int hh = 0; hh < G; ++hh)
 #pragma unroll

@@ -567,8 +567,11 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 float v = st[kb][i] * cv[i];
                 if (tile_mask) {
                     const int key = j0 + kb * 16 + 4 * lg + i;
-                    if (has_mask && key < kv_len && q_live)
-                        v += a.mask[(int64_t)q_row * a.S + key] * 1.4426950408889634f;
+                    if (has_mask && key < kv_len && q_live) {
+                        // a masked key is -inf whatever its (possibly unwritten) scale holds
+                        const float mv = a.mask[(int64_t)q_row * a.S + key];
+                        v = mv == NEG_INF ? NEG_INF : v + mv * 1.4426950408889634f;
+                    }
                     if (key > lim || key >= kv_len || !q_live) v = NEG_INF;
                 }
                 sv8[kb * 4 + i] = v;
@@ -606,7 +609,9 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             const float svv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                const float pv0 = p8[e] * svv[e], pv1 = p8[e + 1] * svv[e + 1];
+                // a dropped key (p = 0) adds exactly 0, whatever its scale holds
+                const float pv0 = p8[e] == 0.0f ? 0.0f : p8[e] * svv[e];
+                const float pv1 = p8[e + 1] == 0.0f ? 0.0f : p8[e + 1] * svv[e + 1];
                 const half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv0, pv1));
                 pb[0][e] = h2[0];
                 pb[0][e + 1] = h2[1];

@@ -143,8 +143,12 @@ def test_host_validation_errors(kvq):
 
 
 def test_workspace_size(kvq):
+    """A counter region (one 4-byte ticket per (b, kv head), rounded up to
+    256 bytes) followed by whole per-split partials of (D + 2) fp32 values
+    per (b, query head)."""
     n = kvq.sdpa_decode_workspace_bytes(8, 32, 8, 8192, 128)
-    assert n > 0 and n % (8 * 32 * 130 * 4) == 0
+    ctr = -(-8 * 8 * 4 // 256) * 256
+    assert n > ctr and (n - ctr) % (8 * 32 * 130 * 4) == 0
     assert kvq.sdpa_decode_workspace_bytes(0, 32, 8, 8192, 128) == 0
 
 
