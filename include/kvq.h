@@ -238,6 +238,28 @@ kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int Hq,
                                   void* workspace, size_t workspace_bytes,
                                   int32_t* err_flags, void* stream);
 
+/* kvq_sdpa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results as kvq_sdpa_decode, without the
+ * workspace arguments.  The counters and partials live in one library-owned
+ * device array per GPU of KVQ_DECODE_NOALLOC_BYTES bytes (a fixed counter
+ * block of KVQ_DECODE_NOALLOC_CTR_BYTES, then the partials), placed with the
+ * code object and held until the process ends.  The first call on a device,
+ * with that device current, looks up the array's address and enqueues a
+ * clear of the counter block on `stream`; no call allocates, frees or calls
+ * an allocating routine.  KVQ_ERR_WORKSPACE, with nothing enqueued, when the
+ * call needs more: B * heads tickets above the counter block, or partials
+ * above the rest (at D = 128, Hq = 32 every shape fits).  Every call on one
+ * GPU shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; order them. */
+#define KVQ_DECODE_NOALLOC_BYTES (16u << 20)
+#define KVQ_DECODE_NOALLOC_CTR_BYTES (64u << 10)
+kvq_status kvq_sdpa_decode_noalloc(const void* q, int q_dtype, int B, int Hq,
+                                   const kvq_cache* k, const kvq_cache* v,
+                                   const int32_t* kv_len, const float* mask, int64_t mask_stride_b,
+                                   int mask_is_causal, float sm_scale, void* out, int out_dtype,
+                                   int32_t* err_flags, void* stream);
+
 /* Chunked-prefill attention over quantized K/V caches ([PR20351]): the Lq
  * query rows sit at positions [kv_len - Lq, kv_len); row r attends keys
  * j < kv_len, and when mask_is_causal only j <= kv_len - Lq + r.  The KV loop

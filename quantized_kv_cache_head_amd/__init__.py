@@ -41,7 +41,7 @@ EXPORTS = (
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
     "kvq_sdpa_prefill_varlen", "kvq_sdpa_prefill_split_workspace_bytes", "kvq_sdpa_prefill_split",
-    "kvq_sdpa_prefill_split_varlen",
+    "kvq_sdpa_prefill_split_varlen", "kvq_sdpa_decode_noalloc",
 )
 
 
@@ -92,6 +92,8 @@ def lib():
         L.kvq_sdpa_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.kvq_sdpa_decode.restype = _I
         L.kvq_sdpa_decode.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _SZ, _P, _P]
+        L.kvq_sdpa_decode_noalloc.restype = _I
+        L.kvq_sdpa_decode_noalloc.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _P]
         L.kvq_sdpa_prefill.restype = _I
         L.kvq_sdpa_prefill.argtypes = [_P, _I, _I, _I, _I, _CP, _CP, _P, _P, _I, ctypes.c_uint, _F, _P, _I, _P, _P]
         L.kvq_sdpa_decode_varlen.restype = _I
@@ -302,6 +304,31 @@ def sdpa_decode(q, k: Cache, v: Cache, kv_len=None, mask=None, sm_scale=None, ou
         _ptr(q), _dtype_code(q), B, Hq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), _ptr(mask), msb,
         int(bool(mask_is_causal)), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(err_flags), _stream(stream)))
+    return out
+
+
+def sdpa_decode_noalloc(q, k: Cache, v: Cache, kv_len=None, mask=None, sm_scale=None, out=None,
+                        out_dtype=None, err_flags=None, mask_is_causal=False, stream=None):
+    """kvq_sdpa_decode_noalloc: kvq_sdpa_decode on the library's own per-GPU
+    scratch array (no workspace); allocates only `out` when it is None."""
+    _need_cuda(q, kv_len, mask, out, err_flags)
+    B, Hq, Lq, D = q.shape
+    if Lq != 1 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 1, D]")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    msb = 0
+    if mask is not None:
+        if mask.dtype != torch.float32 or not mask.is_contiguous():
+            raise ValueError("mask must be contiguous float32 [n_slots] or [B, n_slots]")
+        msb = 0 if mask.dim() == 1 or mask.shape[0] == 1 else mask.stride(0)
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_decode_noalloc", lib().kvq_sdpa_decode_noalloc(
+        _ptr(q), _dtype_code(q), B, Hq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), _ptr(mask), msb,
+        int(bool(mask_is_causal)), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(err_flags),
+        _stream(stream)))
     return out
 
 

@@ -3,11 +3,15 @@
 // Every entry point validates on the host and returns a kvq_status without
 // enqueuing anything when an argument is rejected; otherwise it enqueues on
 // the caller's stream and returns without synchronizing.  The library never
-// allocates device memory.  Unsupported-but-valid requests are rejected with
-// KVQ_ERR_UNSUPPORTED rather than run in a degraded form (pytorch/executorch
+// allocates device memory; the one device array it owns is the fixed-size
+// scratch of kvq_sdpa_decode_noalloc, placed with the code object.
+// Unsupported-but-valid requests are rejected with KVQ_ERR_UNSUPPORTED rather
+// than run in a degraded form (pytorch/executorch
 // PR 24473, Summary: caches that cannot be run are rejected, never flattened).
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
+
+#include <mutex>
 
 #define KVQ_API extern "C" __attribute__((visibility("default")))
 
@@ -217,21 +221,32 @@ KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slo
 
 namespace {
 
-kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v,
-                            const int32_t* kv_len, int kv_len_sb, const float* mask, int64_t mask_stride_b,
-                            float sm_scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
-                            int32_t* err_flags, void* stream) {
-    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
-    if (st != KVQ_OK) return st;
-    if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
+// Split count and partial bytes of one decode call: the single-pass int8
+// kernel where it applies (its ticket counters live in the counter region),
+// else the split pass plus combine kernel.
+struct DecodePlan {
+    bool single;
+    int nsplit;
+    size_t part_bytes;
+};
+
+DecodePlan decode_plan(int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v) {
     const int D = k->head_dim;
     const int G = Hq / k->heads;
-    const bool single = kvq::stream_supported(k->qmode, D, G, k->n_slots) && aligned(k->zps, 4) && aligned(v->zps, 4);
-    const int nsplit = single ? kvq::stream_splits(B, k->heads, k->n_slots, D, G, q_dtype == KVQ_BF16)
-                              : kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
-    const size_t ctr = decode_ctr_bytes(B, k->heads);
-    const size_t need = ctr + decode_part_bytes(B, Hq, nsplit, D);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
+    DecodePlan p;
+    p.single = kvq::stream_supported(k->qmode, D, G, k->n_slots) && aligned(k->zps, 4) && aligned(v->zps, 4);
+    p.nsplit = p.single ? kvq::stream_splits(B, k->heads, k->n_slots, D, G, q_dtype == KVQ_BF16)
+                        : kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
+    p.part_bytes = decode_part_bytes(B, Hq, p.nsplit, D);
+    return p;
+}
+
+// Enqueue a validated decode call: ctr holds one zero ticket per (b, kv
+// head), part at least plan.part_bytes bytes (16-byte aligned).
+kvq_status sdpa_decode_enqueue(const DecodePlan& plan, const void* q, int q_dtype, int B, int Hq,
+                               const kvq_cache* k, const kvq_cache* v, const int32_t* kv_len, int kv_len_sb,
+                               const float* mask, int64_t mask_stride_b, float sm_scale, void* out, int out_dtype,
+                               unsigned* ctr, float* part, int32_t* err_flags, void* stream) {
     kvq::DecodeLaunch L;
     L.q = q;
     L.q_bf16 = q_dtype == KVQ_BF16;
@@ -239,7 +254,7 @@ kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq
     L.Hq = Hq;
     L.Hkv = k->heads;
     L.S = k->n_slots;
-    L.D = D;
+    L.D = k->head_dim;
     L.qmode = k->qmode;
     L.kc = reinterpret_cast<const uint8_t*>(k->codes);
     L.ks = reinterpret_cast<const float*>(k->scales);
@@ -254,18 +269,32 @@ kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq
     L.sm_scale = sm_scale;
     L.out = out;
     L.out_bf16 = out_dtype == KVQ_BF16;
-    L.nsplit = nsplit;
+    L.nsplit = plan.nsplit;
     L.err = err_flags;
-    L.ctr = reinterpret_cast<unsigned*>(workspace);
-    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
-    if (single) {
+    L.ctr = ctr;
+    if (plan.single) {
         L.part_ml = part;
-        L.part_o = part + (size_t)B * Hq * nsplit * 2;
+        L.part_o = part + (size_t)B * Hq * plan.nsplit * 2;
         return from_hip(kvq::launch_sdpa_decode_stream(L, reinterpret_cast<hipStream_t>(stream)));
     }
     L.part_o = part;
-    L.part_ml = L.part_o + (size_t)B * Hq * nsplit * D;
+    L.part_ml = L.part_o + (size_t)B * Hq * plan.nsplit * L.D;
     return from_hip(kvq::launch_sdpa_decode(L, reinterpret_cast<hipStream_t>(stream)));
+}
+
+kvq_status sdpa_decode_impl(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k, const kvq_cache* v,
+                            const int32_t* kv_len, int kv_len_sb, const float* mask, int64_t mask_stride_b,
+                            float sm_scale, void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                            int32_t* err_flags, void* stream) {
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
+    if (st != KVQ_OK) return st;
+    if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
+    const DecodePlan plan = decode_plan(q_dtype, B, Hq, k, v);
+    const size_t ctr = decode_ctr_bytes(B, k->heads);
+    if (!workspace || workspace_bytes < ctr + plan.part_bytes || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
+    return sdpa_decode_enqueue(plan, q, q_dtype, B, Hq, k, v, kv_len, kv_len_sb, mask, mask_stride_b, sm_scale,
+                               out, out_dtype, reinterpret_cast<unsigned*>(workspace),
+                               reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr), err_flags, stream);
 }
 
 // Bytes of a key-split prefill's partials: [B * Hq * Lq, splits, D + 2] fp32.
@@ -340,6 +369,68 @@ KVQ_API kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int
     if (!kv_lens) return KVQ_ERR_NULL;
     return sdpa_decode_impl(q, q_dtype, B, Hq, k, v, kv_lens, 1, mask, mask_stride_b, sm_scale, out, out_dtype,
                             workspace, workspace_bytes, err_flags, stream);
+}
+
+// ---- decode without a caller workspace --------------------------------------
+// One array per GPU, placed with the code object and held until the process
+// ends: a fixed block of ticket counters, then the partials.  The counter
+// block has a fixed size and offset, so partial bytes of a call of one shape
+// never land where a later call of another shape expects zero tickets.
+static __device__ __align__(256) unsigned char scratch[KVQ_DECODE_NOALLOC_BYTES];
+
+namespace {
+
+constexpr size_t kScratchCtrBytes = KVQ_DECODE_NOALLOC_CTR_BYTES;
+constexpr size_t kScratchPartBytes = KVQ_DECODE_NOALLOC_BYTES - KVQ_DECODE_NOALLOC_CTR_BYTES;
+constexpr int kMaxDevices = 64;
+static_assert(kScratchCtrBytes % 256 == 0 && kScratchPartBytes > 0, "scratch layout");
+
+__global__ void zero_words(unsigned* p, unsigned n) {
+    for (unsigned i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.  The first call on a
+// device looks it up (the array's host-side name is no device address) and
+// clears the counter block on the caller's stream; every decode launch
+// leaves its tickets at zero again.
+kvq_status device_scratch(hipStream_t stream, char** base) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVQ_ERR_LAUNCH;
+        hipLaunchKernelGGL(zero_words, dim3(16), dim3(256), 0, stream, reinterpret_cast<unsigned*>(ptr),
+                           static_cast<unsigned>(kScratchCtrBytes / sizeof(unsigned)));
+        if (hipGetLastError() != hipSuccess) return KVQ_ERR_LAUNCH;
+        g_scratch[dev] = ptr;
+    }
+    *base = static_cast<char*>(g_scratch[dev]);
+    return KVQ_OK;
+}
+
+}  // namespace
+
+KVQ_API kvq_status kvq_sdpa_decode_noalloc(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
+                                           const kvq_cache* v, const int32_t* kv_len, const float* mask,
+                                           int64_t mask_stride_b, int mask_is_causal, float sm_scale, void* out,
+                                           int out_dtype, int32_t* err_flags, void* stream) {
+    (void)mask_is_causal;
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
+    if (st != KVQ_OK) return st;
+    if (mask_stride_b < 0) return KVQ_ERR_SHAPE;
+    if ((size_t)B * k->heads * sizeof(unsigned) > kScratchCtrBytes) return KVQ_ERR_WORKSPACE;
+    const DecodePlan plan = decode_plan(q_dtype, B, Hq, k, v);
+    if (plan.part_bytes > kScratchPartBytes) return KVQ_ERR_WORKSPACE;
+    char* base = nullptr;
+    st = device_scratch(reinterpret_cast<hipStream_t>(stream), &base);
+    if (st != KVQ_OK) return st;
+    return sdpa_decode_enqueue(plan, q, q_dtype, B, Hq, k, v, kv_len, 0, mask, mask_stride_b, sm_scale, out,
+                               out_dtype, reinterpret_cast<unsigned*>(base),
+                               reinterpret_cast<float*>(base + kScratchCtrBytes), err_flags, stream);
 }
 
 KVQ_API kvq_status kvq_sdpa_prefill(const void* q, int q_dtype, int B, int Hq, int Lq, const kvq_cache* k,

@@ -71,6 +71,25 @@ def _fake_cache(kvq, qmode=0, B=1, H=2, S=64, D=64, zps=True):
     return c, buf
 
 
+def test_noalloc_decode_validation(kvq):
+    """kvq_sdpa_decode_noalloc rejects on the host, before it touches the
+    device: bad shapes as kvq_sdpa_decode does, and more tickets than its
+    fixed counter block holds (B * heads above 16384) as a workspace error."""
+    L = kvq.lib()
+    c, keep = _fake_cache(kvq)
+    q = ctypes.c_void_p(c.codes)
+    s = None
+    assert L.kvq_sdpa_decode_noalloc(q, 1, 1, 3, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
+                                     None, s) == 2
+    assert L.kvq_sdpa_decode_noalloc(q, 1, 1, 4, ctypes.byref(c), ctypes.byref(c), None, None, -1, 0, 0.1, q, 1,
+                                     None, s) == 2
+    assert L.kvq_sdpa_decode_noalloc(None, 1, 1, 4, ctypes.byref(c), ctypes.byref(c), None, None, 0, 0, 0.1, q, 1,
+                                     None, s) == 1
+    big, keep2 = _fake_cache(kvq, B=4096, H=8)
+    assert L.kvq_sdpa_decode_noalloc(q, 1, 4096, 32, ctypes.byref(big), ctypes.byref(big), None, None, 0, 0, 0.1,
+                                     q, 1, None, s) == 5
+
+
 def test_host_validation_errors(kvq):
     L = kvq.lib()
     c, keep = _fake_cache(kvq)
