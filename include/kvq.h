@@ -182,7 +182,9 @@ kvq_status kvq_positions_full(const int32_t* start_pos, int T, int capacity,
  * additive float mask): mask_out[r, s] (fp32 [Lq, n_slots]) is 0 when the
  * slot's position cp = cache_positions[s] is visible to query position
  * qp = *start_pos + r, i.e. cp >= 0, cp <= qp and (cp < sink_size or
- * qp - cp < window), and -inf otherwise. */
+ * qp - cp < window), and -inf otherwise.  KVQ_ERR_SHAPE unless
+ * sink_size + window == n_slots (the cache is its sink plus its window; a
+ * full-context cache is sink_size 0, window n_slots). */
 kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos,
                           int Lq, int sink_size, int window, float* mask_out, void* stream);
 

@@ -161,6 +161,8 @@ KVQ_API kvq_status kvq_positions_full(const int32_t* start_pos, int T, int capac
 KVQ_API kvq_status kvq_build_mask(const int32_t* cache_positions, int n_slots, const int32_t* start_pos, int Lq,
                                   int sink_size, int window, float* mask_out, void* stream) {
     if (n_slots < 1 || Lq < 0 || sink_size < 0 || window < 1) return KVQ_ERR_SHAPE;
+    // the cache holds the sink slots and the window, nothing else
+    if ((int64_t)sink_size + window != n_slots) return KVQ_ERR_SHAPE;
     if (Lq == 0) return KVQ_OK;
     if (!cache_positions || !start_pos || !mask_out) return KVQ_ERR_NULL;
     return from_hip(kvq::launch_build_mask(cache_positions, n_slots, start_pos, Lq, sink_size, window, mask_out,

@@ -19,9 +19,13 @@
 //    cooperatively, into LDS.
 //  * Pass 1 (q . k): a K row is split over CK lanes of KB bytes each; codes
 //    become exact fp16 integers (code - zp) (a byte permute under the fp16
-//    exponent of 1024, then one packed fp16 subtraction) and meet q (rescaled
-//    by a power of two into fp16 range, exact for bf16 q; fp32 q uses a
-//    hi + lo pair of fp16 limbs) in v_dot2_f32_f16 with fp32 accumulation.
+//    exponent of 1024, then one packed fp16 subtraction) and meet q in
+//    v_dot2_f32_f16 with fp32 accumulation.  q is rescaled by one power of
+//    two for the G heads so that max|q| lies in [2^-8, 2^15); a bf16 element
+//    is then exact in fp16 when it is at least 2^-17 after the rescale (at
+//    worst 2^-9 of max|q|); a smaller one rounds on fp16's subnormal grid,
+//    an error below 2^-25, i.e. 2^-17 of max|q|.  fp32 q uses a hi + lo pair
+//    of fp16 limbs.
 //    Row dots go to LDS.  The codes stream through a register ring of PD
 //    steps that is refilled right after each slot is converted.
 //  * Middle pass (per head, from LDS): score = dot * scale_k * sm_scale *

@@ -21,8 +21,10 @@
 //    [d][key] in the key order in which the S^T accumulator hands P to the
 //    PV MFMA.  Per-key scales fold into the softmax (K) and into P (V), so
 //    dequantization adds no rounding.
-//  * q is rescaled by a power of two so fp16 holds it (exact for bf16 input);
-//    fp32 input uses hi + lo fp16 limbs.  P * scale_v enters the PV MFMA as
+//  * q is rescaled by a power of two that puts max|q| of the tile in
+//    [2^14, 2^15); a bf16 element is exact in fp16 unless it lies more than
+//    2^31 below that maximum (it then rounds on fp16's subnormal grid, an
+//    error below 2^-39 of max|q|).  fp32 input uses hi + lo fp16 limbs.  P * scale_v enters the PV MFMA as
 //    hi + lo fp16 limbs.
 //  * Online softmax in the log2 domain with lazy rescaling (only when a
 //    column's max grows by more than 8).

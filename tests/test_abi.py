@@ -126,6 +126,10 @@ def test_host_validation_errors(kvq):
     assert L.kvq_positions_full(None, 4, 0, None, None, None, s) == 2
     assert L.kvq_positions_full(None, 4, 16, None, None, None, s) == 1
     assert L.kvq_build_mask(None, 0, None, 1, 0, 4, None, s) == 2
+    # the cache must be exactly its sink plus its window
+    assert L.kvq_build_mask(None, 16, None, 1, 4, 8, None, s) == 2
+    assert L.kvq_build_mask(None, 16, None, 1, 0, 17, None, s) == 2
+    assert L.kvq_build_mask(None, 12, None, 0, 4, 8, None, s) == 0
     # block-mode caches pass validation (decode stops at the missing workspace)
     cb, keep3 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
     q = ctypes.c_void_p(c.codes)

@@ -93,6 +93,29 @@ def test_decode_query_magnitudes():
         check_attention(run_decode(q, K, V, 300, out_dtype=torch.float32, sm=sm), ref, f"|q| {mag}")
 
 
+def wide_range_q(rng, shape, lo=-20.0, hi=3.0):
+    """q whose elements inside one vector span 2^lo .. 2^hi (log-uniform
+    magnitudes, random signs), bf16-exact: the per-vector rescale of q can
+    hold the largest elements exactly but not the smallest."""
+    mag = np.exp2(rng.uniform(lo, hi, shape))
+    sgn = np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    return wl.to_bf16_values((mag * sgn).astype(np.float32))
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32])
+@pytest.mark.parametrize("q_bf16", [True, False])
+def test_decode_query_wide_range_in_vector(qmode, q_bf16):
+    """One q vector whose elements span 23 binades: the small elements lose
+    bits in the rescaled form of q, which must stay inside the gate."""
+    B, Hkv, G, S, D = 2, 2, 4, 700, 128
+    K, V = fill_caches(qmode, B, Hkv, S, D, 700, seed=81)
+    q = wide_range_q(np.random.default_rng(82), (B, Hkv * G, 1, D))
+    say(f"decode wide-range q qmode {qmode} bf16 {q_bf16}")
+    ref = oracle.sdpa(q, K[1], V[1], 611)
+    for od in (torch.bfloat16, torch.float32):
+        check_attention(run_decode(q, K, V, 611, q_bf16=q_bf16, out_dtype=od), ref, f"wide q {od}")
+
+
 def test_decode_mask_and_identities():
     B, Hkv, G, S, D = 2, 2, 4, 1024, 128
     K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, 1024, seed=11)

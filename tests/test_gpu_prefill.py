@@ -9,7 +9,7 @@ import oracle
 import quantized_kv_cache_head_amd as kvq
 import quantized_kv_cache_head_amd.workloads as wl
 from _gpu import DEV, check_attention, dev_input, say
-from test_gpu_decode import fill_caches
+from test_gpu_decode import fill_caches, wide_range_q
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,14 @@ def test_prefill_lq1_matches_decode():
     ref = oracle.sdpa(q, K[1], V[1], 777)
     check_attention(run_prefill(q, K, V, 777, out_dtype=torch.float32), ref, "prefill Lq1")
     assert torch.equal(run_prefill(q, K, V, 777, causal=True), run_prefill(q, K, V, 777, causal=False))
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH, kvq.MXFP4_B32])
+def test_prefill_query_wide_range_in_vector(qmode):
+    """q rows whose elements span 23 binades inside one vector."""
+    B, Hkv, G, S, D, Lq = 1, 2, 2, 512, 128, 48
+    K, V = fill_caches(qmode, B, Hkv, S, D, 400, seed=91)
+    q = wide_range_q(np.random.default_rng(92), (B, Hkv * G, Lq, D))
+    say(f"prefill wide-range q qmode {qmode}")
+    ref = oracle.sdpa(q, K[1], V[1], 400, causal=True)
+    check_attention(run_prefill(q, K, V, 400, out_dtype=torch.float32), ref, "wide q prefill")
