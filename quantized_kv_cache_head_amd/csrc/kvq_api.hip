@@ -214,8 +214,8 @@ KVQ_API size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slo
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || n_slots <= 0 || D <= 0 || D % 16 || Hq % Hkv) return 0;
     size_t part = decode_part_bytes(B, Hq, decode_splits_any(B, Hq, Hkv, n_slots, D), D);
     const int G = Hq / Hkv;
-    if (kvq::stream_supported(KVQ_INT8_TH, D, G, n_slots)) {
-        const size_t ps = decode_part_bytes(B, Hq, kvq::stream_splits_max(B, Hkv, n_slots, D, G), D);
+    if (kvq::mfma_supported(KVQ_INT8_TH, D, G, n_slots)) {
+        const size_t ps = decode_part_bytes(B, Hq, kvq::mfma_splits_max(B, Hkv, n_slots, D, G), D);
         if (ps > part) part = ps;
     }
     return decode_ctr_bytes(B, Hkv) + part;
@@ -236,8 +236,8 @@ DecodePlan decode_plan(int q_dtype, int B, int Hq, const kvq_cache* k, const kvq
     const int D = k->head_dim;
     const int G = Hq / k->heads;
     DecodePlan p;
-    p.single = kvq::stream_supported(k->qmode, D, G, k->n_slots) && aligned(k->zps, 4) && aligned(v->zps, 4);
-    p.nsplit = p.single ? kvq::stream_splits(B, k->heads, k->n_slots, D, G, q_dtype == KVQ_BF16)
+    p.single = kvq::mfma_supported(k->qmode, D, G, k->n_slots) && aligned(k->zps, 4) && aligned(v->zps, 4);
+    p.nsplit = p.single ? kvq::mfma_splits(B, k->heads, k->n_slots, D, G, q_dtype == KVQ_BF16)
                         : kvq::decode_splits(B, Hq, k->heads, k->n_slots, D, k->qmode, q_dtype == KVQ_BF16);
     p.part_bytes = decode_part_bytes(B, Hq, p.nsplit, D);
     return p;
@@ -277,7 +277,7 @@ kvq_status sdpa_decode_enqueue(const DecodePlan& plan, const void* q, int q_dtyp
     if (plan.single) {
         L.part_ml = part;
         L.part_o = part + (size_t)B * Hq * plan.nsplit * 2;
-        return from_hip(kvq::launch_sdpa_decode_stream(L, reinterpret_cast<hipStream_t>(stream)));
+        return from_hip(kvq::launch_sdpa_decode_mfma(L, reinterpret_cast<hipStream_t>(stream)));
     }
     L.part_o = part;
     L.part_ml = L.part_o + (size_t)B * Hq * plan.nsplit * L.D;

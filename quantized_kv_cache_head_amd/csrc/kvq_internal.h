@@ -62,10 +62,10 @@ hipError_t launch_sdpa_decode(const DecodeLaunch& L, hipStream_t s);
 
 // Single-pass decode with the split merge in the same launch (int8
 // per-token-head caches): which requests it runs, its split count, launch.
-bool stream_supported(int qmode, int D, int G, int S);
-int stream_splits_max(int B, int Hkv, int S, int D, int G);
-int stream_splits(int B, int Hkv, int S, int D, int G, bool qbf16);
-hipError_t launch_sdpa_decode_stream(const DecodeLaunch& L, hipStream_t s);
+bool mfma_supported(int qmode, int D, int G, int S);
+int mfma_splits_max(int B, int Hkv, int S, int D, int G);
+int mfma_splits(int B, int Hkv, int S, int D, int G, bool qbf16);
+hipError_t launch_sdpa_decode_mfma(const DecodeLaunch& L, hipStream_t s);
 
 struct PrefillLaunch {
     const void* q;
