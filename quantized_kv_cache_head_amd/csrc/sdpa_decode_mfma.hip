@@ -21,8 +21,8 @@
 //  * Each wave keeps PD units in flight in its LDS ring (global_load_lds):
 //    the K and V tiles [64 keys][D bytes] with 16-byte chunks placed by an
 //    xor swizzle (so that the reads below meet no bank conflicts), then the
-//    scales, mask values and zero points of the unit.  The first units go
-//    out before kv_len is known.
+//    scales, mask values and zero points of the unit.  kv_len (a scalar
+//    load) is waited for first: the copies then cover the wave's units only.
 //  * q . k on v_mfma_i32_16x16x64_i8: A = q of the G heads as int8 limbs
 //    (q * 2^e_h rounded to an integer of 22 bits, e_h per head, as three
 //    balanced base-256 digits; two digits of 14 bits when G = 8), one MFMA row
@@ -95,16 +95,16 @@ __device__ __forceinline__ void for_each_unit(std::integer_sequence<int, U...>, 
 // low byte as a signed digit
 __device__ __forceinline__ int sext8(int x) { return (int)(int8_t)x; }
 
-#ifndef KVQ_MPD
-#define KVQ_MPD 2
-#endif
-constexpr int MPD = KVQ_MPD;        // units in flight per wave (LDS ring slots)
 constexpr int MKEYS = 64;           // keys per unit
 constexpr float MTAU = 8.0f;        // lazy rescale threshold (log2 units)
 
+// Two waves per SIMD (eight per workgroup, four at D = 256), each with PD
+// units in flight: while one wave waits for its copies (or for the copy
+// engine to take more), the other computes.
 template <int D>
 struct MGeom {
-    static constexpr int NW = D == 256 ? 2 : 4;           // waves per workgroup
+    static constexpr int NW = D == 256 ? 4 : 8;           // waves per workgroup
+    static constexpr int PD = 1;                          // units in flight per wave (ring slots)
     static constexpr int NT = 64 * NW;
     static constexpr int NH = D / 64;                     // 64-byte quarters of a row
     static constexpr int CPR = D / 16;                    // 16-byte chunks per row
@@ -161,18 +161,20 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     constexpr int NW = GM::NW, NT = GM::NT, NH = GM::NH, CPR = GM::CPR, TILE = GM::TILE, NKD = GM::NKD;
     constexpr int RPI = GM::RPI, OFF_V = GM::OFF_V, OFF_M = GM::OFF_M, SLOT = GM::SLOT, NDMA = GM::NDMA;
     constexpr int QL = HM::QL, RPH = HM::RPH, HPG = HM::HPG, NPB = HM::NPB;
-    constexpr int PD = MPD;
+    constexpr int PD = GM::PD;
     constexpr float NEG_INF = -__builtin_huge_valf();
     constexpr float LOG2E = 1.4426950408889634f;
     static_assert(PD >= 1 && PD <= 3 && (PD - 1) * NDMA <= 63, "ring depth");
     static_assert(3 * G * D * 4 <= SLOT, "wave partial fits its ring slot");
+    static_assert(!(D == 256 && G == 8), "D 256 with 8 heads per KV head runs the split kernel");
 
     // per wave: the q digits [16 rows][D] (read into registers before the key
-    // loop), then, in the same bytes, the p digits of a unit [NPB * 16 rows]
+    // loop), then, in the same bytes, the p digits of a unit [3 G rows]
     // [80 bytes] (the row pitch keeps 16-byte reads of 8 rows on distinct
     // banks).  No copy engine writes here.
     constexpr int PPITCH = 80;
-    constexpr int QST = 16 * D > NPB * 16 * PPITCH ? 16 * D : NPB * 16 * PPITCH;
+    constexpr int PROWS = 3 * G > 16 ? 3 * G : 16;
+    constexpr int QST = 16 * D > PROWS * PPITCH ? 16 * D : PROWS * PPITCH;
     // q of the group as copied in (every wave copies all of it and waits for
     // its own copies only: the bytes are the same)
     constexpr int QBYTES = G * D * (QBF16 ? 2 : 4);
@@ -234,8 +236,8 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     // metadata word i holds key 16 (i % 4) + i / 4, so that lane n finds the
     // keys n, 16 + n, 32 + n, 48 + n of the unit in words 4n .. 4n + 3
     const int mkey = 16 * (lane & 3) + (lane >> 2);
-    // Asynchronous copies of unit t into ring slot U.  A refill past the
-    // wave's last unit (live = false) reads row 0 instead.
+    // Asynchronous copies of unit t into ring slot U (live = false would read
+    // row 0 instead).
     auto fetch = [&](auto UC, int t, bool live) __attribute__((always_inline)) {
         uint8_t* dst = slot(UC);
         const int row0 = (wp + t * W) * MKEYS;
@@ -279,14 +281,37 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     auto for_slots = [&](auto&& f) __attribute__((always_inline)) {
         for_each_unit(std::make_integer_sequence<int, PD>{}, f);
     };
-    // every slot's first unit goes out before kv_len is known
-    for_slots([&](auto UC) __attribute__((always_inline)) { fetch(UC, decltype(UC)::value, true); });
+    // Wait until at most the copies of `later` units (issued after the ones
+    // waited for) are outstanding.  The wait is explicit: the compiler does
+    // not track these copies.  Copies complete in issue order.
+    auto wait_units = [&](int later) __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int N1 = NDMA, N2 = 2 * NDMA < 63 ? 2 * NDMA : 63, N3 = 3 * NDMA < 63 ? 3 * NDMA : 63;
+        if (later >= 3) __builtin_amdgcn_s_waitcnt((N3 & 15) | ((N3 >> 4) << 14) | (7 << 4) | (15 << 8));
+        else if (later == 2) __builtin_amdgcn_s_waitcnt((N2 & 15) | ((N2 >> 4) << 14) | (7 << 4) | (15 << 8));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt((N1 & 15) | ((N1 >> 4) << 14) | (7 << 4) | (15 << 8));
+        else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // kv_len is known before any cache copy goes out: issued after the copies
+    // of every wave of the chip, its load would return only once those had
+    // been served, and no wave could start before.  The copies then cover
+    // exactly the wave's units.
     if (kv_len < 1 || kv_len > S) {
         if (a.err && split == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_KVLEN);
         kv_len = kv_len < 1 ? 1 : S;
     }
     const int nunits = (kv_len + MKEYS - 1) / MKEYS;
     const int nsteps = wp < nunits ? (nunits - wp + W - 1) / W : 0;
+    // the q copies were issued with the kv_len load and take about as long:
+    // they have landed before the cache copies go out
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));   // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    for_slots([&](auto UC) __attribute__((always_inline)) {
+        constexpr int u = decltype(UC)::value;
+        if (u < nsteps) fetch(UC, u, true);
+    });
 
     // ---- q digits ------------------------------------------------------------
     // Each wave converts the group on its own, through its own LDS words (no
@@ -302,12 +327,6 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     int qs[HPG][QL];                                  // per own head and digit: sum over d
     i32x4_t qA[NH];                                   // MFMA A operand: digits of row n, d chunk 4 dq + c
     {
-        // the q copies were issued before PD * NDMA others (copies complete in
-        // order, so allowing up to 63 of those outstanding is enough)
-        constexpr int LATER = PD * NDMA < 63 ? PD * NDMA : 63;
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((LATER & 15) | ((LATER >> 4) << 14) | (7 << 4) | (15 << 8));
-        __builtin_amdgcn_sched_barrier(0);
         float qv[QPL];
 #pragma unroll
         for (int i = 0; i < QPL; ++i) {
@@ -352,12 +371,25 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         }
 #pragma unroll
         for (int li = 0; li < QL; ++li) {
-            uint8_t* row = s_q[wave] + (hq * RPH + li) * D + e0;
+            uint32_t roff = (uint32_t)((hq * RPH + li) * D + e0);
+            __asm__ volatile("" : "+v"(roff));             // see the tile reads in the key loop
+            uint8_t* row = s_q[wave] + roff;
             if constexpr (QPL % 4 == 0) {
+                // one store per 16 bytes (wider than the compiler would pair)
+                uint32_t wd[QPL / 4];
 #pragma unroll
                 for (int w = 0; w < QPL / 4; ++w)
-                    reinterpret_cast<uint32_t*>(row)[w] = (uint32_t)dig[li][4 * w] | ((uint32_t)dig[li][4 * w + 1] << 8) |
-                                                          ((uint32_t)dig[li][4 * w + 2] << 16) | ((uint32_t)dig[li][4 * w + 3] << 24);
+                    wd[w] = (uint32_t)dig[li][4 * w] | ((uint32_t)dig[li][4 * w + 1] << 8) |
+                            ((uint32_t)dig[li][4 * w + 2] << 16) | ((uint32_t)dig[li][4 * w + 3] << 24);
+                if constexpr (QPL == 4) {
+                    *reinterpret_cast<uint32_t*>(row) = wd[0];
+                } else if constexpr (QPL == 8) {
+                    *reinterpret_cast<uint2*>(row) = make_uint2(wd[0], wd[1]);
+                } else {
+#pragma unroll
+                    for (int w = 0; w < QPL / 4; w += 4)
+                        *reinterpret_cast<uint4*>(row + 4 * w) = make_uint4(wd[w], wd[w + 1], wd[w + 2], wd[w + 3]);
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < QPL; ++i) row[i] = dig[li][i];
@@ -423,53 +455,46 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         return r;
     };
 
-    // The copies of a unit must have landed before its slot is read.  The
-    // wait is explicit (the compiler does not track these copies): copies
-    // complete in issue order, so allowing the `later` units issued after
-    // this one to be outstanding, `later` * NDMA copies, is enough.
-    auto wait_copies = [&](int later) __attribute__((always_inline)) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (later >= 2) {
-            constexpr int N2 = 2 * NDMA;
-            __builtin_amdgcn_s_waitcnt((N2 & 15) | ((N2 >> 4) << 14) | (7 << 4) | (15 << 8));
-        } else if (later == 1) {
-            __builtin_amdgcn_s_waitcnt((NDMA & 15) | ((NDMA >> 4) << 14) | (7 << 4) | (15 << 8));
-        } else {
-            __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    auto step = [&](auto UC, int t, int later) __attribute__((always_inline)) {
-        wait_copies(later);
+    // unit t's copies have landed once at most the units t + 1 .. t + PD - 1
+    // that exist are outstanding
+    auto step = [&](auto UC, int t) __attribute__((always_inline)) {
+        const int later = min(PD - 1, nsteps - 1 - t);
+        wait_units(later);
         const uint8_t* src = slot(UC);
         const int row0 = (wp + t * W) * MKEYS;
-        // ---- scores: S^T[(head, digit)][key] for 4 tiles of 16 keys
-        i32x4_t sc[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            sc[tt] = i32x4_t{0, 0, 0, 0};
-            const int kr = 16 * tt + n;
-#pragma unroll
-            for (int dq = 0; dq < NH; ++dq) {
-                const int cc = 4 * dq + c;
-                uint32_t koff = (uint32_t)(kr * D + 16 * (cc ^ GM::sw(kr)));
-                __asm__ volatile("" : "+v"(koff));         // see the V reads below
-                const i32x4_t kb = *reinterpret_cast<const i32x4_t*>(src + koff);
-                sc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qA[dq], kb, sc[tt], 0, 0, 0);
-            }
-        }
+        // ---- the unit's metadata; the K tile is read by the score MFMAs and
+        // the V tile once the p digits are made, then the slot's refill goes
+        // out, so that the next units stream in during the p.v half of the
+        // work.  Each tile offset passes through an empty asm statement, so that the
+        // compiler neither pairs nor hoists these reads: in the forms it makes
+        // of them it loses which ring slot they read, and then waits for every
+        // copy in flight, the other slots' included.
         const float4 sk4 = *reinterpret_cast<const float4*>(src + OFF_M + 16 * n);
         const float4 sv4 = *reinterpret_cast<const float4*>(src + OFF_M + 256 + 16 * n);
         const float4 mk4 = *reinterpret_cast<const float4*>(src + OFF_M + 512 + 16 * n);
-        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
-        const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
-        const float mkv[4] = {mk4.x, mk4.y, mk4.z, mk4.w};
         int zk[4], zv[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             zk[tt] = (int)reinterpret_cast<const int8_t*>(src + OFF_M + 768)[16 * tt + n];
             zv[tt] = (int)reinterpret_cast<const int8_t*>(src + OFF_M + 832)[16 * tt + n];
+        }
+        const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
+        const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+        const float mkv[4] = {mk4.x, mk4.y, mk4.z, mk4.w};
+        // ---- scores: S^T[(head, digit)][key] for 4 tiles of 16 keys; the B
+        // operand is K row 16 tt + n, 16-byte chunk 4 dq + c
+        i32x4_t sc[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            sc[tt] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int dq = 0; dq < NH; ++dq) {
+                const int kr = 16 * tt + n, cc = 4 * dq + c;
+                uint32_t koff = (uint32_t)(kr * D + 16 * (cc ^ GM::sw(kr)));
+                __asm__ volatile("" : "+v"(koff));
+                const i32x4_t kb = *reinterpret_cast<const i32x4_t*>(src + koff);
+                sc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qA[dq], kb, sc[tt], 0, 0, 0);
+            }
         }
         float s[HPG][4];
         bool up = false;
@@ -547,7 +572,7 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         for (int j = 0; j < HPG; ++j) {
             const int f = (int)fsc[j];
             uint32_t poff = (uint32_t)((3 * (c * HPG + j)) * PPITCH + n);
-            __asm__ volatile("" : "+v"(poff));             // see the V reads below
+            __asm__ volatile("" : "+v"(poff));             // see the tile reads
             uint8_t* prow0 = pbuf + poff;
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
@@ -569,16 +594,10 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         i32x4_t pB[NPB];
 #pragma unroll
-        for (int pb = 0; pb < NPB; ++pb) pB[pb] = *reinterpret_cast<const i32x4_t*>(pbuf + (16 * pb + n) * PPITCH + 16 * c);
-        // ---- o^T[dim][(head, digit)] += V^T (p * scale_v digits)
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh) {
-            // words of 4 dims (dim word 16 hh + n) of the keys 16 c .. 16 c + 15
-            // (each offset passes through an empty asm statement, so that the
-            // compiler neither pairs nor hoists these reads: in the forms it
-            // makes of them it loses which ring slot they read, and then waits
-            // for every copy in flight, the other slots' included)
-            uint32_t w[16];
+        for (int pb = 0; pb < NPB; ++pb)   // (columns past 3 G read a row in use; their results are not used)
+            pB[pb] = *reinterpret_cast<const i32x4_t*>(pbuf + min(16 * pb + n, PROWS - 1) * PPITCH + 16 * c);
+        // V: words of 4 dims (dim word 16 hh + n) of the keys 16 c .. 16 c + 15
+        auto read_v = [&](int hh, uint32_t* w) __attribute__((always_inline)) {
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
                 const int r = 16 * c + kk;
@@ -587,6 +606,15 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
                 __asm__ volatile("" : "+v"(off));
                 w[kk] = *reinterpret_cast<const uint32_t*>(src + off);
             }
+        };
+        uint32_t vw[NH][16];
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) read_v(hh, vw[hh]);
+        if (t + PD < nsteps) fetch(UC, t + PD, true);
+        // ---- o^T[dim][(head, digit)] += V^T (p * scale_v digits)
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            const uint32_t* w = vw[hh];
             // 4 x 4 byte transposes: op[e] word q4 = dim e of keys 4 q4 .. 4 q4 + 3
             i32x4_t op[4];
 #pragma unroll
@@ -615,20 +643,18 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // whole ring rounds (every slot refilled right after use; a refill past
-    // the wave's last unit reads row 0, so the copy counts stay exact), then
-    // the rest of the ring without refills
+    // whole ring rounds (each step refills its slot with the unit PD later,
+    // if the wave has it), then the rest of the ring
     int t0 = 0;
     for (; t0 + PD <= nsteps; t0 += PD) {
         for_slots([&](auto UC) __attribute__((always_inline)) {
             constexpr int u = decltype(UC)::value;
-            step(UC, t0 + u, PD - 1);
-            fetch(UC, t0 + u + PD, t0 + u + PD < nsteps);
+            step(UC, t0 + u);
         });
     }
     for_slots([&](auto UC) __attribute__((always_inline)) {
         constexpr int u = decltype(UC)::value;
-        if (u < PD - 1 && t0 + u < nsteps) step(UC, t0 + u, PD - 1 - u);
+        if (u < PD - 1 && t0 + u < nsteps) step(UC, t0 + u);
     });
     // every copy into the ring has landed before slot 0 is reused
     __builtin_amdgcn_s_waitcnt(0);
@@ -758,12 +784,14 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
 // Zero points are copied as aligned words of four keys, so the planes must
 // keep them aligned (S % 4 == 0 and 4-byte aligned zero-point arrays; the
 // caller checks the pointers).
+// (D = 256 with 8 query heads per KV head would not fit the registers.)
 bool mfma_supported(int qmode, int D, int G, int S) {
     return qmode == QM_INT8_TH && (D == 64 || D == 128 || D == 256) && (G == 1 || G == 2 || G == 4 || G == 8) &&
+           !(D == 256 && G == 8) &&
            S % 4 == 0 && (int64_t)S * D < (int64_t(1) << 32);
 }
 
-static int mfma_nw(int D) { return D == 256 ? 2 : 4; }
+static int mfma_nw(int D) { return D == 256 ? 4 : 8; }
 
 // Splits per plane: one round of resident workgroups (one per CU), and no
 // more than lets every wave of the plane get a unit of a full cache; at most
@@ -806,7 +834,10 @@ static hipError_t launch_mfma_g(const MfmaArgs& a, int G, int nwg, hipStream_t s
     case 1: launch_mfma_t<D, 1, QBF16>(a, nwg, s); break;
     case 2: launch_mfma_t<D, 2, QBF16>(a, nwg, s); break;
     case 4: launch_mfma_t<D, 4, QBF16>(a, nwg, s); break;
-    case 8: launch_mfma_t<D, 8, QBF16>(a, nwg, s); break;
+    case 8:
+        if constexpr (D == 256) return hipErrorInvalidValue;
+        else launch_mfma_t<D, 8, QBF16>(a, nwg, s);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
