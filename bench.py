@@ -4,20 +4,24 @@ Headline workload (Llama-3-8B-shaped decode layer): B 8, 32 query / 8 KV
 heads, head_dim 128, 8192-slot int8 per-token-head cache filled to kv_len 4096,
 bf16 inputs with 4 of every 128 K/V channels scaled x10.  One step is the
 whole decode-side path: slot position of the new token (full-context layout),
-quantize + scatter of its K and V, and decode attention over the cache
-(split-K with the combine fused in).
+quantize + scatter of its K and V, and decode attention over the cache (one
+kernel launch: split pass and split merge in the same launch).
 
 The value is decode-attention HBM throughput: the algorithmic bytes the
 attention must move (codes, scales and zero points of slots [0, kv_len) plus
-q and out) divided by the time of one kvq_sdpa_decode call (split kernel +
-combine kernel), measured with HIP events on the launch stream around replays
-of a HIP graph that holds one decode call per cache replica.  Every launch
-goes through HIP graphs, so host launch overhead does not leak into the GPU
-timings.  The step rotates over cache replicas whose total size is far above
-the 256 MB Infinity Cache, so the bytes come from HBM.  The line also carries
-quant-scatter Mtokens/s, the roofline record of the decode call and the CPU
-oracle timed on the same step.  Secondary legs time the other workloads
-(sink/ring decode, 4-bit chunked prefill on MFMA, block scatter).
+q and out) divided by the time of one kvq_sdpa_decode call.  That time is the
+median, over 16 replays of a HIP graph of 128 decode calls (16 rounds over 8
+cache replicas, 2048 calls in all, independent of --steps), of the per-call
+mean of a replay, timed with HIP events on the launch stream.  The replicas
+total far more than the 256 MB Infinity Cache, so the bytes come from HBM.
+The roofline record carries, next to the 8 TB/s peak, the achievable rate a
+plain read-only stream kernel (16-byte loads) reaches on the same box in the
+same run, for 1 GiB and for the decode call's own byte count.  The line also
+carries quant-scatter Mtokens/s, the CPU oracle timed on the same step and
+secondary legs for the other workloads (tiny prefill + decode, sink/ring
+decode, 4-bit chunk scatter and chunked prefill, block scatter, block-cache
+attention), each with a roofline record and with its inputs rotated past the
+Infinity Cache where the leg is bandwidth-bound.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -79,6 +83,89 @@ def replay_ms(g, reps: int, per_replay: int = 1) -> float:
         b.record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) / per_replay
+
+
+def replay_stats(g, reps: int, per_replay: int) -> dict:
+    """Per-call milliseconds of each replay of g (which holds per_replay
+    calls): HIP events around every replay; median, p10, p90 over replays."""
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    v = np.array([a.elapsed_time(b) for a, b in ev]) / per_replay
+    return {"median": float(np.median(v)), "p10": float(np.percentile(v, 10)), "p90": float(np.percentile(v, 90)),
+            "replays": reps, "calls": reps * per_replay}
+
+
+# --------------------------------------------------------------------------
+# Achievable read bandwidth: a plain read-only stream kernel
+# --------------------------------------------------------------------------
+
+_bench_lib = None
+
+
+def bench_lib():
+    import ctypes
+    global _bench_lib
+    if _bench_lib is None:
+        path = os.path.join(ROOT, "quantized_kv_cache_head_amd", "libkvq_bench.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m quantized_kv_cache_head_amd.build`")
+        L = ctypes.CDLL(path)
+        L.kvq_bench_stream_read.restype = ctypes.c_int
+        L.kvq_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        _bench_lib = L
+    return _bench_lib
+
+
+def stream_ceiling(small_bytes: int) -> dict:
+    """Read rate of a plain streaming kernel (16-byte loads, one contiguous
+    chunk per workgroup, 8 loads in flight per thread): one 1 GiB buffer per
+    launch, and `small_bytes` per launch rotated over buffers that total
+    more than 1 GiB (so neither size is served by the Infinity Cache); the
+    best of three grid sizes, each a HIP graph of back-to-back launches."""
+    import ctypes
+    L = bench_lib()
+    sink = torch.zeros(8192, dtype=torch.int32, device=DEV)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launches(bufs, nbytes, grid, rounds):
+        def run():
+            for _ in range(rounds):
+                for b in bufs:
+                    st = L.kvq_bench_stream_read(ctypes.c_void_p(b.data_ptr()), nbytes, grid,
+                                                 ctypes.c_void_p(sink.data_ptr()),
+                                                 ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    if st != 0:
+                        raise RuntimeError(f"stream kernel launch failed: {st}")
+        return run
+    res = {}
+    big = [torch.empty(1 << 30, dtype=torch.uint8, device=DEV)]
+    small_n = (small_bytes + 15) // 16 * 16
+    nsmall = max(16, -(-(1 << 30) // small_n))
+    small = [torch.empty(small_n, dtype=torch.uint8, device=DEV) for _ in range(nsmall)]
+    for b in big + small:
+        b.fill_(1)
+    torch.cuda.synchronize()
+    for name, bufs, nbytes, rounds in (("1GiB", big, 1 << 30, 4), ("decode_bytes", small, small_n, 1)):
+        best = None
+        for grid in (1024, 2048, 4096):
+            g = capture(launches(bufs, nbytes, grid, rounds))
+            stt = replay_stats(g, 8, len(bufs) * rounds)
+            gbs = nbytes / stt["median"] / 1e6
+            if best is None or gbs > best["gbs"]:
+                best = {"gbs": round(gbs, 1), "us": round(stt["median"] * 1e3, 3), "grid": grid,
+                        "bytes_per_launch": nbytes, "buffers": len(bufs)}
+            del g
+        res[name] = best
+    del big, small
+    torch.cuda.synchronize()
+    return res
 
 
 # --------------------------------------------------------------------------
@@ -202,7 +289,7 @@ def cpu_baseline(st: Llama8BStep, gpu_out, budget_s=10.0):
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("sdpa_decode.hip", "kvq_device.h"):
+    for f in ("sdpa_decode_mfma.hip", "kvq_device.h"):
         with open(os.path.join(ROOT, "quantized_kv_cache_head_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -235,79 +322,155 @@ def time_ms(fn, iters=20, inner=10):
     return replay_ms(capture(many), iters, inner)
 
 
+def roof(bound, achieved, peak, unit, **extra):
+    r = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 5)}
+    r.update(extra)
+    return r
+
+
+def leg_tiny():
+    """Tiny full-context int8 cache (B 1, 4/2 heads, D 64, 256 slots, fp32
+    inputs): the 64-token prefill (positions, K+V quant-scatter, causal
+    prefill attention) and 32 decode steps (positions, K+V quant-scatter,
+    decode attention), as one HIP graph; also the 32 decode steps alone."""
+    w = wl.TINY
+    K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
+    V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
+    q0, k0, v0 = (torch.from_numpy(a).to(DEV) for a in wl.tiny_prefill(w))
+    steps = []
+    for p in range(w.prefill, w.prefill + w.decode_steps):
+        qp, kp, vp = (torch.from_numpy(a).to(DEV) for a in wl.tiny_decode(p, w))
+        steps.append((qp, kp, vp, i32(p), i32(p + 1), torch.empty(1, dtype=torch.int32, device=DEV),
+                      torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=DEV)))
+    sl0 = torch.empty(w.prefill, dtype=torch.int32, device=DEV)
+    start0, kvl0 = i32(0), i32(w.prefill)
+    out0 = torch.empty_like(q0)
+    ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
+
+    def prefill():
+        kvq.positions_full(start0, w.prefill, w.S, sl0)
+        kvq.quant_scatter_kv(k0, v0, sl0, K, V)
+        kvq.sdpa_prefill(q0, K, V, kv_len=kvl0, causal=True, out=out0)
+
+    def decode_steps():
+        for qp, kp, vp, st, kl, sl, o in steps:
+            kvq.positions_full(st, 1, w.S, sl)
+            kvq.quant_scatter_kv(kp, vp, sl, K, V)
+            kvq.sdpa_decode(qp, K, V, kv_len=kl, out=o, workspace=ws)
+
+    def whole():
+        prefill()
+        decode_steps()
+    t_all = replay_stats(capture(whole), 20, 1)
+    t_dec = replay_stats(capture(decode_steps), 20, w.decode_steps)
+    # algorithmic bytes: fp32 inputs read, codes + scale + zp written, q/out,
+    # and the cache rows each attention call reads
+    row = w.D + 4 + 1
+    nb = (2 * w.B * w.Hkv * w.prefill * (w.D * 4 + row) + 2 * w.B * w.Hq * w.prefill * w.D * 4
+          + 2 * w.B * w.Hkv * w.prefill * row)
+    for p in range(w.prefill, w.prefill + w.decode_steps):
+        nb += 2 * w.B * w.Hkv * (w.D * 4 + row) + 2 * w.B * w.Hq * w.D * 4 + 2 * w.B * w.Hkv * (p + 1) * row
+    us = t_all["median"] * 1e3
+    return {"total_us": round(us, 2), "decode_step_us": round(t_dec["median"] * 1e3, 3),
+            "launches": 3 + 3 * w.decode_steps,
+            "roofline": roof("hbm", nb / us / 1e3, HBM_PEAK_GBS, "GB/s", bytes=nb,
+                             note="launch-bound: 99 small launches"),
+            "note": "prefill 64 tokens + 32 decode steps, one HIP graph; median of 20 replays"}
+
+
 def leg_block_scatter():
+    """C5: quantize + scatter 16384 rows of 128 (1638 slots -1) into a
+    65536-slot block cache.  64 input replicas (4 MiB each) and 8 cache
+    replicas rotate, so the inputs come from HBM."""
     w = wl.BLOCKSCATTER
     x_np, slots_np = wl.blockscatter_inputs(w)
-    x = torch.from_numpy(x_np).to(torch.bfloat16).to(DEV)[None, None]
+    x0 = torch.from_numpy(x_np).to(torch.bfloat16).to(DEV)[None, None]
+    xs = [x0.clone() for _ in range(64)]
     slots = torch.from_numpy(slots_np).to(DEV)
     res = {}
     valid = int((slots_np >= 0).sum())
-    warm = kvq.Cache.empty(kvq.FP8E4M3_B32, 1, 1, w.n_slots, w.d)
-    time_ms(lambda: kvq.quant_scatter(x, slots, warm), iters=20, inner=8)     # clocks up before the first timing
     for name, mode, fl in (("fp8_e4m3", kvq.FP8E4M3_B32, 0), ("mxfp4", kvq.MXFP4_B32, 0),
                            ("mxfp8", kvq.MXFP8_B32, 0), ("fp8_e5m2", kvq.FP8E5M2_B32, 0), ("int8", kvq.INT8_B32, 0),
                            ("mxfp4_ocp_scale", kvq.MXFP4_B32, kvq.MX_SCALE_OCP)):
         caches = [kvq.Cache.empty(mode, 1, 1, w.n_slots, w.d).sentinel_fill() for _ in range(8)]
-        it = iter(range(10 ** 9))
-        # the faster of two timings: the first one after a new graph is
-        # sometimes slow
-        ms = min(time_ms(lambda: kvq.quant_scatter(x, slots, caches[next(it) % 8], flags=fl), iters=20, inner=8)
-                 for _ in range(2))
+
+        def calls():
+            for i, x in enumerate(xs):
+                kvq.quant_scatter(x, slots, caches[i % 8], flags=fl)
+        stt = replay_stats(capture(calls), 10, len(xs))
+        ms = stt["median"]
         rb = w.d // 2 if mode == kvq.MXFP4_B32 else w.d
         sb = (w.d // 32) * (1 if mode in kvq.E8M0_MODES else 4)
         nbytes = w.bs * 4 + valid * (w.d * 2 + rb + sb)
-        res[name] = {"us": round(ms * 1e3, 3), "mtok_s": round(w.bs / ms / 1e3, 1),
-                     "gbs": round(nbytes / ms / 1e6, 1)}
+        gbs = nbytes / ms / 1e6
+        res[name] = {"us": round(ms * 1e3, 3), "mtok_s": round(w.bs / ms / 1e3, 1), "gbs": round(gbs, 1),
+                     "roofline": roof("hbm", gbs, HBM_PEAK_GBS, "GB/s", bytes=nbytes),
+                     "note": "inputs rotated over 64 replicas (256 MiB), caches over 8: HBM-cold"}
+        del caches
     return res
 
 
 def leg_sink_ring():
+    """C3: decode step at position 6000 of a sink (4 + 2044 slots) and a ring
+    (1024) cache, B 4, 32/8 heads, D 128: positions, K+V quant-scatter,
+    mask build, decode attention.  16 (sink) / 32 (ring) cache replicas
+    rotate, about 280 MB each way, so the cache bytes come from HBM."""
     w = wl.SINKRING
     res = {}
     gen = torch.Generator(device=DEV)
     gen.manual_seed(1003)
     p = w.last_pos
-    for name, sink, window in (("sink", w.sink, w.window), ("ring", 0, w.ring_window)):
+    for name, sink, window, R in (("sink", w.sink, w.window, 16), ("ring", 0, w.ring_window, 32)):
         S = sink + window
-        K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
-        V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
-        cp = torch.full((S,), -1, dtype=torch.int32, device=DEV)
-        # steady state at position p: the cache holds positions p-S+1 .. p-1
         hist = torch.randn((w.B, w.Hkv, S, w.D), generator=gen, device=DEV).to(torch.bfloat16)
-        sm = torch.empty(S, dtype=torch.int32, device=DEV)
-        if sink:
-            kvq.positions_with_sink(i32(0), sink, sink, window, sm[:sink], cp)
-            kvq.positions_with_sink(i32(p - window + 1), window, sink, window, sm[sink:], cp)
-        else:
-            kvq.positions_ring(i32(p - window + 1), window, window, sm, cp)
-        kvq.quant_scatter(hist, sm, K)
-        kvq.quant_scatter(hist, sm, V)
         q = torch.randn((w.B, w.Hq, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
         knew = torch.randn((w.B, w.Hkv, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
         vnew = torch.randn((w.B, w.Hkv, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
         start, kvl = i32(p), i32(min(p + 1, S))
-        slot = torch.empty(1, dtype=torch.int32, device=DEV)
-        mask = torch.empty((1, S), dtype=torch.float32, device=DEV)
         out = torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.bfloat16, device=DEV)
         ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, S, w.D)
-
-        def step():
+        reps = []
+        for _ in range(R):
+            K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+            V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+            cp = torch.full((S,), -1, dtype=torch.int32, device=DEV)
+            sm = torch.empty(S, dtype=torch.int32, device=DEV)
+            # steady state at position p: the cache holds positions p-S+1 .. p-1
             if sink:
-                kvq.positions_with_sink(start, 1, sink, window, slot, cp)
+                kvq.positions_with_sink(i32(0), sink, sink, window, sm[:sink], cp)
+                kvq.positions_with_sink(i32(p - window + 1), window, sink, window, sm[sink:], cp)
             else:
-                kvq.positions_ring(start, 1, window, slot, cp)
-            kvq.quant_scatter_kv(knew, vnew, slot, K, V)
-            kvq.build_mask(cp, start, 1, sink, window, mask)
-            kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+                kvq.positions_ring(i32(p - window + 1), window, window, sm, cp)
+            kvq.quant_scatter(hist, sm, K)
+            kvq.quant_scatter(hist, sm, V)
+            mask = torch.empty((1, S), dtype=torch.float32, device=DEV)
+            slot = torch.empty(1, dtype=torch.int32, device=DEV)
+            reps.append((K, V, cp, mask, slot))
+        torch.cuda.synchronize()
 
-        def dec():
-            kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+        def steps():
+            for K, V, cp, mask, slot in reps:
+                if sink:
+                    kvq.positions_with_sink(start, 1, sink, window, slot, cp)
+                else:
+                    kvq.positions_ring(start, 1, window, slot, cp)
+                kvq.quant_scatter_kv(knew, vnew, slot, K, V)
+                kvq.build_mask(cp, start, 1, sink, window, mask)
+                kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
 
-        step_ms = time_ms(step, iters=10)
-        dec_ms = time_ms(dec, iters=10)
+        def decs():
+            for K, V, cp, mask, slot in reps:
+                kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+        t_step = replay_stats(capture(steps), 16, R)
+        t_dec = replay_stats(capture(decs), 16, R)
         nbytes = 2 * w.B * w.Hkv * S * (w.D + 5) + 2 * w.B * w.Hq * w.D * 2 + S * 4
-        res[name] = {"step_us": round(step_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
-                     "decode_gbs": round(nbytes / dec_ms / 1e6, 1), "note": "cache planes L2/MALL-warm"}
+        gbs = nbytes / t_dec["median"] / 1e6
+        res[name] = {"step_us": round(t_step["median"] * 1e3, 2), "decode_us": round(t_dec["median"] * 1e3, 2),
+                     "decode_gbs": round(gbs, 1), "replicas": R,
+                     "roofline": roof("hbm", gbs, HBM_PEAK_GBS, "GB/s", bytes=nbytes),
+                     "note": f"{R} cache replicas rotated (HBM-cold); median of 16 graph replays"}
+        del reps
     return res
 
 
@@ -323,24 +486,39 @@ def leg_long_prefill():
         sl = torch.arange(j0, j0 + blk, dtype=torch.int32, device=DEV)
         kvq.quant_scatter(x, sl, K)
         kvq.quant_scatter(x, sl, V)
-    xc = torch.randn((w.B, w.Hkv, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
     res = {}
+    # the chunk's K+V quant-scatter (2048 tokens x 16 heads x 256, bf16 in,
+    # two 4-bit codes per byte out): 8 input replicas (34 MB each) written to
+    # 8 different slot ranges, so inputs and written lines are HBM-cold
+    R = 8
+    xs = [(torch.randn((w.B, w.Hkv, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16),
+           torch.randn((w.B, w.Hkv, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16),
+           torch.arange(w.S - w.Lq * (r + 1), w.S - w.Lq * r, dtype=torch.int32, device=DEV)) for r in range(R)]
+
+    def scatters():
+        for xk, xv, sl in xs:
+            kvq.quant_scatter_kv(xk, xv, sl, K, V)
+    t_sc = replay_stats(capture(scatters), 8, R)
+    sc_bytes = 2 * w.B * w.Hkv * w.Lq * (w.D * 2 + w.D // 2 + 5) + w.Lq * 4
+    sc_gbs = sc_bytes / t_sc["median"] / 1e6
+    res["chunk_scatter_kv_lq2048"] = {
+        "us": round(t_sc["median"] * 1e3, 2), "gbs": round(sc_gbs, 1),
+        "mtok_s": round(w.Lq / t_sc["median"] / 1e3, 1), "bytes": sc_bytes,
+        "roofline": roof("hbm", sc_gbs, HBM_PEAK_GBS, "GB/s", bytes=sc_bytes),
+        "note": "one kvq_quant_scatter_kv launch (K and V); 8 input replicas rotated: HBM-cold"}
+    del xs
     for end in w.chunk_ends:
         q = torch.randn((w.B, w.Hq, w.Lq, w.D), generator=gen, device=DEV).to(torch.bfloat16)
         kvl = i32(end)
         out = torch.empty_like(q)
-        sl = torch.arange(end - w.Lq, end, dtype=torch.int32, device=DEV)
-        sc_ms = time_ms(lambda: kvq.quant_scatter(xc, sl, K), iters=5)
         ms = time_ms(lambda: kvq.sdpa_prefill(q, K, V, kv_len=kvl, causal=True, out=out), iters=3, inner=1)
         Lq = w.Lq
         pairs = Lq * (end - Lq) + Lq * (Lq + 1) // 2
         flops = 4.0 * w.D * w.Hq * pairs
         tfs = flops / ms / 1e9
-        sc_bytes = w.Hkv * w.Lq * (w.D * 2 + w.D // 2 + 5) + w.Lq * 4
         res[f"kv_len_{end}"] = {"prefill_ms": round(ms, 3), "tflops": round(tfs, 1),
                                 "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4),
-                                "chunk_scatter_us": round(sc_ms * 1e3, 2),
-                                "chunk_scatter_gbs": round(sc_bytes / sc_ms / 1e6, 1)}
+                                "roofline": roof("mfma", tfs, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", flops=flops)}
     # shorter chunks over the same cache, ending at 65536: few query tiles,
     # so the key range is split over workgroups (kvq_sdpa_prefill_split)
     end = w.chunk_ends[0]
@@ -357,7 +535,8 @@ def leg_long_prefill():
         res[f"short_chunk_lq{Lq}_kv_len_{end}"] = {
             "prefill_ms": round(ms_one, 4), "tflops": round(flops / ms_one / 1e9, 1),
             "split_prefill_ms": round(ms_split, 4), "split_tflops": round(flops / ms_split / 1e9, 1),
-            "split_mfma_frac": round(flops / ms_split / 1e9 / MFMA_F16_PEAK_TFLOPS, 4)}
+            "split_mfma_frac": round(flops / ms_split / 1e9 / MFMA_F16_PEAK_TFLOPS, 4),
+            "roofline": roof("mfma", flops / ms_split / 1e9, MFMA_F16_PEAK_TFLOPS, "TFLOP/s", flops=flops)}
     return res
 
 
@@ -373,7 +552,8 @@ def leg_block_attention():
     for name, mode in (("fp8_e4m3", kvq.FP8E4M3_B32), ("mxfp4", kvq.MXFP4_B32), ("mxfp8", kvq.MXFP8_B32),
                        ("fp8_e5m2", kvq.FP8E5M2_B32), ("int8", kvq.INT8_B32)):
         reps = []
-        for _ in range(4):
+        R = 8 if mode == kvq.MXFP4_B32 else 4      # > 256 MB of cache planes either way
+        for _ in range(R):
             K = kvq.Cache.empty(mode, w.B, w.Hkv, w.S, w.D)
             V = kvq.Cache.empty(mode, w.B, w.Hkv, w.S, w.D)
             sl = torch.arange(w.kv_len, dtype=torch.int32, device=DEV)
@@ -385,17 +565,18 @@ def leg_block_attention():
         out = torch.empty_like(q)
         ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
         kvl = i32(w.kv_len)
-        it = iter(range(10 ** 9))
 
-        def dec():
-            K, V = reps[next(it) % 4]
-            kvq.sdpa_decode(q, K, V, kv_len=kvl, out=out, workspace=ws)
-        ms = time_ms(dec, iters=10, inner=8)
+        def decs():
+            for K, V in reps:
+                kvq.sdpa_decode(q, K, V, kv_len=kvl, out=out, workspace=ws)
+        ms = replay_stats(capture(decs), 16, len(reps))["median"]
         rb = w.D // 2 if mode == kvq.MXFP4_B32 else w.D
         sb = (w.D // 32) * (1 if mode in kvq.E8M0_MODES else 4)
         nbytes = 2 * w.B * w.Hkv * w.kv_len * (rb + sb) + 2 * w.B * w.Hq * w.D * 2
-        res[f"decode_llama8b_{name}"] = {"us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
-                                         "hbm_frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": nbytes}
+        gbs = nbytes / ms / 1e6
+        res[f"decode_llama8b_{name}"] = {"us": round(ms * 1e3, 2), "gbs": round(gbs, 1),
+                                         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": nbytes,
+                                         "roofline": roof("hbm", gbs, HBM_PEAK_GBS, "GB/s", bytes=nbytes)}
         del reps
     w = wl.LONGPREFILL
     end = w.chunk_ends[0]
@@ -415,9 +596,72 @@ def leg_block_attention():
         pairs = w.Lq * (end - w.Lq) + w.Lq * (w.Lq + 1) // 2
         tfs = 4.0 * w.D * w.Hq * pairs / ms / 1e9
         res[f"prefill_d256_kv{end}_{name}"] = {"ms": round(ms, 3), "tflops": round(tfs, 1),
-                                               "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4)}
+                                               "mfma_frac": round(tfs / MFMA_F16_PEAK_TFLOPS, 4),
+                                               "roofline": roof("mfma", tfs, MFMA_F16_PEAK_TFLOPS, "TFLOP/s")}
         del K, V
     return res
+
+
+# --------------------------------------------------------------------------
+# The oracle on one host thread (run in a child process with OMP_NUM_THREADS=1;
+# it touches no GPU)
+# --------------------------------------------------------------------------
+
+def oracle_one_thread() -> dict:
+    import oracle
+    res = {}
+    # C1: prefill 64 + 32 decode steps
+    w = wl.TINY
+    hk = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    hv = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    q, k, v = wl.tiny_prefill(w)
+    t0 = time.perf_counter()
+    sm, _ = oracle.positions_full(0, w.prefill, w.S)
+    oracle.quant_scatter(hk, k, sm)
+    oracle.quant_scatter(hv, v, sm)
+    oracle.sdpa(q, hk, hv, w.prefill, causal=True)
+    for p in range(w.prefill, w.prefill + w.decode_steps):
+        q, k, v = wl.tiny_decode(p, w)
+        sm, _ = oracle.positions_full(p, 1, w.S)
+        oracle.quant_scatter(hk, k, sm)
+        oracle.quant_scatter(hv, v, sm)
+        oracle.sdpa(q, hk, hv, p + 1)
+    res["tiny_prefill64_decode32_s"] = round(time.perf_counter() - t0, 4)
+    # C2: one decode step (scatter of the new token + attention of all rows)
+    w = wl.LLAMA8B
+    k_np, v_np = wl.llama8b_kv(w)
+    hist = w.kv_len - 1
+    hk = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    hv = oracle.HostCache(oracle.INT8_TH, w.B, w.Hkv, w.S, w.D)
+    slots = np.arange(hist, dtype=np.int32)
+    oracle.quant_scatter(hk, k_np[:, :, :hist], slots)
+    oracle.quant_scatter(hv, v_np[:, :, :hist], slots)
+    q = wl.llama8b_q(w)
+    t0 = time.perf_counter()
+    slot = np.array([hist], np.int32)
+    oracle.quant_scatter(hk, k_np[:, :, hist:hist + 1], slot)
+    oracle.quant_scatter(hv, v_np[:, :, hist:hist + 1], slot)
+    oracle.sdpa(q, hk, hv, w.kv_len)
+    res["llama8b_decode_step_s"] = round(time.perf_counter() - t0, 4)
+    # C5: block quant-scatter, FP8-E4M3 and MX-FP4
+    w = wl.BLOCKSCATTER
+    x_np, slots_np = wl.blockscatter_inputs(w)
+    for name, mode in (("fp8_e4m3", oracle.FP8E4M3_B32), ("mxfp4", oracle.MXFP4_B32)):
+        hc = oracle.HostCache(mode, 1, 1, w.n_slots, w.d)
+        t0 = time.perf_counter()
+        oracle.quant_scatter(hc, x_np[None, None], slots_np[None])
+        res[f"block_scatter_16384x128_{name}_s"] = round(time.perf_counter() - t0, 4)
+    return res
+
+
+def oracle_one_thread_child() -> dict:
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-one-thread"], env=env,
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return {"error": r.stderr[-500:]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
 
 
 # --------------------------------------------------------------------------
@@ -432,9 +676,15 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
-    ap.add_argument("--leg", choices=["block_scatter", "sink_ring", "long_prefill", "block_attention"],
+    ap.add_argument("--leg", choices=["tiny", "block_scatter", "sink_ring", "long_prefill", "block_attention"],
                     help="run only this secondary workload and print its result (for profiling)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the headline decode calls (for a profiler run)")
+    ap.add_argument("--oracle-one-thread", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_one_thread:
+        print(json.dumps(oracle_one_thread()))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -448,8 +698,8 @@ def main():
     kvq.lib()
     torch.cuda.set_device(0)
     if args.leg:
-        legs = {"block_scatter": leg_block_scatter, "sink_ring": leg_sink_ring, "long_prefill": leg_long_prefill,
-                "block_attention": leg_block_attention}
+        legs = {"tiny": leg_tiny, "block_scatter": leg_block_scatter, "sink_ring": leg_sink_ring,
+                "long_prefill": leg_long_prefill, "block_attention": leg_block_attention}
         print(json.dumps({"leg": args.leg, "result": legs[args.leg]()}))
         return
 
@@ -457,11 +707,12 @@ def main():
     w = st.w
     R = args.replicas
     log(f"[bench] {R} replicas x {st.replica_bytes / 2**20:.0f} MiB of cache planes")
-    # one graph per replica for the whole step, one graph with a decode call
-    # per replica and one with the scatter phase per replica
+    # one graph per replica for the whole step; one graph of 128 decode calls
+    # (16 rounds over the replicas) and one of 128 scatter phases
     g_step = [capture(lambda r=r: st.step(r)) for r in range(R)]
-    g_dec = capture(lambda: [st.decode(r) for r in range(R)])
-    g_sc = capture(lambda: [st.scatter(r) for r in range(R)])
+    ROUNDS = 16
+    g_dec = capture(lambda: [st.decode(r) for _ in range(ROUNDS) for r in range(R)])
+    g_sc = capture(lambda: [st.scatter(r) for _ in range(ROUNDS) for r in range(R)])
     # a replay must give what the eager calls give
     st.step(0)
     torch.cuda.synchronize()
@@ -469,6 +720,11 @@ def main():
     g_step[0].replay()
     torch.cuda.synchronize()
     graph_exact = bool(torch.equal(eager, st.out))
+    if args.decode_only:
+        for _ in range(4):
+            g_dec.replay()
+        torch.cuda.synchronize()
+        return
     for i in range(args.warmup):
         g_step[i % R].replay()
     torch.cuda.synchronize()
@@ -485,14 +741,19 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
     step_ev_ms = ev0.elapsed_time(ev1) / args.steps
-    # per-phase times on the same stream: decode calls and scatter phases
-    reps = max(args.steps // R, 4)
-    dec_ms = replay_ms(g_dec, reps, R)
-    sc_ms = replay_ms(g_sc, reps, R)
+    # per-phase times on the launch stream, independent of --steps: the median
+    # over 16 replays of the per-call mean of 128 back-to-back calls
+    dec = replay_stats(g_dec, 16, ROUNDS * R)
+    sc = replay_stats(g_sc, 16, ROUNDS * R)
+    dec_ms, sc_ms = dec["median"], sc["median"]
     gbs = decode_bytes(w) / dec_ms / 1e6
     tokens = w.B
-    log(f"[bench] decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s), scatter+positions {sc_ms * 1e3:.2f} us, "
-        f"step {ms_per_step * 1e3:.2f} us (events {step_ev_ms * 1e3:.2f} us), graph replay exact: {graph_exact}")
+    log(f"[bench] decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s; p10 {dec['p10'] * 1e3:.2f} p90 {dec['p90'] * 1e3:.2f}), "
+        f"scatter+positions {sc_ms * 1e3:.2f} us, step {ms_per_step * 1e3:.2f} us (events {step_ev_ms * 1e3:.2f} us), "
+        f"graph replay exact: {graph_exact}")
+    del g_dec, g_sc
+    ceiling = stream_ceiling(decode_bytes(w))
+    log(f"[bench] read-only stream ceiling: {ceiling}")
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20
@@ -503,6 +764,7 @@ def main():
         torch.cuda.synchronize()
 
     traffic = measured_traffic()
+    ach = ceiling["decode_bytes"]["gbs"]
     result = {
         "metric": "quantized-KV decode attention HBM GB/s (% of peak); quant-scatter Mtokens/s",
         "value": round(gbs, 1),
@@ -521,6 +783,8 @@ def main():
                    "cache": "int8 per-token-head affine", "replicas": R,
                    "replica_mib": round(st.replica_bytes / 2**20, 1)},
         "decode_us": round(dec_ms * 1e3, 3),
+        "decode_us_p10_p90": [round(dec["p10"] * 1e3, 3), round(dec["p90"] * 1e3, 3)],
+        "decode_calls_timed": dec["calls"],
         "step_us_events": round(step_ev_ms * 1e3, 3),
         "graph_replay_bitexact": graph_exact,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -529,18 +793,30 @@ def main():
                           "note": ("positions + one K+V quant-scatter launch for the 8 new tokens of the step: "
                                    "launch-bound at this size; the 16384-token block scatter is "
                                    "secondary.block_scatter_16384x128")},
-        "roofline": {"bound": "hbm", "kernel": "kvq_sdpa_decode (sdpa_decode_split + sdpa_decode_combine)",
+        "roofline": {"bound": "hbm", "kernel": "sdpa_decode_mfma<128,4,bf16> (the whole kvq_sdpa_decode call: "
+                                               "one launch, split pass and split merge)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": decode_bytes(w)},
+                     "bytes_per_launch": decode_bytes(w),
+                     "achievable": {"gbs": ach, "frac_of_peak": round(ach / HBM_PEAK_GBS, 4),
+                                    "frac_achieved": round(gbs / ach, 4),
+                                    "how": ("read-only stream kernel, 16-byte loads, one launch reading the decode "
+                                            "call's byte count from buffers rotated over > 1 GiB, best of grids "
+                                            "1024/2048/4096, same timing method"),
+                                    "stream_1gib_gbs": ceiling["1GiB"]["gbs"],
+                                    "detail": ceiling}},
     }
     if not args.no_cpu_baseline:
         base, parity, _ = cpu_baseline(st, st.out)
+        log("[bench] oracle on one thread (C1, C2, C5)")
+        base["one_thread"] = oracle_one_thread_child()
         result["cpu_baseline"] = base
         result["parity_vs_oracle"] = parity
     if not args.no_secondary:
         log("[bench] secondary legs")
         sec = {}
+        sec["tiny_prefill64_decode32"] = leg_tiny()
+        log("[bench] tiny done")
         sec["block_scatter_16384x128"] = leg_block_scatter()
         log("[bench] block scatter done")
         sec["sink_ring_decode_p6000"] = leg_sink_ring()

@@ -64,6 +64,24 @@ def build(verbose: bool = False, extra=()) -> str:
     return LIB
 
 
+BENCH_CSRC = os.path.join(PKG, "bench_csrc")
+BENCH_LIB = os.path.join(PKG, "libkvq_bench.so")
+
+
+def build_bench(verbose: bool = False) -> str:
+    """libkvq_bench.so: the kernels bench.py uses to calibrate its rooflines
+    (not part of the libkvq C ABI)."""
+    srcs = sorted(os.path.join(BENCH_CSRC, f) for f in os.listdir(BENCH_CSRC) if f.endswith(".hip"))
+    tmp = BENCH_LIB + ".tmp"
+    r = subprocess.run([hipcc(), *COMMON, "-shared", "-o", tmp, *srcs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the bench kernels:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
+    if verbose:
+        print(f"built {BENCH_LIB}")
+    return BENCH_LIB
+
+
 TESTS_CSRC = os.path.join(os.path.dirname(PKG), "tests", "csrc")
 
 
@@ -89,3 +107,4 @@ def build_test_tools(verbose: bool = False) -> list:
 
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])
+    build_bench(verbose=True)
