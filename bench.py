@@ -724,6 +724,12 @@ def main():
         for _ in range(4):
             g_dec.replay()
         torch.cuda.synchronize()
+        if args.calibrate_copy_mib:
+            src = torch.empty(args.calibrate_copy_mib << 20, dtype=torch.uint8, device=DEV)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
         return
     for i in range(args.warmup):
         g_step[i % R].replay()
