@@ -24,10 +24,23 @@
 //  * q is rescaled by a power of two that puts max|q| of the tile in
 //    [2^14, 2^15); a bf16 element is exact in fp16 unless it lies more than
 //    2^31 below that maximum (it then rounds on fp16's subnormal grid, an
-//    error below 2^-39 of max|q|).  fp32 input uses hi + lo fp16 limbs.  P * scale_v enters the PV MFMA as
-//    hi + lo fp16 limbs.
-//  * Online softmax in the log2 domain with lazy rescaling (only when a
-//    column's max grows by more than 8).
+//    error below 2^-39 of max|q|).  fp32 input uses hi + lo fp16 limbs.
+//  * Online softmax in the log2 domain with a lazily raised reference m per
+//    query column that also carries the size of the V scales: p' = 2^(s - m)
+//    and P * scale_v enters the PV MFMA as hi + lo fp16 limbs of
+//    p' * scale_v.  m is raised (and the column's O and l rescaled by the
+//    same factor) only when a tile's bound max(s) + log2 max(scale_v) passes
+//    m + 15, and then set 7.5 below that bound: p' * scale_v stays below
+//    2^15 (fp16 ends at 2^16) and starts near 2^7.5, far above fp16's
+//    subnormals, whether the V scales are tiny or in the thousands.  O and l
+//    share the factor 2^m, which cancels in O / l.  Without a mask the scale
+//    maximum is one value for the workgroup's whole key range, found by a
+//    pass over its V scales before the tile loop (every slot below kv_len
+//    holds a written token then), so the tile loop pays one add for it.
+//    With a mask it runs per tile over the keys below kv_len that the mask
+//    leaves visible to the column (a hidden slot's scale may hold anything).
+//    The two choices round differently, so a zero mask and no mask agree
+//    within rounding rather than to the bit.
 //  * Software pipeline over tiles: the raw codes of tile t+2 stream into LDS
 //    (global_load_lds) and tile t+1 is dequantized while tile t's MFMAs run;
 //    one barrier per tile.  The tile loop is compiled separately for the
@@ -75,7 +88,13 @@ struct PrefillArgs {
     float* part_ml;        //                [B * Hq * Lq, kv_splits, 2] (max, sum) in log2 units
 };
 
-constexpr float PF_TAU = 8.0f;   // lazy rescale threshold (log2 units)
+// Reference raise rule (log2 units): raised when the bound on p' * scale_v
+// passes 2^PF_PV_HI, then set so that the bound is 2^PF_PV_SET; log2 of the
+// V-scale bound taken as at least PF_LSV_MIN (a column with no nonzero live
+// V scale adds nothing to O but still counts its p' in l).
+constexpr float PF_PV_HI = 15.0f;
+constexpr float PF_PV_SET = 7.5f;
+constexpr float PF_LSV_MIN = -48.0f;
 
 __device__ __forceinline__ uint32_t h2_sub(uint32_t a, uint32_t b) {
     half2_t r = __builtin_bit_cast(half2_t, a) - __builtin_bit_cast(half2_t, b);
@@ -105,6 +124,12 @@ __device__ __forceinline__ void dq_dword_u4p(uint32_t w, uint32_t off, uint32_t*
     out[1] = h2_sub(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u), off);
     out[2] = h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u), off);
     out[3] = h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u), off);
+}
+
+// x from another lane of the row by the DPP control CTRL (all rows, all banks)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t zp_pair(int zp, bool u4) {
@@ -177,14 +202,6 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
     constexpr bool F4 = QM == QM_MXFP4_B32;
     constexpr bool SC8 = QM == QM_MXFP4_B32 || QM == QM_MXFP8_B32;     // E8M0 block scales
-    // Block V scales are about amax / Q_MAX, so P * scale_v would drop into the
-    // fp16 subnormals for formats with a large Q_MAX (E5M2: 57344) and lose
-    // its digits against codes that large.  The staged V scales carry
-    // 2^VF = 2^(floor(log2 Q_MAX) - 4), removed exactly from the output.
-    constexpr int VF = QM == QM_FP8E5M2_B32 ? 11
-                     : (QM == QM_FP8E4M3_B32 || QM == QM_MXFP8_B32) ? 4
-                     : QM == QM_INT8_B32 ? 2 : 0;
-    constexpr float VSC = (float)(1 << VF);
     constexpr bool PERM = QM == QM_UINT4_TH;         // affine 4-bit: U4_ORDER element order
     constexpr int NG = D / 32;                       // scale blocks per row (= QK k-steps)
     constexpr int BN = PF_BN;
@@ -386,7 +403,9 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     };
 
     // Dequantize tile tt (raw codes in raw, metadata in mbuf) into the fp16
-    // tiles kt / vt and its key scales into ct / st_.
+    // tiles kt / vt, its K scales (times the q rescale) into ct, and into sv
+    // each key's V scale (block caches, masked calls only: the largest of its
+    // row's block scales), 0 past kv_len.
     auto stage = [&](auto vh, int tt, const uint8_t* raw, int mbuf, _Float16* kt, _Float16* vt, float* ct, float* sv,
                      float* bkt, float* bvt) __attribute__((always_inline)) {
         constexpr bool VH = decltype(vh)::value;
@@ -419,9 +438,18 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 if (tid < NG * BN) {
                     const bool in = (t0 + tt) * BN + tid % BN < kv_len;
                     bkt[tid] = in ? bks_lds[mbuf][tid] : 0.0f;
-                    bvt[tid] = in ? bvs_lds[mbuf][tid] * VSC : 0.0f;
+                    bvt[tid] = in ? bvs_lds[mbuf][tid] : 0.0f;
                 }
-                if (tid < BN) ct[tid] = (t0 + tt) * BN + tid < kv_len ? rs : 0.0f;
+                if (tid < BN) {
+                    const bool in = (t0 + tt) * BN + tid < kv_len;
+                    ct[tid] = in ? rs : 0.0f;
+                    if (has_mask) {                        // the masked path's V-scale bound
+                        float mx = 0.0f;
+#pragma unroll
+                        for (int gg = 0; gg < NG; ++gg) mx = fmaxf(mx, bvs_lds[mbuf][gg * BN + tid]);
+                        sv[tid] = in ? mx : 0.0f;
+                    }
+                }
             } else if (tid < BN) {
                 const bool in = (t0 + tt) * BN + tid < kv_len;
                 ct[tid] = in ? mks_lds[mbuf][tid] * rs : 0.0f;
@@ -471,6 +499,46 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
     };
 
+    // ---- no mask: log2 of the largest V scale of this workgroup's keys -----
+    // (block caches: of all their block scales); a per-wave maximum now, the
+    // workgroup's after the prologue's barrier.  The range is the split's
+    // share below kv_len, not cut at the causal bound, so skipping the tiles
+    // past that bound still changes no bit.
+    __shared__ float vb_lds[PF_WAVES];
+    float lsv_wg = PF_LSV_MIN;
+    if (!has_mask && n_tiles > 0) {
+        const int k0 = t0 * BN, k1 = min(kv_len, (t0 + per_split) * BN);
+        float x = 0.0f;
+        if constexpr (BLK) {
+            const int64_t g0 = (plane + k0) * NG;
+            const int cnt = (k1 - k0) * NG;
+            if constexpr (SC8) {
+                const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vs) + g0;
+                uint32_t mb = 0;
+#pragma unroll 8
+                for (int i = tid; i < cnt; i += 64 * PF_WAVES) mb = max(mb, (uint32_t)vb[i]);
+                x = mb ? blk_scale(mb) : 0.0f;
+            } else {
+#pragma unroll 8
+                for (int i = tid; i < cnt; i += 64 * PF_WAVES) x = fmaxf(x, a.vs[g0 + i]);
+            }
+        } else {
+#pragma unroll 8
+            for (int j = k0 + tid; j < k1; j += 64 * PF_WAVES) x = fmaxf(x, a.vs[plane + j]);
+        }
+        // wave maximum: within quads (xor 1, xor 2), half rows and rows
+        // (mirrors), then across rows (lanes l^16, l^32)
+        x = fmaxf(x, dpp_f32<0xB1>(x));
+        x = fmaxf(x, dpp_f32<0x4E>(x));
+        x = fmaxf(x, dpp_f32<0x141>(x));
+        x = fmaxf(x, dpp_f32<0x140>(x));
+        auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+        auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+        if (lane == 0) vb_lds[wave] = x;
+    }
+
     // ---- prologue: tiles 0 and 1 in flight, tile 0 dequantized ---------------
     if (n_tiles > 0) {
         fetch_meta(0);
@@ -483,6 +551,12 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (!has_mask) {
+            float x = 0.0f;
+#pragma unroll
+            for (int w = 0; w < PF_WAVES; ++w) x = fmaxf(x, vb_lds[w]);
+            lsv_wg = fmaxf(__builtin_amdgcn_logf(x), PF_LSV_MIN);
+        }
         if (vhalf) stage(std::true_type{}, 0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
         else stage(std::false_type{}, 0, raw_a, 0, k_a, v_a, c_a, s_a, bk_a, bv_a);
         __syncthreads();
@@ -560,6 +634,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         const bool tile_mask = (a.causal && j0 + BN - 1 > diag_lo) || (j0 + BN > kv_len) || has_mask || !q_live;
         float sv8[8];
         float tmax = NEG_INF;
+        uint32_t hid = 0;                                  // keys the mask hides from this column
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const float4 c4 = *reinterpret_cast<const float4*>(cc + kb * 16 + 4 * lg);
@@ -573,6 +648,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                         // a masked key is -inf whatever its (possibly unwritten) scale holds
                         const float mv = a.mask[(int64_t)q_row * a.S + key];
                         v = mv == NEG_INF ? NEG_INF : v + mv * 1.4426950408889634f;
+                        if (mv == NEG_INF) hid |= 1u << (kb * 4 + i);
                     }
                     if (key > lim || key >= kv_len || !q_live) v = NEG_INF;
                 }
@@ -587,9 +663,30 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
             tmax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
         }
-        const bool upd = tmax > m_run + PF_TAU;
+        // log2 of the largest V scale the column may weight in this tile
+        float lsv;
+        if (has_mask) {
+            float vmax = 0.0f;                             // staged 0 past kv_len
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const float4 v4 = *reinterpret_cast<const float4*>(sc + kb * 16 + 4 * lg);
+                const float vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, (hid >> (kb * 4 + i)) & 1u ? 0.0f : vv[i]);
+            }
+            auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(vmax), __float_as_uint(vmax), false, false);
+            vmax = fmaxf(__uint_as_float(w32[0]), __uint_as_float(w32[1]));
+            auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(vmax), __float_as_uint(vmax), false, false);
+            vmax = fmaxf(__uint_as_float(w16[0]), __uint_as_float(w16[1]));
+            lsv = fmaxf(__builtin_amdgcn_logf(vmax), PF_LSV_MIN);
+        } else {
+            lsv = lsv_wg;
+        }
+        // bound on log2(p' * scale_v) over the tile, less m_run
+        const float bnd = tmax + lsv;
+        const bool upd = bnd > m_run + PF_PV_HI;
         if (__any(upd)) {
-            const float mn = upd ? tmax : m_run;
+            const float mn = upd ? bnd - PF_PV_SET : m_run;
             const float al = m_run == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m_run - mn);
             m_run = mn;
             l_run *= al;
@@ -680,8 +777,8 @@ void sdpa_prefill_mfma(PrefillArgs a) {
     }
     if (!q_live) return;
     if (a.kv_splits > 1) {
-        // partial (m, l, o) of this key range for the split combine; o carries
-        // the V-scale factor 2^VF removed
+        // partial (m, l, o) of this key range for the split combine (o and l
+        // both in units of 2^m)
         const int64_t pr = (((int64_t)b * a.Hq + q_head) * a.Lq + q_row) * a.kv_splits + blockIdx.y;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -689,7 +786,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             for (int i = 0; i < 4; ++i) {
                 const int R = db * 16 + 4 * lg + i;
                 const int d = BLK ? R : (R % DG) * 8 + R / DG;
-                a.part_o[pr * D + d] = o_acc[db][i] * (1.0f / VSC);
+                a.part_o[pr * D + d] = o_acc[db][i];
             }
         }
         if (lg == 0) {
@@ -698,7 +795,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         }
         return;
     }
-    const float inv = l_run > 0.0f ? (1.0f / l_run) * (1.0f / VSC) : 0.0f;
+    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     const int64_t obase = (((int64_t)b * a.Hq + q_head) * a.Lq + q_row) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

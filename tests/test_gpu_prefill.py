@@ -8,7 +8,7 @@ import torch
 import oracle
 import quantized_kv_cache_head_amd as kvq
 import quantized_kv_cache_head_amd.workloads as wl
-from _gpu import DEV, check_attention, dev_input, say
+from _gpu import DEV, assert_cache_equal, check_attention, dev_input, new_pair, say
 from test_gpu_decode import fill_caches, wide_range_q
 
 pytestmark = pytest.mark.gpu
@@ -83,9 +83,13 @@ def test_prefill_non_causal_mask_and_garbage():
     ref = oracle.sdpa(q, K[1], V[1], kv_len, mask=mask, causal=False)
     got = run_prefill(q, K, V, kv_len, causal=False, mask=mask, out_dtype=torch.float32)
     check_attention(got, ref, "mask")
-    # zero mask == no mask (bit-identical), garbage past kv_len has no effect
+    # a zero mask agrees with no mask (the two bound the V scales over
+    # different key sets, so they round differently); garbage past kv_len
+    # has no effect (bit-identical)
     base = run_prefill(q, K, V, kv_len, causal=True)
-    assert torch.equal(base, run_prefill(q, K, V, kv_len, causal=True, mask=np.zeros((Lq, S), np.float32)))
+    ref_c = oracle.sdpa(q, K[1], V[1], kv_len, causal=True)
+    check_attention(base, ref_c, "no mask")
+    check_attention(run_prefill(q, K, V, kv_len, causal=True, mask=np.zeros((Lq, S), np.float32)), ref_c, "zero mask")
     for dc, _ in (K, V):
         dc.codes[:, :, kv_len:] = 0xFF
         dc.scales[:, :, kv_len:] = float("nan")
@@ -114,3 +118,55 @@ def test_prefill_query_wide_range_in_vector(qmode):
     say(f"prefill wide-range q qmode {qmode}")
     ref = oracle.sdpa(q, K[1], V[1], 400, causal=True)
     check_attention(run_prefill(q, K, V, 400, out_dtype=torch.float32), ref, "wide q prefill")
+
+
+ALL_MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+
+
+def scaled_v_caches(qmode, B, Hkv, S, D, n, vgain, seed):
+    """K at unit scale, V at vgain times unit scale, written by both sides."""
+    rng = np.random.default_rng(seed)
+    pairs = []
+    for which in range(2):
+        x = rng.standard_normal((B, Hkv, n, D)).astype(np.float32)
+        x[..., rng.choice(D, 4, replace=False)] *= 10
+        if which == 1:
+            x *= vgain
+        x = wl.to_bf16_values(x)
+        dc, hc = new_pair(qmode, B, Hkv, S, D)
+        slots = np.broadcast_to(np.arange(n, dtype=np.int32), (B, n)).copy()
+        kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
+        oracle.quant_scatter(hc, x, slots, parallel=True)
+        pairs.append((dc, hc))
+    torch.cuda.synchronize()
+    for dc, hc in pairs:
+        assert_cache_equal(dc, hc, "history")
+    return pairs[0], pairs[1]
+
+
+@pytest.mark.parametrize("vgain", [1e-3, 1e3])
+@pytest.mark.parametrize("qmode", ALL_MODES)
+def test_prefill_v_magnitude(qmode, vgain):
+    """V far from unit scale: P * scale_v neither overflows fp16 (amax in the
+    thousands gives scales in the hundreds) nor falls into its subnormals
+    (amax near 1e-3).  The output is linear in V, so the gate is the unit
+    gate times vgain.  The one-workgroup-per-tile kernel, the key-range split
+    (the reference m goes into the partials) and a masked call."""
+    B, Hkv, G, S, D, Lq, n = 1, 2, 4, 1024, 128, 128, 1000
+    assert kvq.sdpa_prefill_split_workspace_bytes(B, Hkv * G, Hkv, Lq, S, D) > 0
+    say(f"prefill V x{vgain} qmode {qmode}")
+    K, V = scaled_v_caches(qmode, B, Hkv, S, D, n, vgain, seed=100 + qmode)
+    q = wl.to_bf16_values(np.random.default_rng(101).standard_normal((B, Hkv * G, Lq, D)).astype(np.float32))
+    ref = oracle.sdpa(q, K[1], V[1], n, causal=True)
+    got = run_prefill(q, K, V, n, out_dtype=torch.float32)
+    check_attention(got / vgain, ref / vgain, f"V x{vgain} qmode {qmode}")
+    kl = torch.tensor([n], dtype=torch.int32, device=DEV)
+    got = kvq.sdpa_prefill_split(dev_input(q, True), K[0], V[0], kv_len=kl, causal=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attention(got / vgain, ref / vgain, f"split V x{vgain} qmode {qmode}")
+    # with an additive mask (the scale bound then runs over the keys the mask
+    # leaves visible to each row)
+    mask = np.where(np.random.default_rng(102).random((Lq, S)) < 0.3, -np.inf, 0.0).astype(np.float32)
+    ref = oracle.sdpa(q, K[1], V[1], n, mask=mask, causal=False)
+    got = run_prefill(q, K, V, n, causal=False, mask=mask, out_dtype=torch.float32)
+    check_attention(got / vgain, ref / vgain, f"masked V x{vgain} qmode {qmode}")
