@@ -218,8 +218,8 @@ class Llama8BStep:
         torch.cuda.synchronize()
 
     def scatter(self, r):
-        kvq.positions_full(self.start_pos, 1, self.w.S, self.slot)
-        kvq.quant_scatter_kv(self.k_new, self.v_new, self.slot, self.K[r], self.V[r])
+        # positions and the K+V quant-scatter in one launch (slot = start_pos)
+        kvq.quant_scatter_kv_full(self.k_new, self.v_new, self.start_pos, self.K[r], self.V[r])
 
     def decode(self, r):
         kvq.sdpa_decode(self.q, self.K[r], self.V[r], kv_len=self.kv_len, out=self.out, workspace=self.ws)
@@ -331,8 +331,8 @@ def roof(bound, achieved, peak, unit, **extra):
 
 def leg_tiny():
     """Tiny full-context int8 cache (B 1, 4/2 heads, D 64, 256 slots, fp32
-    inputs): the 64-token prefill (positions, K+V quant-scatter, causal
-    prefill attention) and 32 decode steps (positions, K+V quant-scatter,
+    inputs): the 64-token prefill (K+V quant-scatter at the device start
+    position, causal prefill attention) and 32 decode steps (the same scatter,
     decode attention), as one HIP graph; also the 32 decode steps alone."""
     w = wl.TINY
     K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
@@ -343,20 +343,17 @@ def leg_tiny():
         qp, kp, vp = (torch.from_numpy(a).to(DEV) for a in wl.tiny_decode(p, w))
         steps.append((qp, kp, vp, i32(p), i32(p + 1), torch.empty(1, dtype=torch.int32, device=DEV),
                       torch.empty((w.B, w.Hq, 1, w.D), dtype=torch.float32, device=DEV)))
-    sl0 = torch.empty(w.prefill, dtype=torch.int32, device=DEV)
     start0, kvl0 = i32(0), i32(w.prefill)
     out0 = torch.empty_like(q0)
     ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, w.S, w.D)
 
     def prefill():
-        kvq.positions_full(start0, w.prefill, w.S, sl0)
-        kvq.quant_scatter_kv(k0, v0, sl0, K, V)
+        kvq.quant_scatter_kv_full(k0, v0, start0, K, V)
         kvq.sdpa_prefill(q0, K, V, kv_len=kvl0, causal=True, out=out0)
 
     def decode_steps():
         for qp, kp, vp, st, kl, sl, o in steps:
-            kvq.positions_full(st, 1, w.S, sl)
-            kvq.quant_scatter_kv(kp, vp, sl, K, V)
+            kvq.quant_scatter_kv_full(kp, vp, st, K, V)
             kvq.sdpa_decode(qp, K, V, kv_len=kl, out=o, workspace=ws)
 
     def whole():
@@ -373,9 +370,9 @@ def leg_tiny():
         nb += 2 * w.B * w.Hkv * (w.D * 4 + row) + 2 * w.B * w.Hq * w.D * 4 + 2 * w.B * w.Hkv * (p + 1) * row
     us = t_all["median"] * 1e3
     return {"total_us": round(us, 2), "decode_step_us": round(t_dec["median"] * 1e3, 3),
-            "launches": 3 + 3 * w.decode_steps,
+            "launches": 2 + 2 * w.decode_steps,
             "roofline": roof("hbm", nb / us / 1e3, HBM_PEAK_GBS, "GB/s", bytes=nb,
-                             note="launch-bound: 99 small launches"),
+                             note="launch-bound: 66 small launches"),
             "note": "prefill 64 tokens + 32 decode steps, one HIP graph; median of 20 replays"}
 
 
@@ -796,7 +793,8 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
                           "tokens_per_step": tokens, "bytes": scatter_bytes(w),
-                          "note": ("positions + one K+V quant-scatter launch for the 8 new tokens of the step: "
+                          "note": ("one K+V quant-scatter launch at the device start position for the 8 new "
+                                   "tokens of the step: "
                                    "launch-bound at this size; the 16384-token block scatter is "
                                    "secondary.block_scatter_16384x128")},
         "roofline": {"bound": "hbm", "kernel": "sdpa_decode_mfma<128,4,bf16> (the whole kvq_sdpa_decode call: "

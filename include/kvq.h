@@ -151,6 +151,22 @@ kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int
                                 const kvq_cache* k_cache, const kvq_cache* v_cache,
                                 int32_t* err_flags, void* stream);
 
+/* The K and V update of a full-context cache in one launch, its slots
+ * derived on the device: exactly kvq_positions_full(start_pos, T, n_slots,
+ * slots, NULL, err_flags) followed by kvq_quant_scatter_kv(xk, xv, ...,
+ * slots, 0, k_cache, v_cache, err_flags) ([PR20351] commit notes: the new
+ * token's K and V go to the cache at the device-side input position, so a
+ * captured step needs no host value).  Token t of every batch row goes to
+ * slot p = *start_pos + t; a negative *start_pos writes nothing and sets
+ * KVQ_FLAG_SLOT_RANGE, a p >= n_slots writes nothing for that token and sets
+ * KVQ_FLAG_POS_CAPACITY.  start_pos: device int32 scalar.  Arguments, limits
+ * and errors otherwise as kvq_quant_scatter_kv (KVQ_ERR_NULL for a null
+ * start_pos when T > 0). */
+kvq_status kvq_quant_scatter_kv_full(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                     int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                     const int32_t* start_pos, const kvq_cache* k_cache,
+                                     const kvq_cache* v_cache, int32_t* err_flags, void* stream);
+
 /* Write slots for positions p = *start_pos + t, t in [0, T), attention-sink
  * layout ([PR24473]): n_slots = sink_size + window, slot = p for p < sink_size,
  * else sink_size + (p - sink_size) mod window.  slot_mapping_out: int32 [T].

@@ -37,7 +37,7 @@ NO_CAUSAL_SKIP = 1
 
 EXPORTS = (
     "kvq_status_string", "kvq_cache_bytes", "kvq_quant_scatter", "kvq_quant_scatter_flags", "kvq_quant_scatter_kv",
-    "kvq_positions_with_sink",
+    "kvq_quant_scatter_kv_full", "kvq_positions_with_sink",
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
     "kvq_sdpa_prefill_varlen", "kvq_sdpa_prefill_split_workspace_bytes", "kvq_sdpa_prefill_split",
@@ -80,6 +80,8 @@ def lib():
                                               _P, _P]
         L.kvq_quant_scatter_kv.restype = _I
         L.kvq_quant_scatter_kv.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _I64, _CP, _CP, _P, _P]
+        L.kvq_quant_scatter_kv_full.restype = _I
+        L.kvq_quant_scatter_kv_full.argtypes = [_P, _P, _I, _I, _I, _I, _I, _I64, _I64, _I64, _P, _CP, _CP, _P, _P]
         L.kvq_positions_with_sink.restype = _I
         L.kvq_positions_with_sink.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P]
         L.kvq_positions_ring.restype = _I
@@ -242,6 +244,22 @@ def quant_scatter_kv(xk: torch.Tensor, xv: torch.Tensor, slot_mapping: torch.Ten
     _check("kvq_quant_scatter_kv", lib().kvq_quant_scatter_kv(
         _ptr(xk), _ptr(xv), _dtype_code(xk), B, H, T, D, xk.stride(0), xk.stride(1), xk.stride(2),
         _ptr(slot_mapping), ssb, ctypes.byref(kc), ctypes.byref(vc), _ptr(err_flags), _stream(stream)))
+
+
+def quant_scatter_kv_full(xk: torch.Tensor, xv: torch.Tensor, start_pos: torch.Tensor, k_cache: Cache,
+                          v_cache: Cache, err_flags=None, stream=None):
+    """kvq_quant_scatter_kv_full: positions_full and quant_scatter_kv in one
+    launch (token t to slot *start_pos + t); start_pos a device int32 scalar."""
+    _need_cuda(xk, xv, start_pos, err_flags)
+    if xk.dim() != 4 or xk.stride(3) != 1 or xk.shape != xv.shape or xk.stride() != xv.stride() or xk.dtype != xv.dtype:
+        raise ValueError("xk and xv must be [B, H, T, D] with D contiguous, equal shapes, strides and dtype")
+    if start_pos.dtype != torch.int32 or start_pos.numel() != 1:
+        raise ValueError("start_pos must be one int32")
+    B, H, T, D = xk.shape
+    kc, vc = k_cache.struct(), v_cache.struct()
+    _check("kvq_quant_scatter_kv_full", lib().kvq_quant_scatter_kv_full(
+        _ptr(xk), _ptr(xv), _dtype_code(xk), B, H, T, D, xk.stride(0), xk.stride(1), xk.stride(2),
+        _ptr(start_pos), ctypes.byref(kc), ctypes.byref(vc), _ptr(err_flags), _stream(stream)))
 
 
 def positions_with_sink(start_pos, T, sink_size, window, slot_mapping_out, cache_positions, err_flags=None, stream=None):

@@ -108,10 +108,10 @@ KVQ_API kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, i
                                    slot_stride_b, cache, 0u, err_flags, stream);
 }
 
-KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
-                                        int64_t stride_b, int64_t stride_h, int64_t stride_t,
-                                        const int32_t* slot_mapping, int64_t slot_stride_b, const kvq_cache* k_cache,
-                                        const kvq_cache* v_cache, int32_t* err_flags, void* stream) {
+// K and V caches of one update: same mode and sizes, x as the scatter takes it.
+static kvq_status check_kv_update(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                  int64_t stride_b, int64_t stride_h, int64_t stride_t, const kvq_cache* k_cache,
+                                  const kvq_cache* v_cache) {
     kvq_status st = check_cache(k_cache);
     if (st != KVQ_OK) return st;
     if ((st = check_cache(v_cache)) != KVQ_OK) return st;
@@ -121,16 +121,41 @@ KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dt
     if (x_dtype != KVQ_F32 && x_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
     if (T < 0 || B != k_cache->batch || H != k_cache->heads || D != k_cache->head_dim) return KVQ_ERR_SHAPE;
     if (T == 0) return KVQ_OK;
-    if (!xk || !xv || !slot_mapping) return KVQ_ERR_NULL;
-    if (stride_b < 0 || stride_h < 0 || stride_t < 0 || slot_stride_b < 0) return KVQ_ERR_SHAPE;
+    if (!xk || !xv) return KVQ_ERR_NULL;
+    if (stride_b < 0 || stride_h < 0 || stride_t < 0) return KVQ_ERR_SHAPE;
     const int64_t vec = x_dtype == KVQ_BF16 ? 8 : 4;
     if (!aligned(xk, 16) || !aligned(xv, 16) || stride_b % vec || stride_h % vec || stride_t % vec)
         return KVQ_ERR_SHAPE;
     if (!scatter_size_ok(B, H, T, D)) return KVQ_ERR_SHAPE;
+    return KVQ_OK;
+}
+
+KVQ_API kvq_status kvq_quant_scatter_kv(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                        int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                        const int32_t* slot_mapping, int64_t slot_stride_b, const kvq_cache* k_cache,
+                                        const kvq_cache* v_cache, int32_t* err_flags, void* stream) {
+    const kvq_status st = check_kv_update(xk, xv, x_dtype, B, H, T, D, stride_b, stride_h, stride_t, k_cache, v_cache);
+    if (st != KVQ_OK || T == 0) return st;
+    if (!slot_mapping) return KVQ_ERR_NULL;
+    if (slot_stride_b < 0) return KVQ_ERR_SHAPE;
     return from_hip(kvq::launch_quant_scatter_kv(
         k_cache->qmode, x_dtype == KVQ_BF16, xk, xv, B, H, T, D, stride_b, stride_h, stride_t, slot_mapping,
         slot_stride_b, k_cache->n_slots, reinterpret_cast<uint8_t*>(k_cache->codes), k_cache->scales, k_cache->zps,
-        reinterpret_cast<uint8_t*>(v_cache->codes), v_cache->scales, v_cache->zps, err_flags,
+        reinterpret_cast<uint8_t*>(v_cache->codes), v_cache->scales, v_cache->zps, nullptr, err_flags,
+        reinterpret_cast<hipStream_t>(stream)));
+}
+
+KVQ_API kvq_status kvq_quant_scatter_kv_full(const void* xk, const void* xv, int x_dtype, int B, int H, int T, int D,
+                                             int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                                             const int32_t* start_pos, const kvq_cache* k_cache,
+                                             const kvq_cache* v_cache, int32_t* err_flags, void* stream) {
+    const kvq_status st = check_kv_update(xk, xv, x_dtype, B, H, T, D, stride_b, stride_h, stride_t, k_cache, v_cache);
+    if (st != KVQ_OK || T == 0) return st;
+    if (!start_pos) return KVQ_ERR_NULL;
+    return from_hip(kvq::launch_quant_scatter_kv(
+        k_cache->qmode, x_dtype == KVQ_BF16, xk, xv, B, H, T, D, stride_b, stride_h, stride_t, nullptr, 0,
+        k_cache->n_slots, reinterpret_cast<uint8_t*>(k_cache->codes), k_cache->scales, k_cache->zps,
+        reinterpret_cast<uint8_t*>(v_cache->codes), v_cache->scales, v_cache->zps, start_pos, err_flags,
         reinterpret_cast<hipStream_t>(stream)));
 }
 

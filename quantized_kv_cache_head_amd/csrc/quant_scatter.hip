@@ -68,7 +68,28 @@ struct ScatterArgs {
     int flags;             // QF_MX_SCALE_OCP for the MX modes
     uint32_t rows;         // B * H * T
     FastDiv div_t, div_h, div_lpr;   // by T, by H, by the lanes of a row (block modes: D / 8)
+    const int32_t* start_pos;        // non-null: slot = *start_pos + t (full-context layout), slots unused
 };
+
+// The slot of token t: from the slot mapping, or (full-context layout) the
+// position *start_pos + t itself, as kvq_positions_full gives it: a negative
+// start writes nothing and sets the slot-range flag, a position past the
+// cache writes nothing and sets the capacity flag.  report: the one lane of
+// the row that may set flags.
+__device__ __forceinline__ int token_slot(const ScatterArgs& a, int b, int t, bool report) {
+    if (!a.start_pos) return a.slots[(int64_t)b * a.ssb + t];
+    const int start = *a.start_pos;
+    if (start < 0) {
+        if (report && t == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
+        return -1;
+    }
+    const int64_t p = (int64_t)start + t;
+    if (p >= a.n_slots) {
+        if (report && a.err) atomicOr(a.err, KVQ_DEV_FLAG_POS_CAPACITY);
+        return -1;
+    }
+    return (int)p;
+}
 
 // Row index -> (b, h, t).
 __device__ __forceinline__ void row_coords(const ScatterArgs& a, uint32_t row, int& b, int& h, int& t) {
@@ -100,7 +121,7 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
         for (int i = 0; i < 8; ++i) v[p][i] = 0.0f;
     if (row < a.rows) {
         row_coords(a, row, b, h, t);
-        slot = a.slots[(int64_t)b * a.ssb + t];
+        slot = token_slot(a, b, t, h == 0 && li == 0);
         const int64_t xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -178,7 +199,7 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
     for (int i = 0; i < 8; ++i) v[i] = 0.0f;
     if (row < a.rows) {
         row_coords(a, row, b, h, t);
-        slot = a.slots[(int64_t)b * a.ssb + t];
+        slot = token_slot(a, b, t, h == 0 && g == 0 && qi == 0);
         load8<BF16>(a.x, (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st + d0, v);
         if (slot < -1 || slot >= a.n_slots) {
             if (h == 0 && g == 0 && qi == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
@@ -299,16 +320,20 @@ hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int 
                                 int64_t sb, int64_t sh, int64_t st, const int32_t* slots,
                                 int64_t ssb, int n_slots, uint8_t* codes, void* scales,
                                 int8_t* zps, int flags, int32_t* err, hipStream_t s) {
-    const ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err, flags};
+    const ScatterArgs a{x, B, H, T, D, sb, sh, st, slots, ssb, n_slots, codes, scales, zps, err, flags, 0, {}, {}, {},
+                        nullptr};
     return launch_scatter_n(qmode, bf16, a, a, 1, s);
 }
 
 hipError_t launch_quant_scatter_kv(int qmode, bool bf16, const void* xk, const void* xv, int B, int H, int T, int D,
                                    int64_t sb, int64_t sh, int64_t st, const int32_t* slots, int64_t ssb,
                                    int n_slots, uint8_t* kcodes, void* kscales, int8_t* kzps, uint8_t* vcodes,
-                                   void* vscales, int8_t* vzps, int32_t* err, hipStream_t s) {
-    const ScatterArgs ak{xk, B, H, T, D, sb, sh, st, slots, ssb, n_slots, kcodes, kscales, kzps, err, 0};
-    const ScatterArgs av{xv, B, H, T, D, sb, sh, st, slots, ssb, n_slots, vcodes, vscales, vzps, err, 0};
+                                   void* vscales, int8_t* vzps, const int32_t* start_pos, int32_t* err,
+                                   hipStream_t s) {
+    const ScatterArgs ak{xk, B, H, T, D, sb, sh, st, slots, ssb, n_slots, kcodes, kscales, kzps, err, 0, 0, {}, {}, {},
+                         start_pos};
+    const ScatterArgs av{xv, B, H, T, D, sb, sh, st, slots, ssb, n_slots, vcodes, vscales, vzps, err, 0, 0, {}, {}, {},
+                         start_pos};
     return launch_scatter_n(qmode, bf16, ak, av, 2, s);
 }
 

@@ -126,6 +126,23 @@ __device__ __forceinline__ void dq_dword_u4p(uint32_t w, uint32_t off, uint32_t*
     out[3] = h2_sub(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u), off);
 }
 
+// Largest of p[0, n) (non-negative floats; 0 for n <= 0) over the lanes of a
+// 512-thread workgroup, this lane's share: 16-byte loads where aligned.
+__device__ __forceinline__ float range_max_f32(const float* p, int n, int tid) {
+    const int h = min((int)(((16 - ((uintptr_t)p & 15)) & 15) >> 2), max(n, 0));
+    float x = tid < h ? p[tid] : 0.0f;
+    const float4* p4 = reinterpret_cast<const float4*>(p + h);
+    const int n4 = (n - h) >> 2;
+#pragma unroll 16
+    for (int i = tid; i < n4; i += 512) {
+        const float4 v = p4[i];
+        x = fmaxf(x, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+    const int tl = h + 4 * max(n4, 0);
+    if (tid < n - tl) x = fmaxf(x, p[tl + tid]);
+    return x;
+}
+
 // x from another lane of the row by the DPP control CTRL (all rows, all banks)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -513,18 +530,30 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             const int64_t g0 = (plane + k0) * NG;
             const int cnt = (k1 - k0) * NG;
             if constexpr (SC8) {
+                // E8M0 bytes: 16 at a time where aligned (the order of the
+                // codes is the order of the scales)
                 const uint8_t* vb = reinterpret_cast<const uint8_t*>(a.vs) + g0;
-                uint32_t mb = 0;
-#pragma unroll 8
-                for (int i = tid; i < cnt; i += 64 * PF_WAVES) mb = max(mb, (uint32_t)vb[i]);
+                const int h = min((int)((16 - ((uintptr_t)vb & 15)) & 15), cnt);
+                uint32_t mb = tid < h ? vb[tid] : 0u;
+                const uint4* v16 = reinterpret_cast<const uint4*>(vb + h);
+                const int n16 = (cnt - h) / 16;
+#pragma unroll 16
+                for (int i = tid; i < n16; i += 64 * PF_WAVES) {
+                    const uint4 w4 = v16[i];
+                    const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        mb = max(mb, max(max(ws[k] & 0xFFu, (ws[k] >> 8) & 0xFFu),
+                                         max((ws[k] >> 16) & 0xFFu, ws[k] >> 24)));
+                }
+                const int tl = h + n16 * 16;
+                if (tid < cnt - tl) mb = max(mb, (uint32_t)vb[tl + tid]);
                 x = mb ? blk_scale(mb) : 0.0f;
             } else {
-#pragma unroll 8
-                for (int i = tid; i < cnt; i += 64 * PF_WAVES) x = fmaxf(x, a.vs[g0 + i]);
+                x = range_max_f32(a.vs + g0, cnt, tid);
             }
         } else {
-#pragma unroll 8
-            for (int j = k0 + tid; j < k1; j += 64 * PF_WAVES) x = fmaxf(x, a.vs[plane + j]);
+            x = range_max_f32(a.vs + plane + k0, k1 - k0, tid);
         }
         // wave maximum: within quads (xor 1, xor 2), half rows and rows
         // (mirrors), then across rows (lanes l^16, l^32)

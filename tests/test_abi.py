@@ -120,6 +120,16 @@ def test_host_validation_errors(kvq):
                                   ctypes.byref(c), None, s) == 1
     assert L.kvq_quant_scatter_kv(None, None, 1, 1, 2, 0, 64, 0, 0, 64, None, 0, ctypes.byref(c),
                                   ctypes.byref(c), None, s) == 0
+    # the same update with its slots derived on the device: the same checks,
+    # and a null start_pos is rejected (T > 0)
+    assert L.kvq_quant_scatter_kv_full(None, None, 1, 1, 2, 4, 64, 0, 0, 64, None, ctypes.byref(c),
+                                       ctypes.byref(cv_other), None, s) == 2
+    assert L.kvq_quant_scatter_kv_full(None, None, 1, 1, 2, 4, 64, 0, 0, 64, None, ctypes.byref(c),
+                                       ctypes.byref(c), None, s) == 1
+    assert L.kvq_quant_scatter_kv_full(None, None, 5, 1, 2, 4, 64, 0, 0, 64, None, ctypes.byref(c),
+                                       ctypes.byref(c), None, s) == 3
+    assert L.kvq_quant_scatter_kv_full(None, None, 1, 1, 2, 0, 64, 0, 0, 64, None, ctypes.byref(c),
+                                       ctypes.byref(c), None, s) == 0
     # positions: window must be >= 1, T >= 0
     assert L.kvq_positions_with_sink(None, 4, 4, 0, None, None, None, s) == 2
     assert L.kvq_positions_ring(None, -1, 8, None, None, None, s) == 2

@@ -144,13 +144,15 @@ def _graph_of(fn):
     return g
 
 
-def test_full_context_step_graph_vs_oracle():
-    """The full-context decode step (positions, K+V quant-scatter, decode) as
-    one captured graph, replayed at three successive positions: before each
-    replay new q / K / V values and the device start position and kv_len are
-    written from the host.  After each replay the cache bytes equal the
-    oracle's (which takes the same step) and the output is within the
-    attention gate of the oracle's attention."""
+@pytest.mark.parametrize("fused", [False, True], ids=["positions+scatter", "scatter_kv_full"])
+def test_full_context_step_graph_vs_oracle(fused):
+    """The full-context decode step (positions, K+V quant-scatter, decode; or
+    the scatter that derives the slot from the device start position, and
+    decode) as one captured graph, replayed at three successive positions:
+    before each replay new q / K / V values and the device start position and
+    kv_len are written from the host.  After each replay the cache bytes
+    equal the oracle's (which takes the same step) and the output is within
+    the attention gate of the oracle's attention."""
     import oracle
     import quantized_kv_cache_head_amd.workloads as wl
     from _gpu import assert_cache_equal, check_attention, new_pair
@@ -173,8 +175,11 @@ def test_full_context_step_graph_vs_oracle():
     ws = kvq.decode_workspace(B, Hq, Hkv, S, D)
 
     def step():
-        kvq.positions_full(start, 1, S, slot)
-        kvq.quant_scatter_kv(knew, vnew, slot, K, V)
+        if fused:
+            kvq.quant_scatter_kv_full(knew, vnew, start, K, V)
+        else:
+            kvq.positions_full(start, 1, S, slot)
+            kvq.quant_scatter_kv(knew, vnew, slot, K, V)
         kvq.sdpa_decode(q, K, V, kv_len=kv_len, out=out, workspace=ws)
 
     def load(p):
@@ -199,7 +204,9 @@ def test_full_context_step_graph_vs_oracle():
             g.replay()
             torch.cuda.synchronize()
         sm, flags = oracle.positions_full(p, 1, S)
-        assert flags == 0 and int(slot.item()) == int(sm[0]) == p
+        assert flags == 0 and int(sm[0]) == p
+        if not fused:
+            assert int(slot.item()) == p
         oracle.quant_scatter(hk, kn, sm)
         oracle.quant_scatter(hv, vn, sm)
         assert_cache_equal(K, hk, f"K after the step at position {p}")
