@@ -27,11 +27,11 @@
  *                                   on dim 2, nibble packing on the last dim)
  *   cache scales     INT8_TH/UINT4_TH: float [B, H, S]
  *                    FP8E4M3_B32, FP8E5M2_B32, INT8_B32: float [B, H, S, D/32]
- *                    MXFP4_B32, MXFP8_B32: uint8 E8M0 [B, H, S, D/32]
+ *                    MXFP4_B32, MXFP8_B32, MXFP4E1M2_B32: uint8 E8M0 [B, H, S, D/32]
  *   cache zps        INT8_TH/UINT4_TH: int8 [B, H, S]; NULL for block modes
  *   q / out          [B, Hq, Lq, D] contiguous             ([ABADDON]
  *                                   forward_attention)
- *   row_bytes        D/2 for UINT4_TH and MXFP4_B32 (two codes per byte,
+ *   row_bytes        D/2 for UINT4_TH, MXFP4_B32 and MXFP4E1M2_B32 (two codes per byte,
  *                    element 2i in the low nibble), D for the other modes.
  *
  * Device error flags: entry points that take `int32_t* err_flags` (device,
@@ -66,7 +66,10 @@ typedef enum kvq_qmode {
     KVQ_MXFP4_B32 = 3,    /* per-32 block FP4-E2M1 + E8M0 scale [IQC] */
     KVQ_MXFP8_B32 = 4,    /* per-32 block FP8-E4M3FN + E8M0 scale (MX-FP8 mode) [IQC] */
     KVQ_FP8E5M2_B32 = 5,  /* per-32 block FP8-E5M2 + fp32 scale, amax/57344 [IQC] */
-    KVQ_INT8_B32 = 6      /* per-32 block symmetric int8 in a uint8 plane + fp32 scale, amax/127 [IQC] */
+    KVQ_INT8_B32 = 6,     /* per-32 block symmetric int8 in a uint8 plane + fp32 scale, amax/127 [IQC] */
+    KVQ_MXFP4E1M2_B32 = 7 /* per-32 block FP4-E1M2 + E8M0 scale (MX-FP4 mode, FLOAT4_E1M2 cache) [IQC]:
+                             sign, one exponent bit of bias 0, two mantissa bits, so magnitude code
+                             k (0..7) is worth k / 2; Q_MAX 3.5, emax 1; packed as MXFP4_B32 */
 } kvq_qmode;
 
 typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -79,7 +82,7 @@ typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
                                     (the per-tile causal bound switched off) */
 
 #define KVQ_MX_SCALE_OCP 1u      /* quantize, MX modes: E8M0 scale 2^(floor(log2 amax)
-                                    - emax) (emax 2 for E2M1, 8 for E4M3; elements
+                                    - emax) (emax 2 for E2M1, 1 for E1M2, 8 for E4M3; elements
                                     past Q_MAX saturate) instead of the smallest
                                     power of two >= amax / Q_MAX.  The reading of
                                     [IQC]'s round_scale = false. */
@@ -130,7 +133,7 @@ kvq_status kvq_quant_scatter(const void* x, int x_dtype, int B, int H, int T, in
                              const kvq_cache* cache, int32_t* err_flags, void* stream);
 
 /* kvq_quant_scatter with quantization options: flags = 0 is kvq_quant_scatter;
- * KVQ_MX_SCALE_OCP selects the floor rule for the E8M0 scale of MXFP4_B32 and
+ * KVQ_MX_SCALE_OCP selects the floor rule for the E8M0 scale of MXFP4_B32, MXFP4E1M2_B32 and
  * MXFP8_B32 caches.  KVQ_ERR_UNSUPPORTED for unknown bits or for an option the
  * cache's mode does not have. */
 kvq_status kvq_quant_scatter_flags(const void* x, int x_dtype, int B, int H, int T, int D,
@@ -219,7 +222,7 @@ size_t kvq_sdpa_decode_workspace_bytes(int B, int Hq, int Hkv, int n_slots, int 
  * over j in [0, kv_len), g = h / (Hq / Hkv), k_hat / v_hat dequantized on the
  * fly: (code - zp) * scale for the affine modes (INT8_TH, UINT4_TH),
  * decode(code) * scale of the element's 32-element block for the five block
- * modes (FP8E4M3_B32, FP8E5M2_B32, MXFP8_B32, MXFP4_B32, INT8_B32: the read
+ * modes (FP8E4M3_B32, FP8E5M2_B32, MXFP8_B32, MXFP4_B32, INT8_B32, MXFP4E1M2_B32: the read
  * side of [IQC]'s per-block write).  A slot at or past kv_len, or one the
  * mask sets to -inf, takes no part at all (its codes and scales may hold any
  * bytes, NaN included).  A row with no visible key gives 0.

@@ -22,9 +22,9 @@ _SRC = os.path.join(_HERE, "kvq_oracle.c")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
 INT8_TH, UINT4_TH, FP8E4M3_B32, MXFP4_B32 = 0, 1, 2, 3
-MXFP8_B32, FP8E5M2_B32, INT8_B32 = 4, 5, 6
-BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32)
-E8M0_MODES = (MXFP4_B32, MXFP8_B32)
+MXFP8_B32, FP8E5M2_B32, INT8_B32, MXFP4E1M2_B32 = 4, 5, 6, 7
+BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32, MXFP4E1M2_B32)
+E8M0_MODES = (MXFP4_B32, MXFP8_B32, MXFP4E1M2_B32)
 MX_SCALE_OCP = 1            # quantize option: MX scale by the OCP floor rule
 FLAG_SLOT_RANGE, FLAG_KVLEN, FLAG_POS_CAPACITY = 1, 2, 4
 
@@ -69,10 +69,12 @@ def _declare(L):
     L.orc_e2m1_encode.argtypes = [ctypes.c_float]
     L.orc_e2m1_decode.restype = ctypes.c_float
     L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+    L.orc_e1m2_decode.restype = ctypes.c_float
+    L.orc_e1m2_decode.argtypes = [ctypes.c_uint8]
     L.orc_e8m0_ceil.restype = ctypes.c_uint8
     L.orc_e8m0_ceil.argtypes = [ctypes.c_float]
     for name in ("orc_e4m3fn_encode_array", "orc_e2m1_encode_array", "orc_e8m0_ceil_array",
-                 "orc_e5m2_encode_array"):
+                 "orc_e5m2_encode_array", "orc_e1m2_encode_array"):
         f = getattr(L, name)
         f.restype = None
         f.argtypes = [_P, _P, _LL]
@@ -140,6 +142,13 @@ def e2m1_encode(y):
     return out
 
 
+def e1m2_encode(y):
+    y = _c(np.asarray(y, dtype=np.float32), np.float32)
+    out = np.empty(y.shape, np.uint8)
+    lib().orc_e1m2_encode_array(_ptr(y), _ptr(out), y.size)
+    return out
+
+
 def e8m0_ceil(s):
     s = _c(np.asarray(s, dtype=np.float32), np.float32)
     out = np.empty(s.shape, np.uint8)
@@ -173,6 +182,10 @@ def e2m1_decode(code: int) -> float:
     return lib().orc_e2m1_decode(int(code))
 
 
+def e1m2_decode(code: int) -> float:
+    return lib().orc_e1m2_decode(int(code))
+
+
 def affine_params(x, qmin: int, qmax: int):
     x = _c(np.asarray(x, dtype=np.float32), np.float32)
     scale = ctypes.c_float()
@@ -186,7 +199,7 @@ def affine_params(x, qmin: int, qmax: int):
 # --------------------------------------------------------------------------
 
 def row_bytes(qmode: int, D: int) -> int:
-    return D // 2 if qmode in (UINT4_TH, MXFP4_B32) else D
+    return D // 2 if qmode in (UINT4_TH, MXFP4_B32, MXFP4E1M2_B32) else D
 
 
 def scales_per_row(qmode: int, D: int) -> int:

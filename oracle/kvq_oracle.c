@@ -56,6 +56,13 @@
  *   R24 round_scale = false, and the OCP variant of MX-FP4: the scale is
  *       2^(floor(log2 amax) - emax), emax = 8 (E4M3) or 2 (E2M1), clamped to
  *       the E8M0 range; elements beyond Q_MAX then saturate (R8).
+ *   R27 FLOAT4_E1M2 (a cache dtype of the MX-FP4 mode on the IndexerQuantCache
+ *       page, parameter table): sign, one exponent bit, two mantissa bits,
+ *       exponent bias 0 (the IEEE rule 2^(k-1) - 1 for k = 1 exponent bit):
+ *       exponent 0 is subnormal 0.mm x 2^1, exponent 1 is 1.mm x 2^1, so
+ *       magnitude code c (0..7) is worth c / 2, Q_MAX = 3.5, emax = 1.  Under
+ *       a power-of-two block scale any other bias only moves the stored E8M0
+ *       exponent: the dequantized values stay the same.
  *
  * Parity pins: every function here is checked by the CPU tests against
  * closed forms, exhaustive grid search, library routines and hand-derived
@@ -75,6 +82,7 @@
 #define ORC_MXFP8_B32 4     /* E4M3FN codes, E8M0 scale per 32 ([IQC] quant_mode 0) */
 #define ORC_FP8E5M2_B32 5   /* E5M2 codes, fp32 scale per 32 ([IQC] Normal mode, E5M2 cache) */
 #define ORC_INT8_B32 6      /* int8 codes in a uint8 cache, fp32 scale per 32 ([IQC] Normal, INT8) */
+#define ORC_MXFP4E1M2_B32 7 /* FP4-E1M2 codes, E8M0 scale per 32 ([IQC] MX-FP4 mode, FLOAT4_E1M2 cache) */
 
 /* Quantize option: the MX scale by the OCP floor rule (R24) instead of the
  * smallest power of two >= amax / Q_MAX (R9). */
@@ -91,6 +99,7 @@
 /* Largest finite magnitudes (reading R6). */
 static const float E4M3_MAX = 448.0f;
 static const float E2M1_MAX = 6.0f;
+static const float E1M2_MAX = 3.5f;     /* R27 */
 
 /* Unbiased exponent floor(log2 a) of a positive normal fp32 value. */
 static int fp32_floor_log2(float a) {
@@ -158,6 +167,27 @@ float orc_e2m1_decode(uint8_t code) {
     static const float mags[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
     float v = mags[code & 7];
     return (code & 8) ? -v : v;
+}
+
+/* FP4 E1M2 (reading R27): bit 3 sign, bit 2 exponent, bits 1..0 mantissa.
+ * Exponent 0: 0.mm x 2^1 (subnormal); exponent 1: 1.mm x 2^1. */
+float orc_e1m2_decode(uint8_t code) {
+    int e = (code >> 2) & 1, m = code & 3;
+    float v = e ? ldexpf(1.0f + (float)m / 4.0f, 1) : ldexpf((float)m / 4.0f, 1);
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest E1M2 value, ties to the even code, |y| >= 3.5 saturates.  The
+ * values 0, .5, ..., 3.5 are evenly spaced (the subnormal step 2^-1 equals
+ * the normal one), so the nearest one to |y| is rne(2 |y|) / 2, and an even
+ * code is an even mantissa. */
+uint8_t orc_e1m2_encode(float y) {
+    uint8_t sign = signbit(y) ? 0x8 : 0x0;
+    float a = fabsf(y);
+    uint8_t mag;
+    if (!(a < E1M2_MAX)) mag = 7;
+    else mag = (uint8_t)rintf(a * 2.0f);
+    return sign | mag;
 }
 
 /* E8M0 scale for an MX block (reading R9): the smallest power of two that is
@@ -270,10 +300,12 @@ int orc_affine_code(float x, float scale, int zp, int qmin, int qmax) {
 /* ------------------------------------------------------------------------ */
 
 static int row_bytes(int qmode, int D) {
-    return (qmode == ORC_UINT4_TH || qmode == ORC_MXFP4_B32) ? D / 2 : D;
+    return (qmode == ORC_UINT4_TH || qmode == ORC_MXFP4_B32 || qmode == ORC_MXFP4E1M2_B32) ? D / 2 : D;
 }
 static int is_block(int qmode) { return qmode >= ORC_FP8E4M3_B32; }
-static int e8m0_scales(int qmode) { return qmode == ORC_MXFP4_B32 || qmode == ORC_MXFP8_B32; }
+static int e8m0_scales(int qmode) {
+    return qmode == ORC_MXFP4_B32 || qmode == ORC_MXFP8_B32 || qmode == ORC_MXFP4E1M2_B32;
+}
 static int scales_per_row(int qmode, int D) {
     return is_block(qmode) ? D / 32 : 1;
 }
@@ -335,16 +367,19 @@ static void quantize_row(int qmode, int flags, const float* x, int D,
             }
         } else {
             /* MX: E8M0 power-of-two scale X, codes of x / X (exact division) */
-            int fp4 = qmode == ORC_MXFP4_B32;
-            float qmax = fp4 ? E2M1_MAX : E4M3_MAX;
-            uint8_t e8 = (flags & ORC_MX_SCALE_OCP) ? orc_e8m0_floor(amax, fp4 ? 2 : 8)
+            int e1m2 = qmode == ORC_MXFP4E1M2_B32;
+            int fp4 = qmode == ORC_MXFP4_B32 || e1m2;
+            float qmax = e1m2 ? E1M2_MAX : fp4 ? E2M1_MAX : E4M3_MAX;
+            int emax = e1m2 ? 1 : fp4 ? 2 : 8;
+            uint8_t e8 = (flags & ORC_MX_SCALE_OCP) ? orc_e8m0_floor(amax, emax)
                                                     : orc_e8m0_ceil(amax / qmax);
             float X = orc_e8m0_value(e8);
             ((uint8_t*)scales)[g] = e8;
             if (fp4) {
                 for (int i = 0; i < 16; ++i) {
-                    uint8_t c0 = orc_e2m1_encode(xg[2 * i] / X);
-                    uint8_t c1 = orc_e2m1_encode(xg[2 * i + 1] / X);
+                    float y0 = xg[2 * i] / X, y1 = xg[2 * i + 1] / X;
+                    uint8_t c0 = e1m2 ? orc_e1m2_encode(y0) : orc_e2m1_encode(y0);
+                    uint8_t c1 = e1m2 ? orc_e1m2_encode(y1) : orc_e2m1_encode(y1);
                     codes[16 * g + i] = (uint8_t)(c0 | (c1 << 4));
                 }
             } else {
@@ -373,6 +408,11 @@ static double dequant_elem(int qmode, const uint8_t* codes, const void* scales,
         return (double)orc_e5m2_decode(codes[d]) * (double)((const float*)scales)[d / 32];
     case ORC_INT8_B32:
         return (double)(int8_t)codes[d] * (double)((const float*)scales)[d / 32];
+    case ORC_MXFP4E1M2_B32: {
+        int c = (codes[d / 2] >> (4 * (d & 1))) & 0xF;
+        return (double)orc_e1m2_decode((uint8_t)c) *
+               (double)orc_e8m0_value(((const uint8_t*)scales)[d / 32]);
+    }
     default: {
         int c = (codes[d / 2] >> (4 * (d & 1))) & 0xF;
         return (double)orc_e2m1_decode((uint8_t)c) *
@@ -630,6 +670,10 @@ int orc_sdpa_rows(const double* q, int B, int Hq, int Lq,
 void orc_e4m3fn_encode_array(const float* y, uint8_t* out, long long n) {
     for (long long i = 0; i < n; ++i) out[i] = orc_e4m3fn_encode(y[i]);
 }
+void orc_e1m2_encode_array(const float* y, uint8_t* out, long long n) {
+    for (long long i = 0; i < n; ++i) out[i] = orc_e1m2_encode(y[i]);
+}
+
 void orc_e2m1_encode_array(const float* y, uint8_t* out, long long n) {
     for (long long i = 0; i < n; ++i) out[i] = orc_e2m1_encode(y[i]);
 }

@@ -22,11 +22,11 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 # kvq_qmode
 INT8_TH, UINT4_TH, FP8E4M3_B32, MXFP4_B32 = 0, 1, 2, 3
-MXFP8_B32, FP8E5M2_B32, INT8_B32 = 4, 5, 6
+MXFP8_B32, FP8E5M2_B32, INT8_B32, MXFP4E1M2_B32 = 4, 5, 6, 7
 QMODES = {"int8": INT8_TH, "uint4": UINT4_TH, "fp8": FP8E4M3_B32, "mxfp4": MXFP4_B32, "mxfp8": MXFP8_B32,
-          "fp8e5m2": FP8E5M2_B32, "int8_block": INT8_B32}
-BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32)
-E8M0_MODES = (MXFP4_B32, MXFP8_B32)
+          "fp8e5m2": FP8E5M2_B32, "int8_block": INT8_B32, "mxfp4_e1m2": MXFP4E1M2_B32}
+BLOCK_MODES = (FP8E4M3_B32, MXFP4_B32, MXFP8_B32, FP8E5M2_B32, INT8_B32, MXFP4E1M2_B32)
+E8M0_MODES = (MXFP4_B32, MXFP8_B32, MXFP4E1M2_B32)
 # quantize options
 MX_SCALE_OCP = 1
 # kvq_dtype

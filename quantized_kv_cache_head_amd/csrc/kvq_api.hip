@@ -19,14 +19,16 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int row_bytes(int qmode, int D) { return (qmode == KVQ_UINT4_TH || qmode == KVQ_MXFP4_B32) ? D / 2 : D; }
+int row_bytes(int qmode, int D) {
+    return (qmode == KVQ_UINT4_TH || qmode == KVQ_MXFP4_B32 || qmode == KVQ_MXFP4E1M2_B32) ? D / 2 : D;
+}
 bool is_affine(int qmode) { return qmode == KVQ_INT8_TH || qmode == KVQ_UINT4_TH; }
-bool is_mx(int qmode) { return qmode == KVQ_MXFP4_B32 || qmode == KVQ_MXFP8_B32; }
+bool is_mx(int qmode) { return qmode == KVQ_MXFP4_B32 || qmode == KVQ_MXFP8_B32 || qmode == KVQ_MXFP4E1M2_B32; }
 int scales_per_row(int qmode, int D) { return is_affine(qmode) ? 1 : D / 32; }
 int scale_bytes(int qmode) { return is_mx(qmode) ? 1 : 4; }
 
 kvq_status check_dims(int qmode, int D) {
-    if (qmode < KVQ_INT8_TH || qmode > KVQ_INT8_B32) return KVQ_ERR_DTYPE;
+    if (qmode < KVQ_INT8_TH || qmode > KVQ_MXFP4E1M2_B32) return KVQ_ERR_DTYPE;
     if (D <= 0 || D > 8192) return KVQ_ERR_SHAPE;
     if (is_affine(qmode) ? (D % 8 != 0) : (D % 32 != 0)) return KVQ_ERR_SHAPE;
     return KVQ_OK;

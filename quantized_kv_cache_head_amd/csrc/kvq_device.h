@@ -96,6 +96,29 @@ __device__ __forceinline__ uint32_t cvt4_e5m2(const float* y) {
     const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_mag(y[0], 57344.0f), clamp_mag(y[1], 57344.0f), 0, false);
     return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(clamp_mag(y[2], 57344.0f), clamp_mag(y[3], 57344.0f), lo, true);
 }
+// FP4-E1M2 (sign, one exponent bit of bias 0, two mantissa bits): the
+// magnitudes k / 2, k = 0..7, are evenly spaced, so the code of y is
+// rne(2 |y|) with 2 |y| clamped to 7 (a NaN too), y's sign in bit 3.
+__device__ __forceinline__ uint32_t cvt8_e1m2(const float* y) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float k = __builtin_rintf(fminf(2.0f * __builtin_fabsf(y[i]), 7.0f));
+        w |= ((uint32_t)k | ((__float_as_uint(y[i]) >> 28) & 8u)) << (4 * i);
+    }
+    return w;
+}
+// Elements 2j and 2j + 1 of eight FP4-E1M2 codes (element i in nibble i of
+// w) as an exact fp16 pair: in [512, 1024) the fp16 ulp is 1/2, so magnitude
+// code k placed in the mantissa of 512 (0x6000) reads 512 + k / 2, and
+// subtracting 512 under the same sign leaves +-k / 2.
+__device__ __forceinline__ uint32_t e1m2_pair_h2(uint32_t w, int j) {
+    const uint32_t n = (w >> (8 * j)) & 0xFFu;                          // the two codes
+    const uint32_t sg = ((n & 0x8u) << 12) | ((n & 0x80u) << 24);       // their fp16 sign bits
+    const uint32_t a = 0x60006000u | sg | (n & 0x7u) | ((n & 0x70u) << 12);
+    const uint32_t b = 0x60006000u | sg;
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) - __builtin_bit_cast(half2_t, b));
+}
 __device__ __forceinline__ uint32_t cvt8_e2m1(const float* y) {
     uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, clamp_mag(y[0], 6.0f), clamp_mag(y[1], 6.0f), 1.0f, 0);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(y[2], 6.0f), clamp_mag(y[3], 6.0f), 1.0f, 1);

@@ -12,7 +12,7 @@
 namespace kvq {
 
 enum { QM_INT8_TH = 0, QM_UINT4_TH = 1, QM_FP8E4M3_B32 = 2, QM_MXFP4_B32 = 3, QM_MXFP8_B32 = 4, QM_FP8E5M2_B32 = 5,
-       QM_INT8_B32 = 6 };
+       QM_INT8_B32 = 6, QM_MXFP4E1M2_B32 = 7 };
 enum { QF_MX_SCALE_OCP = 1 };   // quantize option (kvq.h KVQ_MX_SCALE_OCP)
 
 hipError_t launch_quant_scatter(int qmode, bool bf16, const void* x, int B, int H, int T, int D,

@@ -242,15 +242,17 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
         if (qi == 0) reinterpret_cast<float*>(a.scales)[crow * gpr + g] = scale;
     } else {
         // MX: E8M0 power-of-two scale X; x / X is exact
-        constexpr bool F4 = QM == QM_MXFP4_B32;
-        const uint32_t e8 = (a.flags & QF_MX_SCALE_OCP) ? e8m0_floor(amax, F4 ? 2 : 8)
-                                                         : e8m0_ceil(amax / (F4 ? 6.0f : 448.0f));
+        constexpr bool E1M2 = QM == QM_MXFP4E1M2_B32;
+        constexpr bool F4 = QM == QM_MXFP4_B32 || E1M2;
+        constexpr int EMAX = E1M2 ? 1 : F4 ? 2 : 8;
+        constexpr float QMAX = E1M2 ? 3.5f : F4 ? 6.0f : 448.0f;
+        const uint32_t e8 = (a.flags & QF_MX_SCALE_OCP) ? e8m0_floor(amax, EMAX) : e8m0_ceil(amax / QMAX);
         const float inv = __uint_as_float(e8 == 254u ? 0x00400000u : (254u - e8) << 23);   // 1 / X, exact
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * inv;
         if constexpr (F4) {
-            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = cvt8_e2m1(y);
+            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = E1M2 ? cvt8_e1m2(y) : cvt8_e2m1(y);
         } else {
             *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(cvt4_e4m3fn(y), cvt4_e4m3fn(y + 4));
         }
@@ -307,6 +309,7 @@ static hipError_t launch_scatter_n(int qmode, bool bf16, ScatterArgs a, ScatterA
     switch (qmode) {
     case QM_FP8E4M3_B32: KVQ_BLK(QM_FP8E4M3_B32) break;
     case QM_MXFP4_B32: KVQ_BLK(QM_MXFP4_B32) break;
+    case QM_MXFP4E1M2_B32: KVQ_BLK(QM_MXFP4E1M2_B32) break;
     case QM_MXFP8_B32: KVQ_BLK(QM_MXFP8_B32) break;
     case QM_FP8E5M2_B32: KVQ_BLK(QM_FP8E5M2_B32) break;
     case QM_INT8_B32: KVQ_BLK(QM_INT8_B32) break;

@@ -154,11 +154,17 @@ __device__ __forceinline__ void codes_to_f32(const uint4 w, float out[U4 ? 32 : 
 // int8 as (code + 128) placed under the fp16 exponent of 1024 minus 1152.  The
 // per-block scale is applied afterwards, in fp32.
 template <int QM>
-__device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[QM == QM_MXFP4_B32 ? 16 : 8]) {
+constexpr bool fp4_mode = QM == QM_MXFP4_B32 || QM == QM_MXFP4E1M2_B32;
+
+template <int QM>
+__device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[fp4_mode<QM> ? 16 : 8]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if constexpr (QM == QM_MXFP4_B32) {
+        if constexpr (QM == QM_MXFP4E1M2_B32) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[4 * i + j] = e1m2_pair_h2(ws[i], j);
+        } else if constexpr (QM == QM_MXFP4_B32) {
             out[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 0));
             out[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 1));
             out[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(ws[i], 1.0f, 2));
@@ -178,11 +184,18 @@ __device__ __forceinline__ void blk_to_h2(const uint4 w, uint32_t out[QM == QM_M
 }
 
 template <int QM>
-__device__ __forceinline__ void blk_to_f32(const uint4 w, float out[QM == QM_MXFP4_B32 ? 32 : 16]) {
+__device__ __forceinline__ void blk_to_f32(const uint4 w, float out[fp4_mode<QM> ? 32 : 16]) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        if constexpr (QM == QM_MXFP4_B32) {
+        if constexpr (QM == QM_MXFP4E1M2_B32) {
+            // k / 2 with the code's sign (element e in nibble e)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t n = (ws[i] >> (4 * e)) & 0xFu;
+                out[8 * i + e] = __uint_as_float(__float_as_uint((float)(n & 7u) * 0.5f) | ((n & 8u) << 28));
+            }
+        } else if constexpr (QM == QM_MXFP4_B32) {
             const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 0);
             const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 1);
             const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(ws[i], 1.0f, 2);
@@ -351,8 +364,8 @@ __device__ __forceinline__ uint4 load16(gptr<uint8_t> base, uint32_t off) {
 template <int D, int QM, int G, bool QBF16>
 __global__ __launch_bounds__(256) void sdpa_decode_split(DecodeArgs a) {
     constexpr bool BLK = QM >= QM_FP8E4M3_B32;      // per-32 block scales, no zero point
-    constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
-    constexpr bool SC8 = QM == QM_MXFP4_B32 || QM == QM_MXFP8_B32;     // E8M0 block scales
+    constexpr bool U4 = QM == QM_UINT4_TH || fp4_mode<QM>;             // two codes per byte
+    constexpr bool SC8 = fp4_mode<QM> || QM == QM_MXFP8_B32;           // E8M0 block scales
     constexpr int SPR = D / 32;                      // block scales per row
     constexpr int SCB = SC8 ? 1 : 4;                 // bytes per block scale
     constexpr DecGeom GM = dec_geom(D, U4, G);
@@ -857,7 +870,7 @@ __global__ __launch_bounds__(D) void sdpa_decode_combine(const float* __restrict
 // enough splits for 4096 resident workgroups, and at least enough that every
 // slice fits the LDS row buffer.
 int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode) {
-    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32, Hq / Hkv);
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32 || qmode == QM_MXFP4E1M2_B32, Hq / Hkv);
     const int pairs = B * Hkv;
     const int max_useful = (S + DEC_CHUNK_ALIGN - 1) / DEC_CHUNK_ALIGN;
     int splits = (4096 + pairs - 1) / pairs;
@@ -885,6 +898,7 @@ static const void* split_kernel_for(int D, int qm, int G, bool qbf16) {
     case QM_MXFP8_B32: { KVQ_SK(DD, QM_MXFP8_B32) }          \
     case QM_FP8E5M2_B32: { KVQ_SK(DD, QM_FP8E5M2_B32) }      \
     case QM_INT8_B32: { KVQ_SK(DD, QM_INT8_B32) }            \
+    case QM_MXFP4E1M2_B32: { KVQ_SK(DD, QM_MXFP4E1M2_B32) }  \
     default: { KVQ_SK(DD, QM_MXFP4_B32) }                    \
     }
     if (D == 64) { KVQ_SKD(64) }
@@ -936,7 +950,7 @@ static int resident_workgroups(int D, int qm, int G, bool qbf16) {
 // one round (a second, partly filled round would run with little latency
 // hiding), within [rows fit in LDS, decode_splits_max].
 int decode_splits(int B, int Hq, int Hkv, int S, int D, int qmode, bool qbf16) {
-    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32, Hq / Hkv);
+    const DecGeom gm = dec_geom(D, qmode == QM_UINT4_TH || qmode == QM_MXFP4_B32 || qmode == QM_MXFP4E1M2_B32, Hq / Hkv);
     const int pairs = B * Hkv;
     const int hi = decode_splits_max(B, Hq, Hkv, S, D, qmode);
     const int need = (S + gm.rows_max - 1) / gm.rows_max;
@@ -981,6 +995,7 @@ static hipError_t dispatch_m(const DecodeArgs& a, int qmode, bool qbf16, int G, 
     case QM_MXFP8_B32: return dispatch_q<D, QM_MXFP8_B32>(a, qbf16, G, nsplit, s);
     case QM_FP8E5M2_B32: return dispatch_q<D, QM_FP8E5M2_B32>(a, qbf16, G, nsplit, s);
     case QM_INT8_B32: return dispatch_q<D, QM_INT8_B32>(a, qbf16, G, nsplit, s);
+    case QM_MXFP4E1M2_B32: return dispatch_q<D, QM_MXFP4E1M2_B32>(a, qbf16, G, nsplit, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -196,7 +196,10 @@ __device__ __forceinline__ int pf_vswb(int row) { return (row >> 3) & 3; }
 // 1152.
 template <int QM>
 __device__ __forceinline__ void blk_dword(uint32_t w, uint32_t* out) {
-    if constexpr (QM == QM_MXFP4_B32) {
+    if constexpr (QM == QM_MXFP4E1M2_B32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = e1m2_pair_h2(w, j);
+    } else if constexpr (QM == QM_MXFP4_B32) {
         out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
         out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
         out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
@@ -216,9 +219,9 @@ template <int D, int QM, int QL, int PL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sdpa_prefill_mfma(PrefillArgs a) {
     constexpr bool BLK = QM >= QM_FP8E4M3_B32;      // per-32 block scales
-    constexpr bool U4 = QM == QM_UINT4_TH || QM == QM_MXFP4_B32;       // two codes per byte
-    constexpr bool F4 = QM == QM_MXFP4_B32;
-    constexpr bool SC8 = QM == QM_MXFP4_B32 || QM == QM_MXFP8_B32;     // E8M0 block scales
+    constexpr bool F4 = QM == QM_MXFP4_B32 || QM == QM_MXFP4E1M2_B32;  // FP4 codes, two per byte
+    constexpr bool U4 = QM == QM_UINT4_TH || F4;                        // two codes per byte
+    constexpr bool SC8 = F4 || QM == QM_MXFP8_B32;                      // E8M0 block scales
     constexpr bool PERM = QM == QM_UINT4_TH;         // affine 4-bit: U4_ORDER element order
     constexpr int NG = D / 32;                       // scale blocks per row (= QK k-steps)
     constexpr int BN = PF_BN;
@@ -869,6 +872,7 @@ static hipError_t dispatch_pm(const PrefillArgs& a, int qmode, bool q_bf16, hipS
     case QM_MXFP8_B32: return dispatch_pf<D, QM_MXFP8_B32>(a, q_bf16, s);
     case QM_FP8E5M2_B32: return dispatch_pf<D, QM_FP8E5M2_B32>(a, q_bf16, s);
     case QM_INT8_B32: return dispatch_pf<D, QM_INT8_B32>(a, q_bf16, s);
+    case QM_MXFP4E1M2_B32: return dispatch_pf<D, QM_MXFP4E1M2_B32>(a, q_bf16, s);
     default: return hipErrorNotSupported;
     }
 }

@@ -14,6 +14,8 @@ uint8_t orc_e4m3fn_encode(float y);
 float orc_e4m3fn_decode(uint8_t code);
 uint8_t orc_e2m1_encode(float y);
 float orc_e2m1_decode(uint8_t code);
+uint8_t orc_e1m2_encode(float y);
+float orc_e1m2_decode(uint8_t code);
 uint8_t orc_e8m0_ceil(float s);
 uint8_t orc_e8m0_floor(float amax, int emax);
 uint8_t orc_e5m2_encode(float y);
@@ -54,7 +56,8 @@ static float normal(void) {
     return (float)(sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
 }
 
-static size_t scale_bytes(int qmode) { return (qmode == 3 || qmode == 4) ? 1 : 4; }
+static int mx_mode(int qmode) { return qmode == 3 || qmode == 4 || qmode == 7; }
+static size_t scale_bytes(int qmode) { return mx_mode(qmode) ? 1 : 4; }
 
 int main(void) {
     /* encoders and decoders on edge values */
@@ -62,25 +65,26 @@ int main(void) {
                           1e30f, -1e30f, INFINITY, -INFINITY, NAN, 6.0f, 5.0f, 0.25f, 0.75f};
     unsigned acc = 0;
     for (size_t i = 0; i < sizeof(edge) / sizeof(edge[0]); ++i) {
-        acc += orc_e4m3fn_encode(edge[i]) + orc_e2m1_encode(edge[i]) + orc_e5m2_encode(edge[i]);
+        acc += orc_e4m3fn_encode(edge[i]) + orc_e2m1_encode(edge[i]) + orc_e5m2_encode(edge[i]) + orc_e1m2_encode(edge[i]);
         acc += orc_e8m0_ceil(fabsf(edge[i])) + orc_e8m0_floor(fabsf(edge[i]), 8) + orc_e8m0_floor(fabsf(edge[i]), 2);
+        acc += orc_e8m0_floor(fabsf(edge[i]), 1);
     }
     for (int c = 0; c < 256; ++c) {
         volatile float f = orc_e4m3fn_decode((uint8_t)c) + orc_e5m2_decode((uint8_t)c);
         (void)f;
-        if (c < 16) { volatile float g = orc_e2m1_decode((uint8_t)c); (void)g; }
+        if (c < 16) { volatile float g = orc_e2m1_decode((uint8_t)c) + orc_e1m2_decode((uint8_t)c); (void)g; }
     }
     /* quantize + scatter, every mode, both flags, serial and parallel */
     enum { B = 2, H = 3, T = 5, D = 64, S = 16, Hq = 6, Lq = 3 };
     float* x = malloc(sizeof(float) * B * H * T * D);
     for (int i = 0; i < B * H * T * D; ++i) x[i] = normal() * (i % 37 == 0 ? 20.0f : 1.0f);
     int32_t slots[B * T] = {0, 3, -1, 15, 7, 2, -1, 99, 4, -5};
-    for (int qmode = 0; qmode <= 6; ++qmode) {
+    for (int qmode = 0; qmode <= 7; ++qmode) {
         const int rb = orc_row_bytes(qmode, D), spr = orc_scales_per_row(qmode, D);
         uint8_t* codes = calloc((size_t)B * H * S * rb, 1);
         void* scales = calloc((size_t)B * H * S * spr, scale_bytes(qmode));
         int8_t* zps = calloc((size_t)B * H * S, 1);
-        for (int qflags = 0; qflags <= ((qmode == 3 || qmode == 4) ? 1 : 0); ++qflags) {
+        for (int qflags = 0; qflags <= (mx_mode(qmode) ? 1 : 0); ++qflags) {
             int f1 = orc_quant_scatter_f(qmode, qflags, x, B, H, T, D, slots, T, S, codes, scales, zps);
             int f2 = orc_quant_scatter_par_f(qmode, qflags, x, B, H, T, D, slots, T, S, codes, scales, zps);
             if (f1 != 1 || f2 != 1) { printf("unexpected flags %d %d (mode %d)\n", f1, f2, qmode); return 1; }

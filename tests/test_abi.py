@@ -55,12 +55,13 @@ def test_cache_bytes(kvq):
     assert kvq.cache_bytes(kvq.MXFP8_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4, 0)
     assert kvq.cache_bytes(kvq.FP8E5M2_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
     assert kvq.cache_bytes(kvq.INT8_B32, 1, 1, 65536, 128) == (65536 * 128, 65536 * 4 * 4, 0)
+    assert kvq.cache_bytes(kvq.MXFP4E1M2_B32, 1, 1, 65536, 128) == (65536 * 64, 65536 * 4, 0)
     with pytest.raises(kvq.KvqError):
         kvq.cache_bytes(kvq.FP8E4M3_B32, 1, 1, 16, 48)        # D % 32 != 0
     with pytest.raises(kvq.KvqError):
         kvq.cache_bytes(kvq.UINT4_TH, 1, 1, 16, 60)           # D % 8 != 0
     with pytest.raises(kvq.KvqError):
-        kvq.cache_bytes(7, 1, 1, 16, 64)
+        kvq.cache_bytes(8, 1, 1, 16, 64)                      # no such mode
 
 
 def _fake_cache(kvq, qmode=0, B=1, H=2, S=64, D=64, zps=True):

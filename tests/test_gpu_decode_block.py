@@ -15,7 +15,7 @@ from test_gpu_decode import fill_caches, run_decode
 
 pytestmark = pytest.mark.gpu
 
-BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32, kvq.MXFP4E1M2_B32]
 
 
 @pytest.mark.parametrize("qmode", BLOCK_MODES)
@@ -104,11 +104,12 @@ def test_block_decode_every_code(qmode):
     say(f"block decode every code qmode={qmode}")
     K = kvq.Cache.empty(qmode, B, Hkv, S, D)
     V = kvq.Cache.empty(qmode, B, Hkv, S, D)
-    if qmode == kvq.MXFP4_B32:
+    if qmode in (kvq.MXFP4_B32, kvq.MXFP4E1M2_B32):
         nib = (np.arange(B * D) % 16).astype(np.uint8)
         nib = np.random.default_rng(5).permutation(nib).reshape(B, D)
         codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
-        ref = np.array([[oracle.e2m1_decode(int(c)) for c in row] for row in nib])
+        dec = oracle.e2m1_decode if qmode == kvq.MXFP4_B32 else oracle.e1m2_decode
+        ref = np.array([[dec(int(c)) for c in row] for row in nib])
     else:
         codes = np.arange(256, dtype=np.uint8).reshape(B, D)
         if qmode in (kvq.FP8E4M3_B32, kvq.MXFP8_B32):

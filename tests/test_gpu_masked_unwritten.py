@@ -16,7 +16,7 @@ from _gpu import DEV, assert_cache_equal, check_attention, dev_input, new_pair, 
 
 pytestmark = pytest.mark.gpu
 
-MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32]
+MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.MXFP4E1M2_B32]
 
 
 def ring_caches(qmode, B, Hkv, S, D, written, seed):

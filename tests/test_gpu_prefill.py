@@ -120,7 +120,8 @@ def test_prefill_query_wide_range_in_vector(qmode):
     check_attention(run_prefill(q, K, V, 400, out_dtype=torch.float32), ref, "wide q prefill")
 
 
-ALL_MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+ALL_MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32,
+             kvq.MXFP4E1M2_B32]
 
 
 def scaled_v_caches(qmode, B, Hkv, S, D, n, vgain, seed):

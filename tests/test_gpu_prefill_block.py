@@ -17,7 +17,7 @@ from test_gpu_prefill import run_prefill
 
 pytestmark = pytest.mark.gpu
 
-BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+BLOCK_MODES = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32, kvq.MXFP4E1M2_B32]
 
 
 @pytest.mark.parametrize("qmode", BLOCK_MODES)

@@ -11,8 +11,10 @@ from _gpu import DEV, assert_cache_equal, dev_input, new_pair, say
 
 pytestmark = pytest.mark.gpu
 
-MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
-BLOCK = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32,
+         kvq.MXFP4E1M2_B32]
+BLOCK = [kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32, kvq.MXFP4E1M2_B32]
+OCP = [(kvq.MXFP4_B32, True), (kvq.MXFP8_B32, True), (kvq.MXFP4E1M2_B32, True)]
 
 
 def _inputs(rng, B, H, T, D, bf16):
@@ -62,7 +64,7 @@ def test_scatter_other_head_dims(qmode, D):
     assert_cache_equal(dc, hc, f"D {D}")
 
 
-@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + [(kvq.MXFP4_B32, True), (kvq.MXFP8_B32, True)])
+@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + OCP)
 def test_scatter_block_mode_extremes(qmode, ocp):
     """Blocks at the edges of the encoders: exact ties, saturation, subnormal
     results, power-of-two amax, all-zero blocks, E8M0 clamp (both MX scale
@@ -139,7 +141,7 @@ def test_scatter_kv_single_launch(qmode):
     assert int(err.item()) & 1
 
 
-@pytest.mark.parametrize("qmode", [kvq.MXFP4_B32, kvq.MXFP8_B32])
+@pytest.mark.parametrize("qmode", [kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.MXFP4E1M2_B32])
 @pytest.mark.parametrize("D", [64, 256])
 def test_scatter_mx_ocp_scale_parity(qmode, D):
     """The OCP floor rule for the E8M0 scale (quantize option), bit-exact
@@ -182,7 +184,7 @@ def _unit_scale_rows(code_values, qmax, top):
     return x
 
 
-@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + [(kvq.MXFP4_B32, True), (kvq.MXFP8_B32, True)])
+@pytest.mark.parametrize("qmode,ocp", [(m, False) for m in BLOCK] + OCP)
 def test_scatter_block_every_rounding_boundary(qmode, ocp):
     """Every code, every tie between neighbouring codes and the values one ulp
     either side of it, at a block scale of exactly 1 (fp32 input), so the
@@ -192,6 +194,8 @@ def test_scatter_block_every_rounding_boundary(qmode, ocp):
     exercises saturation."""
     if qmode == kvq.MXFP4_B32:
         codes, qmax = [oracle.e2m1_decode(c) for c in range(8)], 6.0
+    elif qmode == kvq.MXFP4E1M2_B32:
+        codes, qmax = [oracle.e1m2_decode(c) for c in range(8)], 3.5
     elif qmode == kvq.FP8E5M2_B32:
         codes, qmax = [oracle.e5m2_decode(c) for c in range(0x7C)], 57344.0
     elif qmode == kvq.INT8_B32:
@@ -199,7 +203,7 @@ def test_scatter_block_every_rounding_boundary(qmode, ocp):
     else:
         codes, qmax = [oracle.e4m3fn_decode(c) for c in range(0x7F)], 448.0
     # OCP floor rule: the scale is 1 for any block maximum in [2^emax, 2^(emax+1))
-    top = (7.5 if qmode == kvq.MXFP4_B32 else 511.0) if ocp else qmax
+    top = {kvq.MXFP4_B32: 7.5, kvq.MXFP4E1M2_B32: 3.75}.get(qmode, 511.0) if ocp else qmax
     blocks = _unit_scale_rows(codes, qmax, top)
     D = 128
     T = -(-blocks.shape[0] // (D // 32))

@@ -16,7 +16,8 @@ from _gpu import DEV, assert_cache_equal, dev_input, new_pair, say
 
 pytestmark = pytest.mark.gpu
 
-MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32]
+MODES = [kvq.INT8_TH, kvq.UINT4_TH, kvq.FP8E4M3_B32, kvq.MXFP4_B32, kvq.MXFP8_B32, kvq.FP8E5M2_B32, kvq.INT8_B32,
+         kvq.MXFP4E1M2_B32]
 
 
 def bytes_equal(a: "kvq.Cache", b: "kvq.Cache", what):

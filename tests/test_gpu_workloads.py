@@ -208,7 +208,8 @@ def test_long_prefill_4bit_sampled_rows():
 
 
 @pytest.mark.parametrize("qmode,ocp", [(kvq.FP8E4M3_B32, False), (kvq.MXFP4_B32, False), (kvq.MXFP8_B32, False),
-                                       (kvq.FP8E5M2_B32, False), (kvq.INT8_B32, False), (kvq.MXFP4_B32, True),
+                                       (kvq.FP8E5M2_B32, False), (kvq.INT8_B32, False), (kvq.MXFP4E1M2_B32, False),
+                                       (kvq.MXFP4E1M2_B32, True), (kvq.MXFP4_B32, True),
                                        (kvq.MXFP8_B32, True)])
 def test_block_scatter_full(qmode, ocp):
     """x [16384, 128] bf16 with 1% outliers x20 into a 65536-slot block cache,

@@ -1,4 +1,4 @@
-"""Pins for the oracle's element encoders (FP8-E4M3FN, FP4-E2M1, E8M0).
+"""Pins for the oracle's element encoders (FP8-E4M3FN, FP4-E2M1, FP4-E1M2, E8M0).
 
 Each encoder is checked against an exhaustive nearest-grid search written from
 the format definitions alone (every code enumerated, its value computed from
@@ -27,6 +27,17 @@ def _e2m1_grid():
     for code in range(8):
         e, m = code >> 1, code & 1
         vals.append(m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1))
+    return np.array(vals, np.float64)
+
+
+def _e1m2_grid():
+    """FP4-E1M2 magnitudes from the bit fields: one exponent bit (bias 0, the
+    IEEE rule 2^(k-1) - 1 for k = 1), two mantissa bits; exponent 0 is
+    subnormal.  Index = 3-bit magnitude code."""
+    vals = []
+    for code in range(8):
+        e, m = code >> 2, code & 3
+        vals.append(m / 4 * 2.0 ** 1 if e == 0 else (1 + m / 4) * 2.0 ** (e - 0))
     return np.array(vals, np.float64)
 
 
@@ -112,6 +123,30 @@ def test_e2m1_ties(orc):
     for c in range(16):
         v = orc.e2m1_decode(c)
         assert orc.e2m1_encode([v])[0] == c
+
+
+def test_e1m2_grid_is_the_format(orc):
+    # the 8 magnitudes are evenly spaced: the subnormal step equals the normal one
+    assert list(_e1m2_grid()) == [0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0, 3.5]
+    for c in range(16):
+        v = orc.e1m2_decode(c)
+        assert v == (-1.0 if c & 8 else 1.0) * _e1m2_grid()[c & 7]
+        assert np.signbit(v) == bool(c & 8)
+
+
+def test_e1m2_exhaustive_bf16(orc):
+    y = _all_finite_bf16_as_f32()
+    assert np.array_equal(orc.e1m2_encode(y), _nearest_even(y, _e1m2_grid(), 0x8))
+
+
+def test_e1m2_ties(orc):
+    # 0.25 -> 0 (codes 0|1 tie, even 0), 0.75 -> 1.0 (1|2 -> 2), 1.25 -> 1.0 (2|3 -> 2),
+    # 1.75 -> 2.0 (3|4 -> 4), 2.25 -> 2.0 (4|5 -> 4), 2.75 -> 3.0 (5|6 -> 6),
+    # 3.25 -> 3.0 (6|7 -> 6); >= 3.5 saturates to 7; -0.1 -> -0 (code 8).
+    y = np.array([0.25, 0.75, 1.25, 1.75, 2.25, 2.75, 3.25, 3.5, 3.75, 100.0, -0.1], np.float32)
+    assert list(orc.e1m2_encode(y)) == [0, 2, 2, 4, 4, 6, 6, 7, 7, 7, 8]
+    for c in range(16):
+        assert orc.e1m2_encode([orc.e1m2_decode(c)])[0] == c
 
 
 def test_e8m0_smallest_power_of_two_at_or_above(orc):

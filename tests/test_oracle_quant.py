@@ -220,6 +220,43 @@ def test_mxfp8_block_worked_examples(orc, ex):
     assert np.all(codes[0, len(ex["codes_head"]):32] == 0)
 
 
+@pytest.mark.parametrize("ex", GOLD["mxfp4_e1m2_block"], ids=lambda e: e["name"])
+def test_mxfp4_e1m2_block_worked_examples(orc, ex):
+    flags = orc.MX_SCALE_OCP if ex["ocp"] else 0
+    codes, scales, _ = orc.quantize_rows(orc.MXFP4E1M2_B32, _block_x(ex["x_head"])[None], flags=flags)
+    assert scales[0, 0] == ex["e8m0"]
+    assert list(codes[0, :len(ex["packed_head"])]) == ex["packed_head"]
+
+
+@pytest.mark.parametrize("ocp", [False, True])
+def test_e1m2_block_properties(orc, ocp):
+    """MX-FP4 with E1M2 elements: the scale rules with Q_MAX 3.5 / emax 1, an
+    error of at most a quarter of X (half the grid step 0.5) where nothing
+    saturates, and the dequantized values on the grid k X / 2, |k| <= 7."""
+    rng = np.random.default_rng(29)
+    x = _vectors(rng, 400, 128)
+    flags = orc.MX_SCALE_OCP if ocp else 0
+    codes, scales, _ = orc.quantize_rows(orc.MXFP4E1M2_B32, x, flags=flags)
+    xhat = orc.dequantize_rows(orc.MXFP4E1M2_B32, codes, scales, None, 128).reshape(400, 4, 32)
+    g = x.reshape(400, 4, 32).astype(np.float64)
+    amax = np.abs(g).max(axis=2)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    ok = (amax > 0) & (scales > 0) & (scales < 254)
+    if ocp:
+        r = amax[ok] / X[ok]
+        assert np.all(r >= 2.0) and np.all(r < 4.0)
+    else:
+        assert np.all(X[ok] >= amax[ok] / 3.5) and np.all(X[ok] / 2 < amax[ok] / 3.5)
+    Xb = np.broadcast_to(X[..., None], g.shape)
+    k = xhat / (Xb / 2)
+    assert np.all(k == np.round(k)) and np.all(np.abs(k) <= 7)
+    sat = np.abs(g) / Xb > 3.5
+    assert ocp or not sat.any()
+    assert np.all(xhat[sat] == np.sign(g[sat]) * 3.5 * Xb[sat])
+    okb = np.broadcast_to(ok[..., None], g.shape) & ~sat
+    assert np.all(np.abs(g - xhat)[okb] <= 0.25 * Xb[okb])
+
+
 @pytest.mark.parametrize("ex", GOLD["mxfp4_ocp_block"], ids=lambda e: e["name"])
 def test_mxfp4_ocp_block_worked_examples(orc, ex):
     codes, scales, _ = orc.quantize_rows(orc.MXFP4_B32, _block_x(ex["x_head"])[None], flags=orc.MX_SCALE_OCP)
