@@ -143,6 +143,11 @@ __device__ __forceinline__ float range_max_f32(const float* p, int n, int tid) {
     return x;
 }
 
+// V scales are staged finite: a NaN or infinite one (which only a slot that
+// was never written can hold, behind the mask) becomes 0, so a dropped key's
+// p = 0 times its scale is exactly 0 without a select per key in the tile loop.
+__device__ __forceinline__ float finite_or_0(float x) { return __builtin_fabsf(x) <= 3.402823466e38f ? x : 0.0f; }
+
 // x from another lane of the row by the DPP control CTRL (all rows, all banks)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -458,7 +463,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
                 if (tid < NG * BN) {
                     const bool in = (t0 + tt) * BN + tid % BN < kv_len;
                     bkt[tid] = in ? bks_lds[mbuf][tid] : 0.0f;
-                    bvt[tid] = in ? bvs_lds[mbuf][tid] : 0.0f;
+                    bvt[tid] = in ? finite_or_0(bvs_lds[mbuf][tid]) : 0.0f;
                 }
                 if (tid < BN) {
                     const bool in = (t0 + tt) * BN + tid < kv_len;
@@ -473,7 +478,7 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             } else if (tid < BN) {
                 const bool in = (t0 + tt) * BN + tid < kv_len;
                 ct[tid] = in ? mks_lds[mbuf][tid] * rs : 0.0f;
-                sv[tid] = in ? mvs_lds[mbuf][tid] : 0.0f;
+                sv[tid] = in ? finite_or_0(mvs_lds[mbuf][tid]) : 0.0f;
             }
         } else {
             // thread -> (8 d, 4 keys); consecutive threads take consecutive d
@@ -740,9 +745,9 @@ void sdpa_prefill_mfma(PrefillArgs a) {
             const float svv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-                // a dropped key (p = 0) adds exactly 0, whatever its scale holds
-                const float pv0 = p8[e] == 0.0f ? 0.0f : p8[e] * svv[e];
-                const float pv1 = p8[e + 1] == 0.0f ? 0.0f : p8[e + 1] * svv[e + 1];
+                // a dropped key (p = 0) adds exactly 0: its staged scale is finite
+                const float pv0 = p8[e] * svv[e];
+                const float pv1 = p8[e + 1] * svv[e + 1];
                 const half2_t h2 = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(pv0, pv1));
                 pb[0][e] = h2[0];
                 pb[0][e + 1] = h2[1];
