@@ -148,6 +148,15 @@ __device__ __forceinline__ float range_max_f32(const float* p, int n, int tid) {
 // p = 0 times its scale is exactly 0 without a select per key in the tile loop.
 __device__ __forceinline__ float finite_or_0(float x) { return __builtin_fabsf(x) <= 3.402823466e38f ? x : 0.0f; }
 
+// max of two floats that are never signalling NaNs (scores, -inf), as one
+// v_max_f32: fmaxf on the result of a lane swap, which the compiler cannot
+// prove quiet, would first quieten both inputs under the IEEE mode
+__device__ __forceinline__ float fmax_q(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // x from another lane of the row by the DPP control CTRL (all rows, all banks)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
@@ -696,9 +705,9 @@ void sdpa_prefill_mfma(PrefillArgs a) {
         // max over the 4 lane groups of this column (lanes l, l^16, l^32, l^48)
         {
             auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+            tmax = fmax_q(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
             auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-            tmax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+            tmax = fmax_q(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
         }
         // log2 of the largest V scale the column may weight in this tile
         float lsv;
