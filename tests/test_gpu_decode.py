@@ -176,3 +176,30 @@ def test_decode_many_splits():
     ref = oracle.sdpa(q, K[1], V[1], kv_len)
     for od in (torch.bfloat16, torch.float32):
         check_attention(run_decode(q, K, V, kv_len, out_dtype=od), ref, f"many splits out {od}")
+
+
+@pytest.mark.parametrize("B,Hkv,S,kv_len", [(4, 8, 2048, 1531), (1, 1, 16384, 16000), (8, 8, 8192, 4096)])
+def test_decode_split_counters_return_to_zero(B, Hkv, S, kv_len):
+    """The split merge's per-(batch, KV head) counters are zero again after
+    every call, so one workspace serves calls in a row: three calls on the
+    same workspace give bit-identical outputs with no error flag, and the
+    counter words read back as zero after each."""
+    G, D = 4, 128
+    say(f"decode split counters B{B} Hkv{Hkv} S{S} kv_len {kv_len}")
+    K, V = fill_caches(kvq.INT8_TH, B, Hkv, S, D, kv_len, seed=31, outliers=False)
+    q_np = wl.to_bf16_values(np.random.default_rng(31).standard_normal((B, Hkv * G, 1, D)).astype(np.float32))
+    q = dev_input(q_np, True)
+    kl = torch.tensor([kv_len], dtype=torch.int32, device=DEV)
+    ws = kvq.decode_workspace(B, Hkv * G, Hkv, S, D, DEV)
+    outs = []
+    for i in range(3):
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        outs.append(kvq.sdpa_decode(q, K[0], V[0], kv_len=kl, out_dtype=torch.float32, workspace=ws, err_flags=err))
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, f"call {i}: error flags {int(err.item())}"
+        ctr = ws[: B * Hkv * 4].view(torch.int32)
+        assert int(ctr.abs().max().item()) == 0, f"call {i}: counters not reset: {ctr.cpu().tolist()[:16]}"
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    if B * S <= 65536:
+        check_attention(outs[0], oracle.sdpa(q_np, K[1], V[1], kv_len), "split counters")
