@@ -707,6 +707,16 @@ def main():
     # one graph per replica for the whole step; one graph of 128 decode calls
     # (16 rounds over the replicas) and one of 128 scatter phases
     g_step = [capture(lambda r=r: st.step(r)) for r in range(R)]
+    # the timed steps: one graph holds R steps, one per replica (as one
+    # token's step over R layers would), so the host's graph launch is paid
+    # once per R steps; a remainder of --steps uses the one-step graphs
+    g_steps = capture(lambda: [st.step(r) for r in range(R)])
+
+    def run_steps(k):
+        for _ in range(k // R):
+            g_steps.replay()
+        for i in range(k % R):
+            g_step[i].replay()
     ROUNDS = 16
     g_dec = capture(lambda: [st.decode(r) for _ in range(ROUNDS) for r in range(R)])
     g_sc = capture(lambda: [st.scatter(r) for _ in range(ROUNDS) for r in range(R)])
@@ -728,8 +738,7 @@ def main():
                 dst.copy_(src)
             torch.cuda.synchronize()
         return
-    for i in range(args.warmup):
-        g_step[i % R].replay()
+    run_steps(args.warmup)
     torch.cuda.synchronize()
 
     # timed region: K whole steps
@@ -737,8 +746,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
-        g_step[i % R].replay()
+    run_steps(args.steps)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -789,6 +797,8 @@ def main():
         "decode_us_p10_p90": [round(dec["p10"] * 1e3, 3), round(dec["p90"] * 1e3, 3)],
         "decode_calls_timed": dec["calls"],
         "step_us_events": round(step_ev_ms * 1e3, 3),
+        "step_timing": f"one step = K+V quant-scatter of the new token + decode of one cache replica; "
+                       f"replayed as graphs of {R} steps (one per replica, as one token's step over {R} layers)",
         "graph_replay_bitexact": graph_exact,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
