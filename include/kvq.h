@@ -247,6 +247,33 @@ kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq,
                            void* workspace, size_t workspace_bytes,
                            int32_t* err_flags, void* stream);
 
+/* One decode step of a full-context cache in a single launch: the new
+ * token's K and V written into the caches, then attention over them
+ * ([ABADDON] append followed by forward_attention; [PR20351] commit notes: the
+ * new token goes to the cache at the device-side input position, and the key
+ * loop stops at the filled length).  Exactly
+ *   kvq_quant_scatter_kv_full(xk, xv, x_dtype, B, Hkv, 1, D, x_stride_b,
+ *                             x_stride_h, 0, start_pos, k, v, err_flags)
+ * followed by kvq_sdpa_decode(q, ..., kv_len = *start_pos + 1, no mask, ...):
+ * the same cache bytes and the same output bits, and the same flags (a
+ * *start_pos < 0 writes nothing and sets KVQ_FLAG_SLOT_RANGE | KVQ_FLAG_KVLEN
+ * with kv_len 1; a *start_pos >= n_slots writes nothing and sets
+ * KVQ_FLAG_POS_CAPACITY | KVQ_FLAG_KVLEN with kv_len n_slots).
+ * xk, xv: [B, Hkv, 1, D] (x_dtype KVQ_F32 or KVQ_BF16) with element strides
+ *   x_stride_b, x_stride_h (>= 0) and unit stride along D; Hkv = k->heads.
+ * start_pos: device int32 scalar.  q, out, sm_scale, workspace (the size
+ *   kvq_sdpa_decode_workspace_bytes gives, same rules) as kvq_sdpa_decode.
+ * Supported: INT8_TH caches whose sizes the single-pass int8 kernel takes
+ *   (D 64, 128, 256; Hq / heads in {1, 2, 4, 8}, not 8 at D = 256;
+ *   n_slots % 4 == 0; 4-byte aligned zero-point arrays); anything else gives
+ *   KVQ_ERR_UNSUPPORTED with nothing enqueued. */
+kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B, int Hq,
+                                       const void* xk, const void* xv, int x_dtype,
+                                       int64_t x_stride_b, int64_t x_stride_h, const int32_t* start_pos,
+                                       const kvq_cache* k, const kvq_cache* v, float sm_scale,
+                                       void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                       int32_t* err_flags, void* stream);
+
 /* kvq_sdpa_decode with one filled length per batch row: kv_lens is a device
  * int32 array [B] (batch row b attends slots [0, kv_lens[b])), each clamped to
  * [1, n_slots] with KVQ_FLAG_KVLEN.  Otherwise as kvq_sdpa_decode; the same

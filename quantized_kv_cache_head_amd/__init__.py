@@ -41,7 +41,7 @@ EXPORTS = (
     "kvq_positions_ring", "kvq_positions_full", "kvq_build_mask",
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
     "kvq_sdpa_prefill_varlen", "kvq_sdpa_prefill_split_workspace_bytes", "kvq_sdpa_prefill_split",
-    "kvq_sdpa_prefill_split_varlen", "kvq_sdpa_decode_noalloc",
+    "kvq_sdpa_prefill_split_varlen", "kvq_sdpa_decode_noalloc", "kvq_sdpa_decode_append_full",
 )
 
 
@@ -94,6 +94,9 @@ def lib():
         L.kvq_sdpa_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.kvq_sdpa_decode.restype = _I
         L.kvq_sdpa_decode.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _SZ, _P, _P]
+        L.kvq_sdpa_decode_append_full.restype = _I
+        L.kvq_sdpa_decode_append_full.argtypes = [_P, _I, _I, _I, _P, _P, _I, _I64, _I64, _P, _CP, _CP, _F, _P, _I,
+                                                  _P, _SZ, _P, _P]
         L.kvq_sdpa_decode_noalloc.restype = _I
         L.kvq_sdpa_decode_noalloc.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _P]
         L.kvq_sdpa_prefill.restype = _I
@@ -322,6 +325,35 @@ def sdpa_decode(q, k: Cache, v: Cache, kv_len=None, mask=None, sm_scale=None, ou
         _ptr(q), _dtype_code(q), B, Hq, ctypes.byref(kc), ctypes.byref(vc), _ptr(kv_len), _ptr(mask), msb,
         int(bool(mask_is_causal)), float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(err_flags), _stream(stream)))
+    return out
+
+
+def sdpa_decode_append_full(q, xk, xv, start_pos, k: Cache, v: Cache, sm_scale=None, out=None, out_dtype=None,
+                            workspace=None, err_flags=None, stream=None):
+    """kvq_sdpa_decode_append_full: the new token's K and V (xk, xv [B, Hkv, 1,
+    D], D contiguous) written at slot *start_pos of full-context caches, then
+    decode attention of q [B, Hq, 1, D] over kv_len = *start_pos + 1, in one
+    launch; returns out [B, Hq, 1, D]."""
+    _need_cuda(q, xk, xv, start_pos, out, workspace, err_flags)
+    B, Hq, Lq, D = q.shape
+    if Lq != 1 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 1, D]")
+    if (xk.dim() != 4 or xk.shape != xv.shape or xk.shape[2] != 1 or xk.stride(3) != 1 or xv.stride(3) != 1
+            or xk.stride()[:2] != xv.stride()[:2] or xk.dtype != xv.dtype):
+        raise ValueError("xk and xv must be [B, Hkv, 1, D] with D contiguous, equal shapes, strides and dtype")
+    if start_pos.dtype != torch.int32 or start_pos.numel() != 1:
+        raise ValueError("start_pos must be one int32")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, k.H, k.S, D, q.device)
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_decode_append_full", lib().kvq_sdpa_decode_append_full(
+        _ptr(q), _dtype_code(q), B, Hq, _ptr(xk), _ptr(xv), _dtype_code(xk), xk.stride(0), xk.stride(1),
+        _ptr(start_pos), ctypes.byref(kc), ctypes.byref(vc), float(sm_scale), _ptr(out), _dtype_code(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_flags), _stream(stream)))
     return out
 
 

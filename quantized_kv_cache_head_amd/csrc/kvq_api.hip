@@ -390,6 +390,60 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
                             workspace, workspace_bytes, err_flags, stream);
 }
 
+KVQ_API kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B, int Hq, const void* xk,
+                                               const void* xv, int x_dtype, int64_t x_stride_b,
+                                               int64_t x_stride_h, const int32_t* start_pos, const kvq_cache* k,
+                                               const kvq_cache* v, float sm_scale, void* out, int out_dtype,
+                                               void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                               void* stream) {
+    kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
+    if (st != KVQ_OK) return st;
+    if (!xk || !xv || !start_pos) return KVQ_ERR_NULL;
+    if (x_dtype != KVQ_F32 && x_dtype != KVQ_BF16) return KVQ_ERR_DTYPE;
+    if (x_stride_b < 0 || x_stride_h < 0) return KVQ_ERR_SHAPE;
+    const size_t es = x_dtype == KVQ_BF16 ? 2 : 4;
+    if (!aligned(xk, es) || !aligned(xv, es)) return KVQ_ERR_SHAPE;
+    const DecodePlan plan = decode_plan(q_dtype, B, Hq, k, v);
+    if (!plan.single) return KVQ_ERR_UNSUPPORTED;
+    const size_t ctr = decode_ctr_bytes(B, k->heads);
+    if (!workspace || workspace_bytes < ctr + plan.part_bytes || !aligned(workspace, 16)) return KVQ_ERR_WORKSPACE;
+    kvq::DecodeLaunch L;
+    L.q = q;
+    L.q_bf16 = q_dtype == KVQ_BF16;
+    L.B = B;
+    L.Hq = Hq;
+    L.Hkv = k->heads;
+    L.S = k->n_slots;
+    L.D = k->head_dim;
+    L.qmode = k->qmode;
+    L.kc = reinterpret_cast<const uint8_t*>(k->codes);
+    L.ks = reinterpret_cast<const float*>(k->scales);
+    L.kz = k->zps;
+    L.vc = reinterpret_cast<const uint8_t*>(v->codes);
+    L.vs = reinterpret_cast<const float*>(v->scales);
+    L.vz = v->zps;
+    L.kv_len = nullptr;
+    L.kv_len_sb = 0;
+    L.mask = nullptr;
+    L.mask_sb = 0;
+    L.sm_scale = sm_scale;
+    L.out = out;
+    L.out_bf16 = out_dtype == KVQ_BF16;
+    L.nsplit = plan.nsplit;
+    L.err = err_flags;
+    L.ctr = reinterpret_cast<unsigned*>(workspace);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + ctr);
+    L.part_ml = part;
+    L.part_o = part + (size_t)B * Hq * plan.nsplit * 2;
+    L.start_pos = start_pos;
+    L.xk = xk;
+    L.xv = xv;
+    L.x_bf16 = x_dtype == KVQ_BF16;
+    L.xsb = x_stride_b;
+    L.xsh = x_stride_h;
+    return from_hip(kvq::launch_sdpa_decode_mfma(L, reinterpret_cast<hipStream_t>(stream)));
+}
+
 KVQ_API kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,
                                           const kvq_cache* v, const int32_t* kv_lens, const float* mask,
                                           int64_t mask_stride_b, float sm_scale, void* out, int out_dtype,

@@ -55,6 +55,14 @@ struct DecodeLaunch {
     float* part_ml;
     int32_t* err;
     unsigned* ctr = nullptr;   // single-pass kernel: per-plane tickets (zero between calls)
+    // single-pass kernel, append variant (start_pos set): the new token's K
+    // and V rows [B, Hkv, D] (element strides xsb, xsh) go to slot *start_pos
+    // and kv_len is *start_pos + 1 (kv_len and mask unused)
+    const int32_t* start_pos = nullptr;
+    const void* xk = nullptr;
+    const void* xv = nullptr;
+    bool x_bf16 = false;
+    int64_t xsb = 0, xsh = 0;
 };
 
 int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode);

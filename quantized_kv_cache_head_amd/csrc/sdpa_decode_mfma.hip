@@ -152,9 +152,39 @@ struct MfmaArgs {
     void* out;
     int out_bf16;
     int32_t* err;
+    // append variant: the new token's K and V rows x[b, kv head, :] (element
+    // strides xsb, xsh), written at slot *start_pos of the full-context cache
+    // and attended with kv_len = *start_pos + 1
+    const void* xk;
+    const void* xv;
+    int x_bf16;
+    int64_t xsb, xsh;
+    const int32_t* start_pos;
 };
 
-template <int D, int G, bool QBF16>
+// Affine int8 code parameters of one row spread over a wave (E elements per
+// lane), with single IEEE fp32 operations in the order of the quant-scatter
+// kernel, so scale, zero point and codes are bit-identical to it: lo = min(0,
+// min x), hi = max(0, max x), scale = max((hi - lo) / 255, 2^-23), zp =
+// clamp(-128 - rne(lo / scale)), code = clamp(rne(x / scale) + zp).
+template <int E>
+__device__ __forceinline__ void affine_row_codes(const float (&x)[E], int (&code)[E], float& scale, int& zp) {
+    float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) { lo = fminf(lo, x[e]); hi = fmaxf(hi, x[e]); }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        lo = fminf(lo, __shfl_xor(lo, o, 64));
+        hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+    }
+    const float range = hi - lo;
+    scale = fmaxf(range / 255.0f, 0x1p-23f);
+    zp = min(max(-128 - (int)__builtin_rintf(lo / scale), -128), 127);
+#pragma unroll
+    for (int e = 0; e < E; ++e) code[e] = min(max((int)__builtin_rintf(x[e] / scale) + zp, -128), 127);
+}
+
+template <int D, int G, bool QBF16, bool APPEND>
 __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) {
     using GM = MGeom<D>;
     using HM = MHeads<G>;
@@ -218,7 +248,21 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     const int wp = split * NW + wave;                 // this wave's position among them
 
     typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
-    int kv_len = a.kv_len ? *(cptr_i32)(a.kv_len + (int64_t)b * a.kv_len_sb) : S;
+    int kv_len = S;
+    int p_new = -1;                                   // slot this call writes (append variant)
+    if constexpr (APPEND) {
+        const int p = *(cptr_i32)(a.start_pos);
+        // exactly the flags of the K+V full-context scatter followed by a
+        // decode with kv_len = p + 1
+        if (p < 0 || p >= S) {
+            if (a.err && split == 0 && tid == 0) atomicOr(a.err, p < 0 ? KVQ_DEV_FLAG_SLOT_RANGE : KVQ_DEV_FLAG_POS_CAPACITY);
+        } else {
+            p_new = p;
+        }
+        kv_len = p < S ? p + 1 : S + 1;
+    } else {
+        if (a.kv_len) kv_len = *(cptr_i32)(a.kv_len + (int64_t)b * a.kv_len_sb);
+    }
 
     auto slot = [&](auto UC) __attribute__((always_inline)) -> uint8_t* {
         constexpr int U = decltype(UC)::value;
@@ -303,6 +347,36 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     }
     const int nunits = (kv_len + MKEYS - 1) / MKEYS;
     const int nsteps = wp < nunits ? (nunits - wp + W - 1) / W : 0;
+    // Append variant: the new slot p_new = kv_len - 1 lies in the last unit,
+    // u_new, which belongs to wave u_new mod W at its last step t_new.  That
+    // wave loads the new K and V rows now (ahead of its cache copies, so any
+    // wait for the copies covers them too), quantizes them, writes them to the
+    // cache and patches them into its tile once the unit's copies have landed.
+    // No other wave reads the slot (clamped rows past the plane may read it
+    // while it is written; they lie at or past kv_len and take no part).
+    constexpr int XE = D / 64;                        // row elements per lane
+    const int u_new = p_new >= 0 ? p_new / MKEYS : 0;
+    const bool owner = APPEND && p_new >= 0 && u_new % W == wp;
+    const int t_new = u_new / W;
+    const int r_new = p_new - u_new * MKEYS;
+    float xnew[2][XE];
+    if constexpr (APPEND) {
+#pragma unroll
+        for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+            for (int e = 0; e < XE; ++e) xnew[kv][e] = 0.0f;
+        if (owner) {
+            const int64_t xo = (int64_t)b * a.xsb + (int64_t)g * a.xsh + lane * XE;
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv) {
+                const void* xp = kv ? a.xv : a.xk;
+#pragma unroll
+                for (int e = 0; e < XE; ++e)
+                    xnew[kv][e] = a.x_bf16 ? bf16_lo(reinterpret_cast<const uint16_t*>(xp)[xo + e])
+                                           : reinterpret_cast<const float*>(xp)[xo + e];
+            }
+        }
+    }
     // the q copies were issued with the kv_len load and take about as long:
     // they have landed before the cache copies go out
     __builtin_amdgcn_sched_barrier(0);
@@ -461,6 +535,40 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         const int later = min(PD - 1, nsteps - 1 - t);
         wait_units(later);
         const uint8_t* src = slot(UC);
+        if constexpr (APPEND) {
+            if (owner && t == t_new) {
+                // quantize the new rows, write them to the cache, and put them
+                // in the tile where the copies put row r_new: chunk c of the
+                // row at r_new D + 16 (c ^ sw(r_new)), the scales in metadata
+                // word 4 (r_new % 16) + r_new / 16, the zero points at byte r_new
+                uint8_t* dst = const_cast<uint8_t*>(src);
+                const int64_t crow = prow + p_new;
+#pragma unroll
+                for (int kv = 0; kv < 2; ++kv) {
+                    int code[XE];
+                    float scale;
+                    int zp;
+                    affine_row_codes<XE>(xnew[kv], code, scale, zp);
+                    uint8_t* cg = const_cast<uint8_t*>(kv ? a.vc : a.kc) + crow * D + lane * XE;
+                    uint8_t* tl = dst + (kv ? OFF_V : 0) + r_new * D;
+#pragma unroll
+                    for (int e = 0; e < XE; ++e) {
+                        const int d = lane * XE + e;
+                        cg[e] = (uint8_t)code[e];
+                        tl[16 * ((d >> 4) ^ GM::sw(r_new)) + (d & 15)] = (uint8_t)code[e];
+                    }
+                    if (lane == 0) {
+                        const_cast<float*>(kv ? a.vs : a.ks)[crow] = scale;
+                        const_cast<int8_t*>(kv ? a.vz : a.kz)[crow] = (int8_t)zp;
+                        *reinterpret_cast<float*>(dst + OFF_M + 256 * kv + 4 * (4 * (r_new % 16) + r_new / 16)) = scale;
+                        dst[OFF_M + 768 + 64 * kv + r_new] = (uint8_t)(int8_t)zp;
+                    }
+                }
+                // the patch is read back by other lanes of the wave
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
         const int row0 = (wp + t * W) * MKEYS;
         // ---- the unit's metadata; the K tile is read by the score MFMAs and
         // the V tile once the p digits are made, then the slot's refill goes
@@ -825,7 +933,8 @@ int mfma_splits(int B, int Hkv, int S, int D, int G, bool qbf16) {
 
 template <int D, int G, bool QBF16>
 static void launch_mfma_t(const MfmaArgs& a, int nwg, hipStream_t s) {
-    hipLaunchKernelGGL((sdpa_decode_mfma<D, G, QBF16>), dim3(nwg), dim3(MGeom<D>::NT), 0, s, a);
+    if (a.start_pos) hipLaunchKernelGGL((sdpa_decode_mfma<D, G, QBF16, true>), dim3(nwg), dim3(MGeom<D>::NT), 0, s, a);
+    else hipLaunchKernelGGL((sdpa_decode_mfma<D, G, QBF16, false>), dim3(nwg), dim3(MGeom<D>::NT), 0, s, a);
 }
 
 template <int D, bool QBF16>
@@ -847,7 +956,8 @@ hipError_t launch_sdpa_decode_mfma(const DecodeLaunch& L, hipStream_t s) {
     const int G = L.Hq / L.Hkv;
     MfmaArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len, L.kv_len_sb, L.mask,
                L.mask_sb, L.sm_scale * 1.4426950408889634f, L.nsplit, L.ctr, L.part_ml, L.part_o, L.out,
-               L.out_bf16 ? 1 : 0, L.err};
+               L.out_bf16 ? 1 : 0, L.err, L.xk, L.xv, L.x_bf16 ? 1 : 0, L.xsb, L.xsh, L.start_pos};
+    if (L.start_pos && (L.mask || !L.xk || !L.xv)) return hipErrorInvalidValue;
     const int nwg = L.B * L.Hkv * L.nsplit;
     switch (L.D) {
     case 64: return L.q_bf16 ? launch_mfma_g<64, true>(a, G, nwg, s) : launch_mfma_g<64, false>(a, G, nwg, s);

@@ -210,3 +210,32 @@ def test_prefill_split_workspace(kvq):
     # the ordinary argument checks come first
     assert L.kvq_sdpa_prefill_split(q, 1, 1, 3, 8, ctypes.byref(c), ctypes.byref(c), None, None, 1, 0, 0.1, q, 1,
                                     None, 0, None, None) == 2
+
+
+def test_decode_append_full_validation(kvq):
+    """kvq_sdpa_decode_append_full rejects on the host, nothing enqueued: null
+    new rows or start_pos, a bad x dtype or stride, caches the single-pass
+    int8 kernel does not take, shape errors as kvq_sdpa_decode, and a missing
+    workspace."""
+    L = kvq.lib()
+    c, keep = _fake_cache(kvq)
+    q = ctypes.c_void_p(c.codes)
+    s = None
+
+    def call(k=c, Hq=4, xk=q, xv=q, xd=1, xsb=128, xsh=64, sp=q, ws=None, wsb=0):
+        return L.kvq_sdpa_decode_append_full(q, 1, 1, Hq, xk, xv, xd, xsb, xsh, sp, ctypes.byref(k), ctypes.byref(k),
+                                             0.1, q, 1, ws, wsb, None, s)
+
+    assert call(xk=None) == 1
+    assert call(xv=None) == 1
+    assert call(sp=None) == 1
+    assert call(xd=5) == 3
+    assert call(xsb=-1) == 2
+    assert call(Hq=3) == 2
+    c4, keep2 = _fake_cache(kvq, qmode=kvq.UINT4_TH)
+    assert call(k=c4) == 4
+    cb, keep3 = _fake_cache(kvq, qmode=kvq.FP8E4M3_B32, zps=False)
+    assert call(k=cb) == 4
+    c62, keep4 = _fake_cache(kvq, S=62)
+    assert call(k=c62) == 4
+    assert call() == 5
