@@ -225,6 +225,11 @@ class Llama8BStep:
         kvq.sdpa_decode(self.q, self.K[r], self.V[r], kv_len=self.kv_len, out=self.out, workspace=self.ws)
 
     def step(self, r):
+        # the new token's K+V written and attended in one launch
+        kvq.sdpa_decode_append_full(self.q, self.k_new, self.v_new, self.start_pos, self.K[r], self.V[r],
+                                    out=self.out, workspace=self.ws)
+
+    def step_two_launches(self, r):
         self.scatter(r)
         self.decode(r)
 
@@ -707,12 +712,18 @@ def main():
     # one graph per replica for the whole step; one graph of 128 decode calls
     # (16 rounds over the replicas) and one of 128 scatter phases
     g_step = [capture(lambda r=r: st.step(r)) for r in range(R)]
-    # the timed steps: one graph holds R steps, one per replica (as one
-    # token's step over R layers would), so the host's graph launch is paid
-    # once per R steps; a remainder of --steps uses the one-step graphs
+    # the timed steps: a graph holds the 32 steps of one token over the
+    # model's 32 layers (the layers' caches are the R replicas, in turn), so
+    # the host's graph launch is paid once per 32 steps; a remainder of
+    # --steps uses graphs of R steps, then one-step graphs
+    LAYERS = 32
+    g_token = capture(lambda: [st.step(i % R) for i in range(LAYERS)])
     g_steps = capture(lambda: [st.step(r) for r in range(R)])
 
     def run_steps(k):
+        for _ in range(k // LAYERS):
+            g_token.replay()
+        k %= LAYERS
         for _ in range(k // R):
             g_steps.replay()
         for i in range(k % R):
@@ -720,6 +731,7 @@ def main():
     ROUNDS = 16
     g_dec = capture(lambda: [st.decode(r) for _ in range(ROUNDS) for r in range(R)])
     g_sc = capture(lambda: [st.scatter(r) for _ in range(ROUNDS) for r in range(R)])
+    g_two = capture(lambda: [st.step_two_launches(i % R) for i in range(LAYERS)])
     # a replay must give what the eager calls give
     st.step(0)
     torch.cuda.synchronize()
@@ -756,13 +768,16 @@ def main():
     # over 16 replays of the per-call mean of 128 back-to-back calls
     dec = replay_stats(g_dec, 16, ROUNDS * R)
     sc = replay_stats(g_sc, 16, ROUNDS * R)
+    two = replay_stats(g_two, 16, LAYERS)
+    one = replay_stats(g_token, 16, LAYERS)
     dec_ms, sc_ms = dec["median"], sc["median"]
     gbs = decode_bytes(w) / dec_ms / 1e6
     tokens = w.B
     log(f"[bench] decode {dec_ms * 1e3:.2f} us ({gbs:.0f} GB/s; p10 {dec['p10'] * 1e3:.2f} p90 {dec['p90'] * 1e3:.2f}), "
-        f"scatter+positions {sc_ms * 1e3:.2f} us, step {ms_per_step * 1e3:.2f} us (events {step_ev_ms * 1e3:.2f} us), "
+        f"scatter+positions {sc_ms * 1e3:.2f} us, step {ms_per_step * 1e3:.2f} us (events {step_ev_ms * 1e3:.2f} us; "
+        f"as scatter + decode launches {two['median'] * 1e3:.2f} us), "
         f"graph replay exact: {graph_exact}")
-    del g_dec, g_sc
+    del g_dec, g_sc, g_two
     ceiling = stream_ceiling(decode_bytes(w))
     log(f"[bench] read-only stream ceiling: {ceiling}")
 
@@ -797,8 +812,11 @@ def main():
         "decode_us_p10_p90": [round(dec["p10"] * 1e3, 3), round(dec["p90"] * 1e3, 3)],
         "decode_calls_timed": dec["calls"],
         "step_us_events": round(step_ev_ms * 1e3, 3),
-        "step_timing": f"one step = K+V quant-scatter of the new token + decode of one cache replica; "
-                       f"replayed as graphs of {R} steps (one per replica, as one token's step over {R} layers)",
+        "step_timing": f"one step = the new token's K+V quantized and written + decode of one cache replica, "
+                       f"one kvq_sdpa_decode_append_full launch; replayed as graphs of {LAYERS} steps (one "
+                       f"token over the model's {LAYERS} layers, whose caches are the {R} replicas in turn)",
+        "step_us_median": round(one["median"] * 1e3, 3),
+        "step_two_launches_us": round(two["median"] * 1e3, 3),
         "graph_replay_bitexact": graph_exact,
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),

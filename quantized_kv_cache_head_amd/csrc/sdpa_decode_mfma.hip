@@ -322,6 +322,27 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
             __builtin_amdgcn_global_load_lds((glb_ptr)(qg + min((j * 64 + lane) * 16, QBYTES - 16)),
                                              (lds_ptr)(&s_qin[1024 * j]), 16, 0, 0);
     }
+    // append variant: every wave loads the plane's new K and V rows with q
+    // (one round trip; which wave owns the new slot is known only later)
+    // (raw words: every load is issued before any value is used)
+    constexpr int XE = D / 64;                        // row elements per lane
+    uint32_t xraw[2][XE];
+    if constexpr (APPEND) {
+        const int64_t xo = (int64_t)b * a.xsb + (int64_t)g * a.xsh + lane * XE;
+        if (a.x_bf16) {
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+                for (int e = 0; e < XE; ++e)
+                    xraw[kv][e] = reinterpret_cast<const uint16_t*>(kv ? a.xv : a.xk)[xo + e];
+        } else {
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+                for (int e = 0; e < XE; ++e)
+                    xraw[kv][e] = reinterpret_cast<const uint32_t*>(kv ? a.xv : a.xk)[xo + e];
+        }
+    }
     auto for_slots = [&](auto&& f) __attribute__((always_inline)) {
         for_each_unit(std::make_integer_sequence<int, PD>{}, f);
     };
@@ -349,34 +370,15 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     const int nsteps = wp < nunits ? (nunits - wp + W - 1) / W : 0;
     // Append variant: the new slot p_new = kv_len - 1 lies in the last unit,
     // u_new, which belongs to wave u_new mod W at its last step t_new.  That
-    // wave loads the new K and V rows now (ahead of its cache copies, so any
-    // wait for the copies covers them too), quantizes them, writes them to the
-    // cache and patches them into its tile once the unit's copies have landed.
-    // No other wave reads the slot (clamped rows past the plane may read it
-    // while it is written; they lie at or past kv_len and take no part).
-    constexpr int XE = D / 64;                        // row elements per lane
+    // wave quantizes the new K and V rows once its first copies are out,
+    // writes them to the cache, and patches them into its tile once the
+    // unit's copies have landed.  No other wave reads the slot (clamped rows
+    // past the plane may read it while it is written; they lie at or past
+    // kv_len and take no part).
     const int u_new = p_new >= 0 ? p_new / MKEYS : 0;
     const bool owner = APPEND && p_new >= 0 && u_new % W == wp;
     const int t_new = u_new / W;
     const int r_new = p_new - u_new * MKEYS;
-    float xnew[2][XE];
-    if constexpr (APPEND) {
-#pragma unroll
-        for (int kv = 0; kv < 2; ++kv)
-#pragma unroll
-            for (int e = 0; e < XE; ++e) xnew[kv][e] = 0.0f;
-        if (owner) {
-            const int64_t xo = (int64_t)b * a.xsb + (int64_t)g * a.xsh + lane * XE;
-#pragma unroll
-            for (int kv = 0; kv < 2; ++kv) {
-                const void* xp = kv ? a.xv : a.xk;
-#pragma unroll
-                for (int e = 0; e < XE; ++e)
-                    xnew[kv][e] = a.x_bf16 ? bf16_lo(reinterpret_cast<const uint16_t*>(xp)[xo + e])
-                                           : reinterpret_cast<const float*>(xp)[xo + e];
-            }
-        }
-    }
     // the q copies were issued with the kv_len load and take about as long:
     // they have landed before the cache copies go out
     __builtin_amdgcn_sched_barrier(0);
@@ -386,6 +388,27 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         constexpr int u = decltype(UC)::value;
         if (u < nsteps) fetch(UC, u, true);
     });
+    int ncode[2][XE], nzp[2];
+    float nscale[2];
+    if constexpr (APPEND) {
+        if (owner) {
+            const int64_t crow = prow + p_new;
+#pragma unroll
+            for (int kv = 0; kv < 2; ++kv) {
+                float xnew[XE];
+#pragma unroll
+                for (int e = 0; e < XE; ++e) xnew[e] = a.x_bf16 ? bf16_lo(xraw[kv][e]) : __uint_as_float(xraw[kv][e]);
+                affine_row_codes<XE>(xnew, ncode[kv], nscale[kv], nzp[kv]);
+                uint8_t* cg = const_cast<uint8_t*>(kv ? a.vc : a.kc) + crow * D + lane * XE;
+#pragma unroll
+                for (int e = 0; e < XE; ++e) cg[e] = (uint8_t)ncode[kv][e];
+                if (lane == 0) {
+                    const_cast<float*>(kv ? a.vs : a.ks)[crow] = nscale[kv];
+                    const_cast<int8_t*>(kv ? a.vz : a.kz)[crow] = (int8_t)nzp[kv];
+                }
+            }
+        }
+    }
 
     // ---- q digits ------------------------------------------------------------
     // Each wave converts the group on its own, through its own LDS words (no
@@ -537,31 +560,23 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         const uint8_t* src = slot(UC);
         if constexpr (APPEND) {
             if (owner && t == t_new) {
-                // quantize the new rows, write them to the cache, and put them
-                // in the tile where the copies put row r_new: chunk c of the
-                // row at r_new D + 16 (c ^ sw(r_new)), the scales in metadata
-                // word 4 (r_new % 16) + r_new / 16, the zero points at byte r_new
+                // put the new rows in the tile where the copies put row r_new:
+                // chunk c of the row at r_new D + 16 (c ^ sw(r_new)), the scales
+                // in metadata word 4 (r_new % 16) + r_new / 16, the zero points
+                // at byte r_new
                 uint8_t* dst = const_cast<uint8_t*>(src);
-                const int64_t crow = prow + p_new;
 #pragma unroll
                 for (int kv = 0; kv < 2; ++kv) {
-                    int code[XE];
-                    float scale;
-                    int zp;
-                    affine_row_codes<XE>(xnew[kv], code, scale, zp);
-                    uint8_t* cg = const_cast<uint8_t*>(kv ? a.vc : a.kc) + crow * D + lane * XE;
                     uint8_t* tl = dst + (kv ? OFF_V : 0) + r_new * D;
 #pragma unroll
                     for (int e = 0; e < XE; ++e) {
                         const int d = lane * XE + e;
-                        cg[e] = (uint8_t)code[e];
-                        tl[16 * ((d >> 4) ^ GM::sw(r_new)) + (d & 15)] = (uint8_t)code[e];
+                        tl[16 * ((d >> 4) ^ GM::sw(r_new)) + (d & 15)] = (uint8_t)ncode[kv][e];
                     }
                     if (lane == 0) {
-                        const_cast<float*>(kv ? a.vs : a.ks)[crow] = scale;
-                        const_cast<int8_t*>(kv ? a.vz : a.kz)[crow] = (int8_t)zp;
-                        *reinterpret_cast<float*>(dst + OFF_M + 256 * kv + 4 * (4 * (r_new % 16) + r_new / 16)) = scale;
-                        dst[OFF_M + 768 + 64 * kv + r_new] = (uint8_t)(int8_t)zp;
+                        *reinterpret_cast<float*>(dst + OFF_M + 256 * kv + 4 * (4 * (r_new % 16) + r_new / 16)) =
+                            nscale[kv];
+                        dst[OFF_M + 768 + 64 * kv + r_new] = (uint8_t)(int8_t)nzp[kv];
                     }
                 }
                 // the patch is read back by other lanes of the wave
