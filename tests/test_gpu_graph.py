@@ -144,11 +144,13 @@ def _graph_of(fn):
     return g
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["positions+scatter", "scatter_kv_full"])
-def test_full_context_step_graph_vs_oracle(fused):
+@pytest.mark.parametrize("mode", ["positions+scatter", "scatter_kv_full", "append_full"])
+def test_full_context_step_graph_vs_oracle(mode):
     """The full-context decode step (positions, K+V quant-scatter, decode; or
     the scatter that derives the slot from the device start position, and
-    decode) as one captured graph, replayed at three successive positions:
+    decode; or the one-launch step kvq_sdpa_decode_append_full) as one
+    captured graph, replayed at three successive positions (across a 64-key
+    unit boundary):
     before each replay new q / K / V values and the device start position and
     kv_len are written from the host.  After each replay the cache bytes
     equal the oracle's (which takes the same step) and the output is within
@@ -156,7 +158,7 @@ def test_full_context_step_graph_vs_oracle(fused):
     import oracle
     import quantized_kv_cache_head_amd.workloads as wl
     from _gpu import assert_cache_equal, check_attention, new_pair
-    B, Hkv, G, S, D, hist = 2, 2, 4, 512, 128, 300
+    B, Hkv, G, S, D, hist = 2, 2, 4, 512, 128, 318
     Hq = Hkv * G
     rng = np.random.default_rng(2024)
     (K, hk), (V, hv) = new_pair(kvq.INT8_TH, B, Hkv, S, D), new_pair(kvq.INT8_TH, B, Hkv, S, D)
@@ -175,7 +177,10 @@ def test_full_context_step_graph_vs_oracle(fused):
     ws = kvq.decode_workspace(B, Hq, Hkv, S, D)
 
     def step():
-        if fused:
+        if mode == "append_full":
+            kvq.sdpa_decode_append_full(q, knew, vnew, start, K, V, out=out, workspace=ws)
+            return
+        if mode == "scatter_kv_full":
             kvq.quant_scatter_kv_full(knew, vnew, start, K, V)
         else:
             kvq.positions_full(start, 1, S, slot)
@@ -205,7 +210,7 @@ def test_full_context_step_graph_vs_oracle(fused):
             torch.cuda.synchronize()
         sm, flags = oracle.positions_full(p, 1, S)
         assert flags == 0 and int(sm[0]) == p
-        if not fused:
+        if mode == "positions+scatter":
             assert int(slot.item()) == p
         oracle.quant_scatter(hk, kn, sm)
         oracle.quant_scatter(hv, vn, sm)
