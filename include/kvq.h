@@ -274,6 +274,33 @@ kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B, int Hq
                                        void* out, int out_dtype, void* workspace, size_t workspace_bytes,
                                        int32_t* err_flags, void* stream);
 
+/* The same one-launch decode step for a sink or ring cache ([PR24473]: the
+ * positions manager with sink picks the slot, keys attend through the
+ * additive mask built from the slots' positions; a ring cache is sink_size
+ * 0).  Exactly
+ *   kvq_positions_with_sink(start_pos, 1, sink_size, window, slot,
+ *                           cache_positions, err_flags),
+ *   kvq_quant_scatter_kv(xk, xv, x_dtype, B, Hkv, 1, D, x_stride_b,
+ *                        x_stride_h, 0, slot, 0, k, v, err_flags),
+ *   kvq_build_mask(cache_positions, n_slots, start_pos, 1, sink_size,
+ *                  window, mask) and
+ *   kvq_sdpa_decode(q, ..., kv_len = min(*start_pos + 1, n_slots), mask, ...):
+ * the same cache bytes, cache_positions, output bits and flags (a negative
+ * *start_pos writes nothing, sets KVQ_FLAG_SLOT_RANGE | KVQ_FLAG_KVLEN and
+ * every key is masked: the output is 0).  The mask is never materialized:
+ * each key's visibility (cp >= 0, cp <= p and (cp < sink_size or p - cp <
+ * window), cp its slot's position) is decided as its tile is read.
+ * cache_positions: int32 [n_slots], in/out (-1 = empty).  sink_size >= 0,
+ * window >= 1 and sink_size + window == n_slots (else KVQ_ERR_SHAPE).
+ * Everything else as kvq_sdpa_decode_append_full. */
+kvq_status kvq_sdpa_decode_append_sink(const void* q, int q_dtype, int B, int Hq,
+                                       const void* xk, const void* xv, int x_dtype,
+                                       int64_t x_stride_b, int64_t x_stride_h, const int32_t* start_pos,
+                                       int sink_size, int window, int32_t* cache_positions,
+                                       const kvq_cache* k, const kvq_cache* v, float sm_scale,
+                                       void* out, int out_dtype, void* workspace, size_t workspace_bytes,
+                                       int32_t* err_flags, void* stream);
+
 /* kvq_sdpa_decode with one filled length per batch row: kv_lens is a device
  * int32 array [B] (batch row b attends slots [0, kv_lens[b])), each clamped to
  * [1, n_slots] with KVQ_FLAG_KVLEN.  Otherwise as kvq_sdpa_decode; the same

@@ -42,6 +42,7 @@ EXPORTS = (
     "kvq_sdpa_decode_workspace_bytes", "kvq_sdpa_decode", "kvq_sdpa_decode_varlen", "kvq_sdpa_prefill",
     "kvq_sdpa_prefill_varlen", "kvq_sdpa_prefill_split_workspace_bytes", "kvq_sdpa_prefill_split",
     "kvq_sdpa_prefill_split_varlen", "kvq_sdpa_decode_noalloc", "kvq_sdpa_decode_append_full",
+    "kvq_sdpa_decode_append_sink",
 )
 
 
@@ -97,6 +98,9 @@ def lib():
         L.kvq_sdpa_decode_append_full.restype = _I
         L.kvq_sdpa_decode_append_full.argtypes = [_P, _I, _I, _I, _P, _P, _I, _I64, _I64, _P, _CP, _CP, _F, _P, _I,
                                                   _P, _SZ, _P, _P]
+        L.kvq_sdpa_decode_append_sink.restype = _I
+        L.kvq_sdpa_decode_append_sink.argtypes = [_P, _I, _I, _I, _P, _P, _I, _I64, _I64, _P, _I, _I, _P, _CP, _CP, _F,
+                                                  _P, _I, _P, _SZ, _P, _P]
         L.kvq_sdpa_decode_noalloc.restype = _I
         L.kvq_sdpa_decode_noalloc.argtypes = [_P, _I, _I, _I, _CP, _CP, _P, _P, _I64, _I, _F, _P, _I, _P, _P]
         L.kvq_sdpa_prefill.restype = _I
@@ -354,6 +358,38 @@ def sdpa_decode_append_full(q, xk, xv, start_pos, k: Cache, v: Cache, sm_scale=N
         _ptr(q), _dtype_code(q), B, Hq, _ptr(xk), _ptr(xv), _dtype_code(xk), xk.stride(0), xk.stride(1),
         _ptr(start_pos), ctypes.byref(kc), ctypes.byref(vc), float(sm_scale), _ptr(out), _dtype_code(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_flags), _stream(stream)))
+    return out
+
+
+def sdpa_decode_append_sink(q, xk, xv, start_pos, sink_size, window, cache_positions, k: Cache, v: Cache,
+                            sm_scale=None, out=None, out_dtype=None, workspace=None, err_flags=None, stream=None):
+    """kvq_sdpa_decode_append_sink: the sink / ring form of
+    sdpa_decode_append_full (slot from the positions manager with sink,
+    cache_positions int32 [n_slots] updated, keys masked by the additive-mask
+    rule); returns out [B, Hq, 1, D]."""
+    _need_cuda(q, xk, xv, start_pos, cache_positions, out, workspace, err_flags)
+    B, Hq, Lq, D = q.shape
+    if Lq != 1 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, Hq, 1, D]")
+    if (xk.dim() != 4 or xk.shape != xv.shape or xk.shape[2] != 1 or xk.stride(3) != 1 or xv.stride(3) != 1
+            or xk.stride()[:2] != xv.stride()[:2] or xk.dtype != xv.dtype):
+        raise ValueError("xk and xv must be [B, Hkv, 1, D] with D contiguous, equal shapes, strides and dtype")
+    if start_pos.dtype != torch.int32 or start_pos.numel() != 1:
+        raise ValueError("start_pos must be one int32")
+    if cache_positions.dtype != torch.int32 or not cache_positions.is_contiguous():
+        raise ValueError("cache_positions must be contiguous int32 [n_slots]")
+    if sm_scale is None:
+        sm_scale = D ** -0.5
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, k.H, k.S, D, q.device)
+    kc, vc = k.struct(), v.struct()
+    _check("kvq_sdpa_decode_append_sink", lib().kvq_sdpa_decode_append_sink(
+        _ptr(q), _dtype_code(q), B, Hq, _ptr(xk), _ptr(xv), _dtype_code(xk), xk.stride(0), xk.stride(1),
+        _ptr(start_pos), int(sink_size), int(window), _ptr(cache_positions), ctypes.byref(kc), ctypes.byref(vc),
+        float(sm_scale), _ptr(out), _dtype_code(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(err_flags), _stream(stream)))
     return out
 
 

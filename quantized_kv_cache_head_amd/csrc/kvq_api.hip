@@ -390,12 +390,15 @@ KVQ_API kvq_status kvq_sdpa_decode(const void* q, int q_dtype, int B, int Hq, co
                             workspace, workspace_bytes, err_flags, stream);
 }
 
-KVQ_API kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B, int Hq, const void* xk,
-                                               const void* xv, int x_dtype, int64_t x_stride_b,
-                                               int64_t x_stride_h, const int32_t* start_pos, const kvq_cache* k,
-                                               const kvq_cache* v, float sm_scale, void* out, int out_dtype,
-                                               void* workspace, size_t workspace_bytes, int32_t* err_flags,
-                                               void* stream) {
+namespace {
+
+// The one-launch decode step (append variant of the single-pass int8
+// kernel); cpos NULL: full-context layout, else sink / ring.
+kvq_status sdpa_decode_append_impl(const void* q, int q_dtype, int B, int Hq, const void* xk, const void* xv,
+                                   int x_dtype, int64_t x_stride_b, int64_t x_stride_h, const int32_t* start_pos,
+                                   int32_t* cpos, int sink_size, int window, const kvq_cache* k,
+                                   const kvq_cache* v, float sm_scale, void* out, int out_dtype, void* workspace,
+                                   size_t workspace_bytes, int32_t* err_flags, void* stream) {
     kvq_status st = check_attention(q, q_dtype, B, Hq, k, v, out, out_dtype);
     if (st != KVQ_OK) return st;
     if (!xk || !xv || !start_pos) return KVQ_ERR_NULL;
@@ -403,6 +406,7 @@ KVQ_API kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B
     if (x_stride_b < 0 || x_stride_h < 0) return KVQ_ERR_SHAPE;
     const size_t es = x_dtype == KVQ_BF16 ? 2 : 4;
     if (!aligned(xk, es) || !aligned(xv, es)) return KVQ_ERR_SHAPE;
+    if (cpos && !aligned(cpos, 4)) return KVQ_ERR_SHAPE;
     const DecodePlan plan = decode_plan(q_dtype, B, Hq, k, v);
     if (!plan.single) return KVQ_ERR_UNSUPPORTED;
     const size_t ctr = decode_ctr_bytes(B, k->heads);
@@ -441,7 +445,37 @@ KVQ_API kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B
     L.x_bf16 = x_dtype == KVQ_BF16;
     L.xsb = x_stride_b;
     L.xsh = x_stride_h;
+    L.cpos = cpos;
+    L.sink = sink_size;
+    L.window = window;
     return from_hip(kvq::launch_sdpa_decode_mfma(L, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+KVQ_API kvq_status kvq_sdpa_decode_append_full(const void* q, int q_dtype, int B, int Hq, const void* xk,
+                                               const void* xv, int x_dtype, int64_t x_stride_b,
+                                               int64_t x_stride_h, const int32_t* start_pos, const kvq_cache* k,
+                                               const kvq_cache* v, float sm_scale, void* out, int out_dtype,
+                                               void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                               void* stream) {
+    return sdpa_decode_append_impl(q, q_dtype, B, Hq, xk, xv, x_dtype, x_stride_b, x_stride_h, start_pos, nullptr, 0,
+                                   0, k, v, sm_scale, out, out_dtype, workspace, workspace_bytes, err_flags, stream);
+}
+
+KVQ_API kvq_status kvq_sdpa_decode_append_sink(const void* q, int q_dtype, int B, int Hq, const void* xk,
+                                               const void* xv, int x_dtype, int64_t x_stride_b,
+                                               int64_t x_stride_h, const int32_t* start_pos, int sink_size,
+                                               int window, int32_t* cache_positions, const kvq_cache* k,
+                                               const kvq_cache* v, float sm_scale, void* out, int out_dtype,
+                                               void* workspace, size_t workspace_bytes, int32_t* err_flags,
+                                               void* stream) {
+    if (!cache_positions) return KVQ_ERR_NULL;
+    if (!k) return KVQ_ERR_NULL;
+    if (sink_size < 0 || window < 1 || (int64_t)sink_size + window != k->n_slots) return KVQ_ERR_SHAPE;
+    return sdpa_decode_append_impl(q, q_dtype, B, Hq, xk, xv, x_dtype, x_stride_b, x_stride_h, start_pos,
+                                   cache_positions, sink_size, window, k, v, sm_scale, out, out_dtype, workspace,
+                                   workspace_bytes, err_flags, stream);
 }
 
 KVQ_API kvq_status kvq_sdpa_decode_varlen(const void* q, int q_dtype, int B, int Hq, const kvq_cache* k,

@@ -63,6 +63,10 @@ struct DecodeLaunch {
     const void* xv = nullptr;
     bool x_bf16 = false;
     int64_t xsb = 0, xsh = 0;
+    // append variant, sink / ring layout (cpos set): the cache is sink +
+    // window slots, cpos [n_slots] the slots' positions (in/out)
+    int32_t* cpos = nullptr;
+    int sink = 0, window = 0;
 };
 
 int decode_splits_max(int B, int Hq, int Hkv, int S, int D, int qmode);

@@ -160,6 +160,14 @@ struct MfmaArgs {
     int x_bf16;
     int64_t xsb, xsh;
     const int32_t* start_pos;
+    // sink / ring layout of the append variant (cpos set): the new slot is
+    // p for p < sink, else sink + (p - sink) mod window (n_slots = sink +
+    // window); cpos [n_slots] holds each slot's position (-1 empty) and
+    // receives cpos[slot] = p; the mask word of a key is its position, made
+    // visible (0) or not (-inf) by the additive-mask rule at query position
+    // p; kv_len = min(p + 1, n_slots)
+    int32_t* cpos;
+    int sink, window;
 };
 
 // Affine int8 code parameters of one row spread over a wave (E elements per
@@ -250,16 +258,30 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
     int kv_len = S;
     int p_new = -1;                                   // slot this call writes (append variant)
+    int qpos = 0;                                     // query position (sink / ring append)
+    const bool sink_app = APPEND && a.cpos != nullptr;
     if constexpr (APPEND) {
         const int p = *(cptr_i32)(a.start_pos);
-        // exactly the flags of the K+V full-context scatter followed by a
-        // decode with kv_len = p + 1
-        if (p < 0 || p >= S) {
-            if (a.err && split == 0 && tid == 0) atomicOr(a.err, p < 0 ? KVQ_DEV_FLAG_SLOT_RANGE : KVQ_DEV_FLAG_POS_CAPACITY);
+        qpos = p;
+        if (sink_app) {
+            // exactly the flags of the sink positions, the K+V scatter and a
+            // decode with kv_len = min(p + 1, n_slots)
+            if (p < 0) {
+                if (a.err && split == 0 && tid == 0) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
+            } else {
+                p_new = p < a.sink ? p : a.sink + (int)(((int64_t)p - a.sink) % a.window);
+            }
+            kv_len = p < S ? p + 1 : S;
         } else {
-            p_new = p;
+            // exactly the flags of the K+V full-context scatter followed by a
+            // decode with kv_len = p + 1
+            if (p < 0 || p >= S) {
+                if (a.err && split == 0 && tid == 0) atomicOr(a.err, p < 0 ? KVQ_DEV_FLAG_SLOT_RANGE : KVQ_DEV_FLAG_POS_CAPACITY);
+            } else {
+                p_new = p;
+            }
+            kv_len = p < S ? p + 1 : S + 1;
         }
-        kv_len = p < S ? p + 1 : S + 1;
     } else {
         if (a.kv_len) kv_len = *(cptr_i32)(a.kv_len + (int64_t)b * a.kv_len_sb);
     }
@@ -368,13 +390,13 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     }
     const int nunits = (kv_len + MKEYS - 1) / MKEYS;
     const int nsteps = wp < nunits ? (nunits - wp + W - 1) / W : 0;
-    // Append variant: the new slot p_new = kv_len - 1 lies in the last unit,
-    // u_new, which belongs to wave u_new mod W at its last step t_new.  That
-    // wave quantizes the new K and V rows once its first copies are out,
-    // writes them to the cache, and patches them into its tile once the
-    // unit's copies have landed.  No other wave reads the slot (clamped rows
-    // past the plane may read it while it is written; they lie at or past
-    // kv_len and take no part).
+    // Append variant: the new slot p_new (< kv_len) lies in unit u_new, which
+    // belongs to wave u_new mod W at its step t_new.  That wave quantizes the
+    // new K and V rows once its first copies are out, writes them to the
+    // cache, and patches them (and, sink / ring, the slot's position) into
+    // its tile once the unit's copies have landed, before any read of it.
+    // No other wave reads the slot (clamped rows past the plane may read it
+    // while it is written; they lie at or past kv_len and take no part).
     const int u_new = p_new >= 0 ? p_new / MKEYS : 0;
     const bool owner = APPEND && p_new >= 0 && u_new % W == wp;
     const int t_new = u_new / W;
@@ -407,6 +429,8 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
                     const_cast<int8_t*>(kv ? a.vz : a.kz)[crow] = (int8_t)nzp[kv];
                 }
             }
+            // the slot's position (one writer: the owner of plane 0)
+            if (sink_app && plane == 0 && lane == 0) a.cpos[p_new] = qpos;
         }
     }
 
@@ -579,6 +603,8 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
                         dst[OFF_M + 768 + 64 * kv + r_new] = (uint8_t)(int8_t)nzp[kv];
                     }
                 }
+                if (sink_app && lane == 0)
+                    *reinterpret_cast<int*>(dst + OFF_M + 512 + 4 * (4 * (r_new % 16) + r_new / 16)) = qpos;
                 // the patch is read back by other lanes of the wave
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -603,7 +629,19 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
         }
         const float skv[4] = {sk4.x, sk4.y, sk4.z, sk4.w};
         const float svv[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
-        const float mkv[4] = {mk4.x, mk4.y, mk4.z, mk4.w};
+        float mkv[4] = {mk4.x, mk4.y, mk4.z, mk4.w};
+        if constexpr (APPEND) {
+            if (sink_app) {
+                // the mask words are the slots' positions: visible when
+                // cp >= 0, cp <= p and (cp < sink or p - cp < window)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int cp = __float_as_int(mkv[tt]);
+                    const bool vis = cp >= 0 && cp <= qpos && (cp < a.sink || qpos - cp < a.window);
+                    mkv[tt] = vis ? 0.0f : NEG_INF;
+                }
+            }
+        }
         // ---- scores: S^T[(head, digit)][key] for 4 tiles of 16 keys; the B
         // operand is K row 16 tt + n, 16-byte chunk 4 dq + c
         i32x4_t sc[4];
@@ -971,8 +1009,16 @@ hipError_t launch_sdpa_decode_mfma(const DecodeLaunch& L, hipStream_t s) {
     const int G = L.Hq / L.Hkv;
     MfmaArgs a{L.q, L.B, L.Hq, L.Hkv, L.S, L.kc, L.ks, L.kz, L.vc, L.vs, L.vz, L.kv_len, L.kv_len_sb, L.mask,
                L.mask_sb, L.sm_scale * 1.4426950408889634f, L.nsplit, L.ctr, L.part_ml, L.part_o, L.out,
-               L.out_bf16 ? 1 : 0, L.err, L.xk, L.xv, L.x_bf16 ? 1 : 0, L.xsb, L.xsh, L.start_pos};
-    if (L.start_pos && (L.mask || !L.xk || !L.xv)) return hipErrorInvalidValue;
+               L.out_bf16 ? 1 : 0, L.err, L.xk, L.xv, L.x_bf16 ? 1 : 0, L.xsb, L.xsh, L.start_pos,
+               L.cpos, L.sink, L.window};
+    if (L.start_pos && (!L.xk || !L.xv)) return hipErrorInvalidValue;
+    if (L.start_pos && (L.cpos ? (L.sink < 0 || L.window < 1 || L.sink + L.window != L.S) : L.mask != nullptr))
+        return hipErrorInvalidValue;
+    if (L.start_pos && L.cpos) {
+        // the positions travel in the mask words (one row shared by the batch)
+        a.mask = reinterpret_cast<const float*>(L.cpos);
+        a.mask_sb = 0;
+    }
     const int nwg = L.B * L.Hkv * L.nsplit;
     switch (L.D) {
     case 64: return L.q_bf16 ? launch_mfma_g<64, true>(a, G, nwg, s) : launch_mfma_g<64, false>(a, G, nwg, s);

@@ -239,3 +239,28 @@ def test_decode_append_full_validation(kvq):
     c62, keep4 = _fake_cache(kvq, S=62)
     assert call(k=c62) == 4
     assert call() == 5
+
+
+def test_decode_append_sink_validation(kvq):
+    """kvq_sdpa_decode_append_sink: a null cache_positions, a layout that is
+    not sink + window == n_slots, and the append checks of the full-context
+    form, all on the host."""
+    L = kvq.lib()
+    c, keep = _fake_cache(kvq)                      # n_slots 64
+    q = ctypes.c_void_p(c.codes)
+    s = None
+
+    def call(sink=4, window=60, cp=q, k=c, xk=q, Hq=4):
+        return L.kvq_sdpa_decode_append_sink(q, 1, 1, Hq, xk, q, 1, 128, 64, q, sink, window, cp, ctypes.byref(k),
+                                             ctypes.byref(k), 0.1, q, 1, None, 0, None, s)
+
+    assert call(cp=None) == 1
+    assert call(window=59) == 2
+    assert call(sink=-1, window=65) == 2
+    assert call(sink=64, window=0) == 2
+    assert call(xk=None) == 1
+    assert call(Hq=3) == 2
+    c4, keep2 = _fake_cache(kvq, qmode=kvq.UINT4_TH)
+    assert call(k=c4) == 4
+    assert call() == 5
+    assert call(sink=0, window=64) == 5
