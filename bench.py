@@ -416,7 +416,8 @@ def leg_block_scatter():
 def leg_sink_ring():
     """C3: decode step at position 6000 of a sink (4 + 2044 slots) and a ring
     (1024) cache, B 4, 32/8 heads, D 128: positions, K+V quant-scatter,
-    mask build, decode attention.  16 (sink) / 32 (ring) cache replicas
+    mask build, decode attention, as four launches and as the one launch of
+    kvq_sdpa_decode_append_sink.  16 (sink) / 32 (ring) cache replicas
     rotate, about 280 MB each way, so the cache bytes come from HBM."""
     w = wl.SINKRING
     res = {}
@@ -464,11 +465,20 @@ def leg_sink_ring():
         def decs():
             for K, V, cp, mask, slot in reps:
                 kvq.sdpa_decode(q, K, V, kv_len=kvl, mask=mask, out=out, workspace=ws)
+
+        def fused_steps():
+            # the same step in one launch (positions, scatter, visibility from
+            # the slots' positions, decode); it leaves each replica as the
+            # four launches do, so the two step graphs time the same work
+            for K, V, cp, mask, slot in reps:
+                kvq.sdpa_decode_append_sink(q, knew, vnew, start, sink, window, cp, K, V, out=out, workspace=ws)
         t_step = replay_stats(capture(steps), 16, R)
         t_dec = replay_stats(capture(decs), 16, R)
+        t_fused = replay_stats(capture(fused_steps), 16, R)
         nbytes = 2 * w.B * w.Hkv * S * (w.D + 5) + 2 * w.B * w.Hq * w.D * 2 + S * 4
         gbs = nbytes / t_dec["median"] / 1e6
         res[name] = {"step_us": round(t_step["median"] * 1e3, 2), "decode_us": round(t_dec["median"] * 1e3, 2),
+                     "step_one_launch_us": round(t_fused["median"] * 1e3, 2),
                      "decode_gbs": round(gbs, 1), "replicas": R,
                      "roofline": roof("hbm", gbs, HBM_PEAK_GBS, "GB/s", bytes=nbytes),
                      "note": f"{R} cache replicas rotated (HBM-cold); median of 16 graph replays"}
