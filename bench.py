@@ -4,8 +4,11 @@ Headline workload (Llama-3-8B-shaped decode layer): B 8, 32 query / 8 KV
 heads, head_dim 128, 8192-slot int8 per-token-head cache filled to kv_len 4096,
 bf16 inputs with 4 of every 128 K/V channels scaled x10.  One step is the
 whole decode-side path: slot position of the new token (full-context layout),
-quantize + scatter of its K and V, and decode attention over the cache (one
-kernel launch: split pass and split merge in the same launch).
+quantize + scatter of its K and V, and decode attention over the cache, all in
+one kernel launch (kvq_sdpa_decode_append_full: the wave that owns the new
+slot quantizes and writes it; split pass and split merge in the same launch).
+The timed steps replay graphs of 32 steps (one token over the 32 layers of
+the model, whose caches are the replicas in turn).
 
 The value is decode-attention HBM throughput: the algorithmic bytes the
 attention must move (codes, scales and zero points of slots [0, kv_len) plus
@@ -337,8 +340,10 @@ def roof(bound, achieved, peak, unit, **extra):
 def leg_tiny():
     """Tiny full-context int8 cache (B 1, 4/2 heads, D 64, 256 slots, fp32
     inputs): the 64-token prefill (K+V quant-scatter at the device start
-    position, causal prefill attention) and 32 decode steps (the same scatter,
-    decode attention), as one HIP graph; also the 32 decode steps alone."""
+    position, causal prefill attention) and 32 decode steps (each one
+    kvq_sdpa_decode_append_full launch), as one HIP graph; also the 32 decode
+    steps alone, and the same with each step as a scatter and a decode
+    launch."""
     w = wl.TINY
     K = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
     V = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, w.S, w.D).sentinel_fill()
@@ -358,14 +363,23 @@ def leg_tiny():
 
     def decode_steps():
         for qp, kp, vp, st, kl, sl, o in steps:
+            kvq.sdpa_decode_append_full(qp, kp, vp, st, K, V, out=o, workspace=ws)
+
+    def decode_steps_two_launches():
+        for qp, kp, vp, st, kl, sl, o in steps:
             kvq.quant_scatter_kv_full(kp, vp, st, K, V)
             kvq.sdpa_decode(qp, K, V, kv_len=kl, out=o, workspace=ws)
 
     def whole():
         prefill()
         decode_steps()
+
+    def whole_two_launches():
+        prefill()
+        decode_steps_two_launches()
     t_all = replay_stats(capture(whole), 20, 1)
     t_dec = replay_stats(capture(decode_steps), 20, w.decode_steps)
+    t_all2 = replay_stats(capture(whole_two_launches), 20, 1)
     # algorithmic bytes: fp32 inputs read, codes + scale + zp written, q/out,
     # and the cache rows each attention call reads
     row = w.D + 4 + 1
@@ -375,9 +389,10 @@ def leg_tiny():
         nb += 2 * w.B * w.Hkv * (w.D * 4 + row) + 2 * w.B * w.Hq * w.D * 4 + 2 * w.B * w.Hkv * (p + 1) * row
     us = t_all["median"] * 1e3
     return {"total_us": round(us, 2), "decode_step_us": round(t_dec["median"] * 1e3, 3),
-            "launches": 2 + 2 * w.decode_steps,
+            "launches": 2 + w.decode_steps,
+            "total_two_launch_steps_us": round(t_all2["median"] * 1e3, 2),
             "roofline": roof("hbm", nb / us / 1e3, HBM_PEAK_GBS, "GB/s", bytes=nb,
-                             note="launch-bound: 66 small launches"),
+                             note=f"launch-bound: {2 + w.decode_steps} small launches"),
             "note": "prefill 64 tokens + 32 decode steps, one HIP graph; median of 20 replays"}
 
 
