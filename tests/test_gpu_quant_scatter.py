@@ -239,3 +239,33 @@ def test_scatter_block_other_head_dims(qmode, D):
     torch.cuda.synchronize()
     oracle.quant_scatter(hc, x, slots)
     assert_cache_equal(dc, hc, f"block qmode {qmode} D {D}")
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_scatter_affine_large_ragged(qmode, D):
+    """A large launch (72018 rows, not a multiple of the rows a workgroup
+    takes), one cache and K+V in one launch: bit-exact against the oracle,
+    skipped and out-of-range slots included."""
+    rng = np.random.default_rng(7 * D + qmode)
+    B, H, T, S = 2, 9, 4001, 4100
+    say(f"scatter large ragged qmode={qmode} D={D}")
+    xk = _inputs(rng, B, H, T, D, True)
+    xv = wl.to_bf16_values(rng.standard_normal((B, H, T, D)).astype(np.float32))
+    slots = np.stack([rng.choice(S, T, replace=False) for _ in range(B)]).astype(np.int32)
+    slots[0, 10] = -1
+    slots[1, T - 1] = S + 1
+    dk, hk = new_pair(qmode, B, H, S, D)
+    dv, hv = new_pair(qmode, B, H, S, D)
+    dk1, hk1 = new_pair(qmode, B, H, S, D)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sl = torch.from_numpy(slots).to(DEV)
+    kvq.quant_scatter_kv(dev_input(xk, True), dev_input(xv, True), sl, dk, dv, err_flags=err)
+    kvq.quant_scatter(dev_input(xk, True), sl, dk1)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hk, xk, slots, parallel=True)
+    oracle.quant_scatter(hv, xv, slots, parallel=True)
+    assert_cache_equal(dk, hk, "large K")
+    assert_cache_equal(dv, hv, "large V")
+    assert_cache_equal(dk1, hk, "large K, one cache")
+    assert int(err.item()) == kvq.FLAG_SLOT_RANGE
