@@ -567,6 +567,51 @@ def leg_long_prefill():
     return res
 
 
+def leg_decode_kv_len():
+    """The Llama-3-8B-shaped decode layer (B 8, 32/8 heads, D 128, int8
+    per-token-head cache) at growing kv_len (n_slots = kv_len), to show how
+    the call's fixed cost (start-up, split merge) amortises as its bytes
+    grow.  The caches hold random codes, scales in [0.01, 0.02) and zero
+    points (the kernel's work does not depend on the values); replicas
+    totalling at least 1 GiB rotate, so the bytes come from HBM."""
+    w = wl.LLAMA8B
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1005)
+    res = {}
+    for kv in (4096, 16384, 65536):
+        S = kv
+        per = 2 * w.B * w.Hkv * S * (w.D + 5)
+        R = max(2, -(-(1 << 30) // per))
+        reps = []
+        for _ in range(R):
+            pair = []
+            for _kv in range(2):
+                c = kvq.Cache.empty(kvq.INT8_TH, w.B, w.Hkv, S, w.D)
+                c.codes.copy_(torch.randint(0, 256, c.codes.shape, generator=gen, device=DEV, dtype=torch.int32))
+                c.scales.copy_(0.01 + 0.01 * torch.rand(c.scales.shape, generator=gen, device=DEV))
+                c.zps.copy_(torch.randint(-128, 128, c.zps.shape, generator=gen, device=DEV, dtype=torch.int32))
+                pair.append(c)
+            reps.append(pair)
+        q = torch.randn((w.B, w.Hq, 1, w.D), generator=gen, device=DEV).to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ws = kvq.decode_workspace(w.B, w.Hq, w.Hkv, S, w.D)
+        kvl = i32(kv)
+        rounds = max(1, 16 // R)
+
+        def calls():
+            for _ in range(rounds):
+                for K, V in reps:
+                    kvq.sdpa_decode(q, K, V, kv_len=kvl, out=out, workspace=ws)
+        t = replay_stats(capture(calls), 8, R * rounds)
+        nb = 2 * w.B * w.Hkv * kv * (w.D + 5) + 2 * w.B * w.Hq * w.D * 2
+        gbs = nb / t["median"] / 1e6
+        res[f"kv_len_{kv}"] = {"us": round(t["median"] * 1e3, 2), "gbs": round(gbs, 1), "replicas": R,
+                               "roofline": roof("hbm", gbs, HBM_PEAK_GBS, "GB/s", bytes=nb)}
+        del reps
+        torch.cuda.synchronize()
+    return res
+
+
 def leg_block_attention():
     """Attention over block-quantized caches (a scale per 32 elements): decode
     on the Llama-shaped layer for each block format (4 cache replicas rotated,
@@ -703,7 +748,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (PMC calibration)")
-    ap.add_argument("--leg", choices=["tiny", "block_scatter", "sink_ring", "long_prefill", "block_attention"],
+    ap.add_argument("--leg", choices=["tiny", "block_scatter", "sink_ring", "long_prefill", "block_attention",
+                                      "decode_kv_len"],
                     help="run only this secondary workload and print its result (for profiling)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the headline decode calls (for a profiler run)")
@@ -726,7 +772,8 @@ def main():
     torch.cuda.set_device(0)
     if args.leg:
         legs = {"tiny": leg_tiny, "block_scatter": leg_block_scatter, "sink_ring": leg_sink_ring,
-                "long_prefill": leg_long_prefill, "block_attention": leg_block_attention}
+                "long_prefill": leg_long_prefill, "block_attention": leg_block_attention,
+                "decode_kv_len": leg_decode_kv_len}
         print(json.dumps({"leg": args.leg, "result": legs[args.leg]()}))
         return
 
@@ -881,6 +928,7 @@ def main():
         sec["long_prefill_uint4_d256"] = leg_long_prefill()
         log("[bench] long prefill done")
         sec["block_cache_attention"] = leg_block_attention()
+        sec["decode_llama8b_kv_len_sweep"] = leg_decode_kv_len()
         log("[bench] block-cache attention done")
         result["secondary"] = sec
     print(json.dumps(result))
