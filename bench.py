@@ -893,9 +893,10 @@ def main():
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "quant_scatter": {"us": round(sc_ms * 1e3, 3), "mtok_s": round(tokens / sc_ms / 1e3, 3),
                           "tokens_per_step": tokens, "bytes": scatter_bytes(w),
-                          "note": ("one K+V quant-scatter launch at the device start position for the 8 new "
-                                   "tokens of the step: "
-                                   "launch-bound at this size; the 16384-token block scatter is "
+                          "note": ("the standalone K+V quant-scatter call (kvq_quant_scatter_kv_full) for the 8 "
+                                   "new tokens of a step: launch-bound at this size; the timed step does this "
+                                   "write inside its one decode launch (step_two_launches_us is the step as "
+                                   "this call plus a decode call); the 16384-token block scatter is "
                                    "secondary.block_scatter_16384x128")},
         "roofline": {"bound": "hbm", "kernel": "sdpa_decode_mfma<128,4,bf16> (the whole kvq_sdpa_decode call: "
                                                "one launch, split pass and split merge)",
