@@ -44,7 +44,8 @@
 //    (m, l, o) per head, written with device-coherent stores; the workgroup
 //    then takes a ticket on the plane's counter, and the last one merges all
 //    splits of the plane in split order, writes the output and sets the
-//    counter back to zero.
+//    counter back to zero.  With one split per plane (small caches) the
+//    workgroup writes the output from its LDS merge: no partial, no ticket.
 #include <type_traits>
 #include <utility>
 
@@ -854,8 +855,38 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     }
     __syncthreads();
 
-    // ---- the workgroup's partial: (m, l, o) per head ---------------------------
+    // ---- one split per plane: the workgroup's merge is the result -------------
     constexpr int OPT = (G * D + NT - 1) / NT;
+    if (ns == 1) {
+#pragma unroll
+        for (int i = 0; i < OPT; ++i) {
+            const int idx = tid + NT * i;
+            if (idx < G * D) {
+                const int h = idx / D, d = idx % D;
+                float M = NEG_INF;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
+                float o = 0.0f, lsum = 0.0f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    const float fw = s_m[w][h] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
+                    const float* ow = reinterpret_cast<const float*>(s_r0 + w * SLOT);
+                    const float ov = ow[(3 * h) * D + d] + ow[(3 * h + 1) * D + d] + ow[(3 * h + 2) * D + d] - s_c[w][h];
+                    o = fmaf(fw, ov, o);
+                    lsum = fmaf(fw, s_l[w][h], lsum);
+                }
+                // o + 0 as the split merge forms it (a -0 sum becomes +0), so
+                // that the result does not depend on the split count's path
+                const float res = lsum > 0.0f ? (o + 0.0f) / lsum : 0.0f;
+                const int64_t oi = ((int64_t)b * a.Hq + (int64_t)g * G) * D + idx;
+                if (a.out_bf16) reinterpret_cast<uint16_t*>(a.out)[oi] = f32_to_bf16_rne(res);
+                else reinterpret_cast<float*>(a.out)[oi] = res;
+            }
+        }
+        return;
+    }
+
+    // ---- the workgroup's partial: (m, l, o) per head ---------------------------
     float* pml = a.part_ml + ((int64_t)plane * ns + split) * G * 2;
     float* po = a.part_o + ((int64_t)plane * ns + split) * G * D;
 #pragma unroll
