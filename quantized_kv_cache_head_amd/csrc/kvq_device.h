@@ -129,17 +129,30 @@ __device__ __forceinline__ uint32_t cvt8_e2m1(const float* y) {
 // ---------------------------------------------------------------------------
 // Cross-lane helpers (wave64)
 // ---------------------------------------------------------------------------
-template <int WIDTH>
-__device__ __forceinline__ float wave_max_sub(float v) {
-#pragma unroll
-    for (int o = WIDTH / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// v of lane (l ^ 1), (l ^ 2) by quad permutes; once every lane of a quad
+// (octet) holds the same value, the half mirror (mirror) of a row of 16
+// brings in the other quad's (octet's) value; across the two rows of a
+// 32-lane half by a swizzle (xor 16), across the halves by a shuffle.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// max / min over aligned groups of WIDTH lanes; every lane gets its group's
+// result (min and max are exact, so the pairing order does not matter)
+template <int WIDTH, bool MAX>
+__device__ __forceinline__ float wave_reduce_sub(float v) {
+    auto op = [](float a, float b) __attribute__((always_inline)) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    if constexpr (WIDTH >= 2) v = op(v, dpp_f<0xB1>(v));     // quad_perm [1, 0, 3, 2]
+    if constexpr (WIDTH >= 4) v = op(v, dpp_f<0x4E>(v));     // quad_perm [2, 3, 0, 1]
+    if constexpr (WIDTH >= 8) v = op(v, dpp_f<0x141>(v));    // row_half_mirror
+    if constexpr (WIDTH >= 16) v = op(v, dpp_f<0x140>(v));   // row_mirror
+    if constexpr (WIDTH >= 32) v = op(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+    if constexpr (WIDTH >= 64) v = op(v, __shfl_xor(v, 32, 64));
     return v;
 }
 template <int WIDTH>
-__device__ __forceinline__ float wave_min_sub(float v) {
-#pragma unroll
-    for (int o = WIDTH / 2; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-    return v;
-}
+__device__ __forceinline__ float wave_max_sub(float v) { return wave_reduce_sub<WIDTH, true>(v); }
+template <int WIDTH>
+__device__ __forceinline__ float wave_min_sub(float v) { return wave_reduce_sub<WIDTH, false>(v); }
 
 }  // namespace kvq

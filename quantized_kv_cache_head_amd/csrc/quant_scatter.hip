@@ -24,8 +24,9 @@
 // writes its 8 codes (8 or 4 bytes) in one store; the L lanes of a row write
 // the contiguous code row.  Block modes: 4 lanes per 32-element block.
 // All arithmetic is single IEEE fp32 operations (file built with
-// -ffp-contract=off; division is correctly rounded; rintf is RNE), so codes,
-// scales and zero points are bit-exact with the documented formulas.  FP8 and
+// -ffp-contract=off; rintf is RNE), and every quotient is the correctly
+// rounded one (a division, or a product shown to round to the same result),
+// so codes, scales and zero points are bit-exact with the documented formulas.  FP8 and
 // E2M1 codes come from the conversion instructions, which round the quotient
 // to nearest even after a magnitude clamp (kvq_device.h).  An MX
 // scale X = 2^k divides by multiplying with 2^-k, which is exactly
@@ -143,22 +144,59 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
     hi = wave_max_sub<L>(hi);
     if (!valid) return;
 
+    // The row's chain (range, scale, 1 / scale, zero point) is the critical
+    // path of a short-lived wave, so none of it is a division.
+    // scale = RN(range / n), n = qmax - qmin (255 or 15), as s0 = range *
+    // RN(1 / n) and one residual step: for these n the result equals the
+    // correctly rounded quotient for every finite range >= 0 (an exhaustive
+    // check over all of them is a CPU test); an infinite range keeps inf.
+    constexpr float NQ = (float)(QMAX - QMIN);
+    constexpr float RNQ = 1.0f / NQ;
     const float range = hi - lo;
-    float scale = range / (float)(QMAX - QMIN);
+    const float s0 = range * RNQ;
+    float scale = fmaf(fmaf(-s0, NQ, range), RNQ, s0);
+    if (!(range < __builtin_huge_valf())) scale = range;
     scale = fmaxf(scale, 0x1p-23f);
-    int zp = QMIN - (int)rintf(lo / scale);
-    zp = min(max(zp, QMIN), QMAX);
 
+    // inv ~ 1 / scale: v_rcp (1 ulp) and one Newton step, within
+    // 2^-24 (1 + 2^-20) of 1 / scale; 0 for an infinite scale.
+    float inv = __builtin_amdgcn_rcpf(scale);
+    inv = fmaf(fmaf(-scale, inv, 1.0f), inv, inv);
+    if (!(scale < __builtin_huge_valf())) inv = 0.0f;
+
+    // rne(x / scale) from x * inv: the product is within 3.01 * 2^-24 |q| of
+    // RN(x / scale), where |q| = |x| / scale < 256 (x lies in [lo, hi] and
+    // scale >= RN(range / n)), so below 2^-14.4.  Where it lies more than 2^-13
+    // from every half-integer, both round to the same integer; a value closer
+    // than that (or a non-finite one) takes the exact quotient instead.
+    constexpr float TIE_MARGIN = 0x1p-13f;
+    int zp;
+    {
+        const float t = lo * inv;
+        float k = rintf(t);
+        if (!(fabsf(t - k) < 0.5f - TIE_MARGIN)) k = rintf(lo / scale);
+        zp = min(max(QMIN - (int)k, QMIN), QMAX);
+    }
     const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int d0 = (p * L + li) * 8;
         if (d0 >= a.D) break;
         int c[8];
+        bool near_tie = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            int q = (int)rintf(v[p][i] / scale) + zp;
-            c[i] = min(max(q, QMIN), QMAX);
+            const float t = v[p][i] * inv;
+            const float k = rintf(t);
+            near_tie |= !(fabsf(t - k) < 0.5f - TIE_MARGIN);
+            c[i] = min(max((int)k + zp, QMIN), QMAX);
+        }
+        if (near_tie) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                int q = (int)rintf(v[p][i] / scale) + zp;
+                c[i] = min(max(q, QMIN), QMAX);
+            }
         }
         if constexpr (U4) {
             uint32_t w = 0;

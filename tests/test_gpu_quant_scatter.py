@@ -269,3 +269,46 @@ def test_scatter_affine_large_ragged(qmode, D):
     assert_cache_equal(dv, hv, "large V")
     assert_cache_equal(dk1, hk, "large K, one cache")
     assert int(err.item()) == kvq.FLAG_SLOT_RANGE
+
+
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.UINT4_TH])
+@pytest.mark.parametrize("D", [64, 256])
+def test_scatter_affine_ties_and_near_ties(qmode, D):
+    """Quotients x / scale at and around the half-integers where the code's
+    rounding changes: exact ties, a few ulps either side, and distances
+    straddling the margin below which the kernel takes exact quotients.
+    fp32 input (the values need more bits than bf16 holds); bit-exact against
+    the oracle."""
+    rng = np.random.default_rng(4242 + D + qmode)
+    qmin, qmax = (-128, 127) if qmode == kvq.INT8_TH else (0, 15)
+    B, H, T, S = 1, 3, 64, 80
+    x = np.zeros((B, H, T, D), np.float32)
+    offsets = np.array([0.0, 2.0 ** -13, -(2.0 ** -13), 1.5 * 2.0 ** -13, -1.5 * 2.0 ** -13,
+                        2.0 ** -12, -(2.0 ** -12), 2.0 ** -16, -(2.0 ** -16)])
+    for h in range(H):
+        for t in range(T):
+            lo = -float(rng.uniform(0.5, 4.0)) if t % 5 else 0.0
+            hi = float(rng.uniform(0.5, 4.0))
+            row = np.empty(D, np.float32)
+            row[0], row[1] = lo, hi
+            scale, zp = oracle.affine_params(row[:2], qmin, qmax)
+            # half-integer quotients inside [lo, hi]
+            kmin, kmax = int(np.ceil(lo / scale)), int(np.floor(hi / scale)) - 1
+            k = rng.integers(kmin, kmax + 1, D - 2)
+            off = offsets[rng.integers(0, len(offsets), D - 2)]
+            vals = ((k + 0.5 + off) * np.float64(scale)).astype(np.float32)
+            ulps = rng.integers(-3, 4, D - 2)
+            for i in range(D - 2):
+                for _ in range(abs(int(ulps[i]))):
+                    vals[i] = np.nextafter(vals[i], np.float32(np.inf if ulps[i] > 0 else -np.inf))
+            row[2:] = np.clip(vals, lo, hi)
+            # the row's range (and so its scale) must be the one constructed
+            assert oracle.affine_params(row, qmin, qmax) == (scale, zp)
+            x[0, h, t] = row
+    slots = rng.choice(S, T, replace=False).astype(np.int32)[None]
+    say(f"scatter affine ties qmode={qmode} D={D}")
+    dc, hc = new_pair(qmode, B, H, S, D)
+    kvq.quant_scatter(dev_input(x, False), torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, f"affine ties qmode {qmode} D {D}")
