@@ -16,8 +16,9 @@
 //  * Grid: B * Hkv planes (one (b, kv head)) times `ns` splits of NW waves.
 //    Block ids are remapped so that the splits of a plane share an XCD (its
 //    L2 then serves the plane's partials).  The plane's keys go in units of
-//    64; unit u belongs to wave (u mod NW ns) of the plane, so the summation
-//    order depends on the sizes only.
+//    64; unit u belongs to wave position (u mod NW ns) of the plane, the
+//    positions running splits fastest, so the summation order depends on the
+//    sizes only.
 //  * Each wave keeps PD units in flight in its LDS ring (global_load_lds):
 //    the K and V tiles [64 keys][D bytes] with 16-byte chunks placed by an
 //    xor swizzle (so that the reads below meet no bank conflicts), then the
@@ -253,8 +254,10 @@ __global__ __launch_bounds__(MGeom<D>::NT, 1) void sdpa_decode_mfma(MfmaArgs a) 
     const bool has_mask = a.mask != nullptr;
     const mptr<float> mrow = has_mask ? wave_ptr(a.mask + (int64_t)b * a.mask_sb) : ksb;
 
-    const int W = ns * NW;                            // waves of the plane
-    const int wp = split * NW + wave;                 // this wave's position among them
+    // waves of the plane, splits fastest: where a small cache has fewer units
+    // than waves, the idle waves are spread over every workgroup of the plane
+    const int W = ns * NW;
+    const int wp = wave * ns + split;                 // this wave's position among them
 
     typedef const __attribute__((address_space(4))) int32_t* cptr_i32;
     int kv_len = S;
@@ -986,12 +989,17 @@ bool mfma_supported(int qmode, int D, int G, int S) {
 static int mfma_nw(int D) { return D == 256 ? 4 : 8; }
 
 // Splits per plane: one round of resident workgroups (one per CU), and no
-// more than lets every wave of the plane get a unit of a full cache; at most
+// more than lets every wave of the plane get a unit of a full cache, except
+// that a small cache may take up to four splits as long as each workgroup
+// keeps half its waves busy (its units then spread over more CUs); at most
 // 64.  `target` is the number of workgroups the device holds at once.
 static int mfma_splits_for(int B, int Hkv, int S, int D, int target) {
     const int planes = B * Hkv;
     int ns = (target + planes - 1) / planes;
-    int cap = S / (mfma_nw(D) * MKEYS);
+    const int units = S / MKEYS;
+    int cap = units / mfma_nw(D);
+    const int spread = units / (mfma_nw(D) / 2);
+    if (cap < 4) cap = spread < 4 ? spread : 4;
     if (cap > 64) cap = 64;
     if (cap < 1) cap = 1;
     if (ns > cap) ns = cap;
