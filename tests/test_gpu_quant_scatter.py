@@ -312,3 +312,47 @@ def test_scatter_affine_ties_and_near_ties(qmode, D):
     torch.cuda.synchronize()
     oracle.quant_scatter(hc, x, slots)
     assert_cache_equal(dc, hc, f"affine ties qmode {qmode} D {D}")
+
+
+@pytest.mark.parametrize("qmode", [kvq.FP8E4M3_B32, kvq.FP8E5M2_B32, kvq.INT8_B32])
+def test_scatter_block_quotients_at_code_boundaries(qmode):
+    """fp32-scale block modes with scales that are not powers of two: elements
+    whose quotients x / scale sit at the rounding boundaries between codes
+    (the midpoints between neighbouring FP8 values, the half-integers of
+    INT8) and a few ulps either side, so the quotient's own rounding decides
+    the code, or tens of ulps either side.  fp32 input; bit-exact against
+    the oracle."""
+    rng = np.random.default_rng(900 + qmode)
+    if qmode == kvq.FP8E4M3_B32:
+        vals, qmax = np.array([oracle.e4m3fn_decode(c) for c in range(0x7F)]), 448.0
+    elif qmode == kvq.FP8E5M2_B32:
+        vals, qmax = np.array([oracle.e5m2_decode(c) for c in range(0x7C)]), 57344.0
+    else:
+        vals, qmax = np.arange(128, dtype=np.float64), 127.0
+    mids = (vals[:-1] + vals[1:]) / 2.0
+    nblk = 512
+    x = np.zeros((nblk, 32), np.float32)
+    for i in range(nblk):
+        amax = np.float32(rng.uniform(0.3, 40.0))
+        scale = np.float32(amax / np.float32(qmax))          # fp32 division, as the format defines it
+        m = mids[rng.integers(0, len(mids), 31)]
+        e = (m * np.float64(scale)).astype(np.float32)
+        # odd blocks: within a few ulps of the boundary; even blocks: 9 to 40
+        # ulps away
+        steps = rng.integers(-3, 4, 31) if i % 2 else rng.integers(9, 41, 31) * np.where(rng.random(31) < 0.5, -1, 1)
+        for j in range(31):
+            for _ in range(abs(int(steps[j]))):
+                e[j] = np.nextafter(e[j], np.float32(np.inf if steps[j] > 0 else -np.inf))
+        e = np.minimum(e, amax) * np.where(rng.random(31) < 0.5, -1.0, 1.0).astype(np.float32)
+        x[i, 0] = amax if i % 2 else -amax
+        x[i, 1:] = e
+    D = 128
+    T = nblk // (D // 32)
+    x = x.reshape(1, 1, T, D)
+    slots = rng.permutation(T + 7)[:T].astype(np.int32)[None]
+    say(f"scatter block quotient boundaries qmode={qmode}")
+    dc, hc = new_pair(qmode, 1, 1, T + 7, D)
+    kvq.quant_scatter(dev_input(x, False), torch.from_numpy(slots).to(DEV), dc)
+    torch.cuda.synchronize()
+    oracle.quant_scatter(hc, x, slots)
+    assert_cache_equal(dc, hc, f"block quotient boundaries qmode {qmode}")
