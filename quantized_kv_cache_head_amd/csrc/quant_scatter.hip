@@ -70,6 +70,7 @@ struct ScatterArgs {
     uint32_t rows;         // B * H * T
     FastDiv div_t, div_h, div_lpr;   // by T, by H, by the lanes of a row (block modes: D / 8)
     const int32_t* start_pos;        // non-null: slot = *start_pos + t (full-context layout), slots unused
+    int off32;             // every element / byte offset of the launch fits in 31 bits (set by the host)
 };
 
 // The slot of token t: from the slot mapping, or (full-context layout) the
@@ -78,7 +79,10 @@ struct ScatterArgs {
 // cache writes nothing and sets the capacity flag.  report: the one lane of
 // the row that may set flags.
 __device__ __forceinline__ int token_slot(const ScatterArgs& a, int b, int t, bool report) {
-    if (!a.start_pos) return a.slots[(int64_t)b * a.ssb + t];
+    if (!a.start_pos) {
+        if (a.off32) return a.slots[(uint32_t)b * (uint32_t)a.ssb + (uint32_t)t];
+        return a.slots[(int64_t)b * a.ssb + t];
+    }
     const int start = *a.start_pos;
     if (start < 0) {
         if (report && t == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
@@ -123,7 +127,11 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
     if (row < a.rows) {
         row_coords(a, row, b, h, t);
         slot = token_slot(a, b, t, h == 0 && li == 0);
-        const int64_t xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
+        // 32-bit offsets where the host found that they fit: the wide
+        // multiplies are a large part of a short-lived wave's instructions
+        int64_t xoff;
+        if (a.off32) xoff = (uint32_t)b * (uint32_t)a.sb + (uint32_t)h * (uint32_t)a.sh + (uint32_t)t * (uint32_t)a.st;
+        else xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int d0 = (p * L + li) * 8;
@@ -177,7 +185,17 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
         if (!(fabsf(t - k) < 0.5f - TIE_MARGIN)) k = rintf(lo / scale);
         zp = min(max(QMIN - (int)k, QMIN), QMAX);
     }
-    const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+    // cache row and the byte offset of its codes
+    constexpr int RB_DIV = U4 ? 2 : 1;
+    int64_t crow, cbyte;
+    if (a.off32) {
+        const uint32_t r = ((uint32_t)b * (uint32_t)a.H + (uint32_t)h) * (uint32_t)a.n_slots + (uint32_t)slot;
+        crow = r;
+        cbyte = r * (uint32_t)(a.D / RB_DIV);
+    } else {
+        crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+        cbyte = crow * (a.D / RB_DIV);
+    }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int d0 = (p * L + li) * 8;
@@ -202,7 +220,7 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
             uint32_t w = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) w |= (uint32_t)c[i] << (4 * i);
-            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = w;
+            *reinterpret_cast<uint32_t*>(a.codes + cbyte + d0 / 2) = w;
         } else {
             uint32_t w0 = 0, w1 = 0;
 #pragma unroll
@@ -210,7 +228,7 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
                 w0 |= ((uint32_t)c[i] & 0xFFu) << (8 * i);
                 w1 |= ((uint32_t)c[4 + i] & 0xFFu) << (8 * i);
             }
-            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+            *reinterpret_cast<uint2*>(a.codes + cbyte + d0) = make_uint2(w0, w1);
         }
     }
     if (li == 0) {
@@ -331,6 +349,14 @@ static bool fill_index(ScatterArgs& a) {
     a.div_t = make_fastdiv((uint32_t)a.T);
     a.div_h = make_fastdiv((uint32_t)a.H);
     a.div_lpr = make_fastdiv((uint32_t)(a.D / 8));
+    // 32-bit offsets: x elements, slot entries and cache bytes (D per row
+    // bounds the code bytes and the scale / zero-point entries) below 2^31
+    const int64_t lim = int64_t(1) << 31;
+    const int64_t xmax = (int64_t)(a.B - 1) * a.sb + (int64_t)(a.H - 1) * a.sh + (int64_t)(a.T - 1) * a.st + a.D;
+    const int64_t smax = a.start_pos ? 0 : (int64_t)(a.B - 1) * a.ssb + a.T;
+    const int64_t cmax = (int64_t)a.B * a.H * a.n_slots * a.D;
+    a.off32 = a.sb >= 0 && a.sh >= 0 && a.st >= 0 && (a.start_pos || a.ssb >= 0) && xmax < lim && smax < lim &&
+              cmax < lim;
     return true;
 }
 
