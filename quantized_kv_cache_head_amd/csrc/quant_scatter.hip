@@ -256,7 +256,10 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
     if (row < a.rows) {
         row_coords(a, row, b, h, t);
         slot = token_slot(a, b, t, h == 0 && g == 0 && qi == 0);
-        load8<BF16>(a.x, (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st + d0, v);
+        int64_t xoff;
+        if (a.off32) xoff = (uint32_t)b * (uint32_t)a.sb + (uint32_t)h * (uint32_t)a.sh + (uint32_t)t * (uint32_t)a.st;
+        else xoff = (int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)t * a.st;
+        load8<BF16>(a.x, xoff + d0, v);
         if (slot < -1 || slot >= a.n_slots) {
             if (h == 0 && g == 0 && qi == 0 && a.err) atomicOr(a.err, KVQ_DEV_FLAG_SLOT_RANGE);
             slot = -1;
@@ -269,7 +272,12 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
     amax = wave_max_sub<4>(amax);
     if (!valid) return;
 
-    const int64_t crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+    int64_t crow;
+    if (a.off32) crow = ((uint32_t)b * (uint32_t)a.H + (uint32_t)h) * (uint32_t)a.n_slots + (uint32_t)slot;
+    else crow = ((int64_t)b * a.H + h) * a.n_slots + slot;
+    // byte offset of the row's codes (32-bit where the launch's offsets fit)
+    constexpr int RB_DIV = (QM == QM_MXFP4_B32 || QM == QM_MXFP4E1M2_B32) ? 2 : 1;
+    const int64_t cbyte = a.off32 ? (int64_t)((uint32_t)crow * (uint32_t)(a.D / RB_DIV)) : crow * (a.D / RB_DIV);
     if constexpr (QM == QM_FP8E4M3_B32 || QM == QM_FP8E5M2_B32 || QM == QM_INT8_B32) {
         // fp32 scale amax / Q_MAX; an all-zero block stores scale 0, codes 0
         constexpr float QMAX = QM == QM_FP8E4M3_B32 ? 448.0f : QM == QM_FP8E5M2_B32 ? 57344.0f : 127.0f;
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
                 }
             }
         }
-        *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(a.codes + cbyte + d0) = make_uint2(w0, w1);
         if (qi == 0) reinterpret_cast<float*>(a.scales)[crow * gpr + g] = scale;
     } else {
         // MX: E8M0 power-of-two scale X; x / X is exact
@@ -308,9 +316,9 @@ __global__ __launch_bounds__(256) void quant_scatter_block(ScatterArgs a0, Scatt
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = v[i] * inv;
         if constexpr (F4) {
-            *reinterpret_cast<uint32_t*>(a.codes + crow * (a.D / 2) + d0 / 2) = E1M2 ? cvt8_e1m2(y) : cvt8_e2m1(y);
+            *reinterpret_cast<uint32_t*>(a.codes + cbyte + d0 / 2) = E1M2 ? cvt8_e1m2(y) : cvt8_e2m1(y);
         } else {
-            *reinterpret_cast<uint2*>(a.codes + crow * a.D + d0) = make_uint2(cvt4_e4m3fn(y), cvt4_e4m3fn(y + 4));
+            *reinterpret_cast<uint2*>(a.codes + cbyte + d0) = make_uint2(cvt4_e4m3fn(y), cvt4_e4m3fn(y + 4));
         }
         if (qi == 0) reinterpret_cast<uint8_t*>(a.scales)[crow * gpr + g] = (uint8_t)e8;
     }

@@ -358,19 +358,20 @@ def test_scatter_block_quotients_at_code_boundaries(qmode):
     assert_cache_equal(dc, hc, f"block quotient boundaries qmode {qmode}")
 
 
-def test_scatter_affine_cache_past_2_31_bytes():
-    """A cache of more than 2^31 code bytes (int8, D 128, 2^24 + 64 slots of
-    one head): the launch takes the 64-bit offset path, and rows written near
-    the end lie past byte 2^31.  Written rows, neighbours and a skipped slot
-    are bit-exact against the oracle."""
+@pytest.mark.parametrize("qmode", [kvq.INT8_TH, kvq.FP8E4M3_B32])
+def test_scatter_affine_cache_past_2_31_bytes(qmode):
+    """A cache of more than 2^31 code bytes (int8 or FP8-E4M3, D 128, 2^24 + 64
+    slots of one head): the launch takes the 64-bit offset path, and rows
+    written near the end lie past byte 2^31.  Written rows, neighbours and a
+    skipped slot are bit-exact against the oracle."""
     rng = np.random.default_rng(2 ** 31 % 1000)
     B, H, T, D = 1, 1, 16, 128
     S = (1 << 24) + 64
     x = _inputs(rng, B, H, T, D, True)
     slots = np.array([[S - 1, S - 2, S - 7, S - 64, S - 65, (1 << 24) - 1, 0, 5, -1, S - 30, S - 31, S - 32,
                        (1 << 23), (1 << 23) + 1, 17, S - 3]], np.int32)
-    say(f"scatter past 2^31 bytes S={S}")
-    dc, hc = new_pair(kvq.INT8_TH, B, H, S, D)
+    say(f"scatter past 2^31 bytes qmode={qmode} S={S}")
+    dc, hc = new_pair(qmode, B, H, S, D)
     kvq.quant_scatter(dev_input(x, True), torch.from_numpy(slots).to(DEV), dc)
     torch.cuda.synchronize()
     oracle.quant_scatter(hc, x, slots)
