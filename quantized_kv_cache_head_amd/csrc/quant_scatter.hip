@@ -201,13 +201,24 @@ __global__ __launch_bounds__(256) void quant_scatter_affine(ScatterArgs a0, Scat
         const int d0 = (p * L + li) * 8;
         if (d0 >= a.D) break;
         int c[8];
+        // per element, with the exact product x * inv inside one fused
+        // operation (it lies even closer to RN(x / scale) than the rounded
+        // product): y = RN(x * inv + 1.5 * 2^23 + zp) holds n + zp, n the
+        // integer nearest x * inv, in its low mantissa bits (|n + zp| < 2^22);
+        // n = y - (1.5 * 2^23 + zp) exactly, and r = RN(x * inv - n) tells how
+        // far x * inv is from n
+        // far x * inv is from n.  The clamp to [qmin, qmax] is a float median
+        // on y (the bounds 1.5 * 2^23 + qmin / qmax are exact), and the code
+        // is the low byte (nibble) of y's bits: 1.5 * 2^23 has none set.
+        const float mz = 0x1.8p23f + (float)zp;
+        constexpr float YLO = 0x1.8p23f + (float)QMIN, YHI = 0x1.8p23f + (float)QMAX;
         bool near_tie = false;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float t = v[p][i] * inv;
-            const float k = rintf(t);
-            near_tie |= !(fabsf(t - k) < 0.5f - TIE_MARGIN);
-            c[i] = min(max((int)k + zp, QMIN), QMAX);
+            const float y = fmaf(v[p][i], inv, mz);
+            const float r = fmaf(v[p][i], inv, -(y - mz));
+            near_tie |= !(fabsf(r) < 0.5f - TIE_MARGIN);
+            c[i] = (int)(__float_as_uint(__builtin_amdgcn_fmed3f(y, YLO, YHI)) & (U4 ? 0xFu : 0xFFu));
         }
         if (near_tie) {
 #pragma unroll
