@@ -991,14 +991,15 @@ static int mfma_nw(int D) { return D == 256 ? 4 : 8; }
 // Splits per plane: one round of resident workgroups (one per CU), and no
 // more than lets every wave of the plane get a unit of a full cache, except
 // that a small cache may take up to eight splits as long as each workgroup
-// keeps half its waves busy (its units then spread over more CUs); at most
-// 64.  `target` is the number of workgroups the device holds at once.
+// keeps half its waves busy, a quarter for eight-wave workgroups once the
+// plane has two units per wave of one workgroup (its units then spread over
+// more CUs); at most 64.  `target` is the number of workgroups the device holds at once.
 static int mfma_splits_for(int B, int Hkv, int S, int D, int target) {
     const int planes = B * Hkv;
     int ns = (target + planes - 1) / planes;
     const int units = S / MKEYS;
     int cap = units / mfma_nw(D);
-    const int spread = units / (mfma_nw(D) / 2);
+    const int spread = (mfma_nw(D) == 8 && units >= 16) ? units / 2 : units / (mfma_nw(D) / 2);
     if (cap < 8) cap = spread < 8 ? spread : 8;
     if (cap > 64) cap = 64;
     if (cap < 1) cap = 1;
